@@ -1,0 +1,43 @@
+"""Build of the gfx950 shared library libbefmoe.so (hipcc, in-tree).
+
+All HIP sources are compiled for gfx950 only, with IEEE fp32 division and
+square root (the hipcc default, stated explicitly) and without fast-math or
+denormal flushing, and with packed-fp32 instruction selection turned off.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+SO = os.path.join(PKG, "libbefmoe.so")
+SOURCES = ["moe_api.hip", "actq.hip", "route.hip", "permute.hip", "gemv.hip", "gemm.hip",
+           "combine.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
+    "-ffp-contract=fast",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+]
+
+
+def build(verbose: bool = False, extra: list[str] | None = None, out: str | None = None) -> str:
+    out = out or SO
+    cmd = [HIPCC, *FLAGS, *(extra or []), *[os.path.join(CSRC, s) for s in SOURCES], "-o",
+           out + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+if __name__ == "__main__":
+    build(verbose=True)

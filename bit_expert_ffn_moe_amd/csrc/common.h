@@ -1,0 +1,206 @@
+// common.h -- device helpers shared by the gfx950 kernels of this library.
+//
+// Format conversions use the CDNA4 hardware converters:
+//   v_cvt_pk_fp8_f32            two fp32 -> two E4M3 codes, round to nearest even
+//   v_cvt_scalef32_pk_f16_fp8   two E4M3 codes -> two fp16 (exact: every E4M3
+//                               value is an fp16 value)
+//   v_cvt_scalef32_pk_f16_fp4   one byte of two E2M1 codes -> two fp16 (exact)
+// and products of those exact fp16 values are summed with v_dot2_f32_f16
+// (fp32 accumulate).  E4M3 and E2M1 are the OCP formats (OCP 8-bit Floating
+// Point rev 1.0; OCP Microscaling Formats v1.0).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bef {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// E4M3 code of v: clamp to +-448 first (the conversion then rounds to
+// nearest even; values in (448, 464) round to 448 either way, so the clamp
+// only turns would-be overflows into the saturated code; -0 stays -0).
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+  d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+  uint32_t v = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)v, true);
+  return v;
+}
+
+// Two E4M3 codes (bytes 0-1 or 2-3 of v) -> (lo element, hi element) fp16.
+__device__ __forceinline__ h2_t e4m3x2_lo(uint32_t v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
+}
+__device__ __forceinline__ h2_t e4m3x2_hi(uint32_t v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, true);
+}
+
+// Two E2M1 codes in byte B of v (element 2j in bits 0-3, 2j+1 in bits 4-7)
+// -> (element 2j, element 2j+1) fp16.
+template <int B>
+__device__ __forceinline__ h2_t e2m1x2(uint32_t v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, B);
+}
+
+__device__ __forceinline__ float dot2(h2_t a, h2_t b, float c) {
+  return __builtin_amdgcn_fdot2(a, b, c, false);
+}
+
+// Eight fp16 pairs of activations (elements 0..15 of a 16-code group, from
+// four dwords of E4M3 codes).
+struct Act16 {
+  h2_t p[8];
+};
+
+__device__ __forceinline__ void e4m3x16_to_h2(const uint4 q, Act16& a) {
+  a.p[0] = e4m3x2_lo(q.x);
+  a.p[1] = e4m3x2_hi(q.x);
+  a.p[2] = e4m3x2_lo(q.y);
+  a.p[3] = e4m3x2_hi(q.y);
+  a.p[4] = e4m3x2_lo(q.z);
+  a.p[5] = e4m3x2_hi(q.z);
+  a.p[6] = e4m3x2_lo(q.w);
+  a.p[7] = e4m3x2_hi(q.w);
+}
+
+// Sum of 16 products: E2M1 codes in one dword w (elements 8d..8d+7 for the
+// bytes 0..3) against activation pairs a.p[...]: the dword holds 8 weights,
+// matching activation pairs p0..p3.
+__device__ __forceinline__ float dot8_fp4(uint32_t w, h2_t p0, h2_t p1, h2_t p2, h2_t p3,
+                                          float acc) {
+  acc = dot2(e2m1x2<0>(w), p0, acc);
+  acc = dot2(e2m1x2<1>(w), p1, acc);
+  acc = dot2(e2m1x2<2>(w), p2, acc);
+  acc = dot2(e2m1x2<3>(w), p3, acc);
+  return acc;
+}
+
+// 32 E2M1 weights (16 bytes) . 32 activations (two Act16) -> fp32.
+__device__ __forceinline__ float dot32_fp4(const uint4 w, const Act16& a0, const Act16& a1) {
+  float acc = 0.0f;
+  acc = dot8_fp4(w.x, a0.p[0], a0.p[1], a0.p[2], a0.p[3], acc);
+  acc = dot8_fp4(w.y, a0.p[4], a0.p[5], a0.p[6], a0.p[7], acc);
+  acc = dot8_fp4(w.z, a1.p[0], a1.p[1], a1.p[2], a1.p[3], acc);
+  acc = dot8_fp4(w.w, a1.p[4], a1.p[5], a1.p[6], a1.p[7], acc);
+  return acc;
+}
+
+// 2^(b - 127) applied exactly (UE8M0 scale byte b).
+__device__ __forceinline__ float scale_ue8m0(float v, uint32_t b) {
+  return __builtin_amdgcn_ldexpf(v, (int)b - 127);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
+// Max over aligned groups of G lanes (G a power of two <= 64).
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int m = G / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// Workspace control block: word 0 = status bits, then counters.
+struct WsCtl {
+  uint32_t status;
+  uint32_t route_done;  // arrival counter of the small-T router
+  uint32_t pad[62];
+};
+
+__device__ __forceinline__ void set_status(uint32_t* st, uint32_t bit) { atomicOr(st, bit); }
+
+__device__ __forceinline__ float silu_mul_accurate(float g, float u) {
+  return g / (1.0f + expf(-g)) * u;
+}
+
+// Exclusive prefix sum of v over a block of exactly 256 threads.  s_tmp holds
+// >= 4 ints.  Returns the prefix; *total receives the block sum.  All
+// threads must call it.
+__device__ __forceinline__ int block256_exclusive_scan(int v, int* s_tmp, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int t = __shfl_up(inc, d, kWave);
+    if (lane >= d) inc += t;
+  }
+  if (lane == 63) s_tmp[wv] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int s = s_tmp[i];
+    base += (i < wv) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
+}
+
+// Group lookup for ragged grouped work.  Groups g = 0..G-1 (G <= 512) own
+// units[g] consecutive work items, units[g] = f(count of rows of g) with
+// count = offsets[g+1]-offsets[g].  Given a linear item index `item`, find
+// (group, index inside the group).  Returns the group or -1 when `item` is
+// past the last item.  All 256 threads of the block must call it.
+template <typename UnitsOf>
+__device__ __forceinline__ int find_group_item(const int32_t* __restrict__ offsets, int G, int item,
+                                               UnitsOf units_of, int* s_tmp /* >= 6 ints */,
+                                               int* local_item) {
+  const int t = threadIdx.x;
+  const int ga = t, gb = t + 256;
+  int ca = 0, cb = 0;
+  if (ga < G) ca = offsets[ga + 1] - offsets[ga];
+  if (gb < G) cb = offsets[gb + 1] - offsets[gb];
+  const int ua = (ga < G) ? units_of(ca) : 0;
+  const int ub = (gb < G) ? units_of(cb) : 0;
+  if (t == 0) {
+    s_tmp[4] = -1;
+    s_tmp[5] = 0;
+  }
+  int tot_a, tot_b;
+  const int pa = block256_exclusive_scan(ua, s_tmp, &tot_a);
+  const int pb = block256_exclusive_scan(ub, s_tmp, &tot_b) + tot_a;
+  if (ua > 0 && item >= pa && item < pa + ua) {
+    s_tmp[4] = ga;
+    s_tmp[5] = item - pa;
+  }
+  if (ub > 0 && item >= pb && item < pb + ub) {
+    s_tmp[4] = gb;
+    s_tmp[5] = item - pb;
+  }
+  __syncthreads();
+  const int g = s_tmp[4];
+  *local_item = s_tmp[5];
+  __syncthreads();
+  return g;
+}
+
+}  // namespace bef

@@ -1,0 +1,59 @@
+// kernels.h -- launchers of the gfx950 kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bef {
+
+constexpr int kRouteSmallT = 4;           // router: per-chunk blocks + last-block top-k
+constexpr int kPermuteSmallPairs = 2048;  // permute: single block up to this many pairs
+constexpr int kPermuteTokBlock = 256;     // permute: tokens per block above that
+constexpr int kGemvMaxRows = 8;           // VALU GEMV path: rows (k + 1) per token
+constexpr int kGemmBM = 128;              // MFMA grouped GEMM: tokens per tile
+constexpr uint32_t MOE_STATUS_BAD_EXPERT_ID_DEV = 1u;
+
+struct GemvArgs {
+  const uint8_t *gq, *gs, *uq, *us, *dq, *ds;
+  const uint8_t* xq;
+  const float* xs;
+  const int32_t *offsets, *row_token, *row_of;
+  const float* topk_w;
+  int E, H, I, k, n_slots;
+  float* h;
+  float* y_rows;
+  void* out;
+  int out_bf16;
+  uint8_t* hq_ws;
+  float* hs_ws;
+};
+
+struct GemmArgs {
+  int fmt;
+  const uint8_t *gq, *uq, *dq;
+  const void *gs, *us, *ds;
+  const uint8_t* xq;
+  const float* xs;
+  const int32_t *offsets, *row_token;
+  int T, k, E, H, I;
+  uint8_t* hq;
+  float* hs;
+  float* y_rows;
+};
+
+hipError_t launch_act_quant(const void* x, bool bf16, int64_t rows, int32_t cols, uint8_t* q,
+                            float* s, hipStream_t st);
+hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int H, int E, int k,
+                        int32_t* ids, float* w, float* part, uint32_t* counter, hipStream_t st);
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
+                          int32_t* row_token, int32_t* row_of, int32_t* cnt, int32_t* base,
+                          uint32_t* status, hipStream_t st);
+hipError_t launch_combine(const float* y, const int32_t* row_of, const float* topk_w, int T, int k,
+                          int H, void* out, bool bf16, hipStream_t st);
+hipError_t launch_gemv_gate_up(const GemvArgs& a, hipStream_t st);
+hipError_t launch_gemv_down(const GemvArgs& a, bool combine, hipStream_t st);
+hipError_t launch_gemm_gate_up(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_down(const GemmArgs& a, hipStream_t st);
+hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t st);
+int gemm_mtile_slots(int T, int k, int E, int BM);
+
+}  // namespace bef

@@ -1,0 +1,437 @@
+// moe_api.hip -- host side of the C ABI declared in include/moe.h:
+// argument validation, workspace carving and launch sequencing.  Nothing here
+// allocates, frees or synchronises (except the two debug helpers, which say
+// so); every entry point validates first and enqueues only on success.
+#include <string.h>
+
+#include <atomic>
+
+#include "common.h"
+#include "kernels.h"
+#include "moe.h"
+
+namespace bef {
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t st) {
+  zero_words_kernel<<<(n + 255) / 256, 256, 0, st>>>(p, n);
+  return hipGetLastError();
+}
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kCtlBytes = 256;
+
+size_t up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Workspace layout for one call shape.  Sections are carved in this order so
+// that the standalone calls, which know fewer sizes, agree with the whole-
+// layer call: control | permute scratch (T, E) | router partials (T, H, E) |
+// everything else (needs the weights' shapes).
+struct Layout {
+  size_t ctl, cnt, base, part, ids, w, xq, xs, offsets, row_token, row_of, h, hq, hs, y, total;
+  size_t end_permute, end_route, end_ffn;
+};
+
+bool gemv_path(int fmt, int T, int k, int H, int I) {
+  return fmt == MOE_W_FP4_E2M1_UE8M0_K32 && T == 1 && k + 1 <= kGemvMaxRows && H <= 8192 &&
+         I <= 4096;
+}
+
+Layout layout_for(int E, int H, int I, int T, int k, bool with_h) {
+  Layout L;
+  const size_t R = (size_t)T * k + T;
+  const size_t nblk = ((size_t)T + kPermuteTokBlock - 1) / kPermuteTokBlock;
+  size_t o = 0;
+  L.ctl = o;
+  o += up(kCtlBytes);
+  L.cnt = o;
+  o += up(nblk * E * 4);
+  L.base = o;
+  o += up(nblk * E * 4);
+  L.end_permute = o;
+  L.part = o;
+  if (T <= kRouteSmallT) o += up((size_t)(H / 64) * T * E * 4);
+  L.end_route = o;
+  L.ids = o;
+  o += up((size_t)T * k * 4);
+  L.w = o;
+  o += up((size_t)T * k * 4);
+  L.xq = o;
+  o += up((size_t)T * H);
+  L.xs = o;
+  o += up((size_t)T * (H / 128) * 4);
+  L.offsets = o;
+  o += up((size_t)(E + 2) * 4);
+  L.row_token = o;
+  o += up(R * 4);
+  L.row_of = o;
+  o += up((size_t)T * (k + 1) * 4);
+  L.h = o;
+  if (with_h) o += up(R * I * 4);
+  L.hq = o;
+  o += up(R * I);
+  L.hs = o;
+  o += up(R * (I / 128) * 4);
+  L.end_ffn = o;
+  L.y = o;
+  o += up(R * H * 4);
+  L.total = o;
+  return L;
+}
+
+Layout layout_w(const moe_weights* w, int T, int k) {
+  return layout_for(w->n_experts, w->hidden, w->inter, T, k,
+                    gemv_path(w->format, T, k, w->hidden, w->inter));
+}
+
+// One-time check per device that it is a gfx950 (the only global state).
+std::atomic<int> g_arch_ok[64];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return MOE_ENOTSUP;
+  }
+  if (dev < 64) {
+    int v = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (v == 1) return MOE_OK;
+    if (v == 2) return MOE_ENOTSUP;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_ENOTSUP;
+  }
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? MOE_OK : MOE_ENOTSUP;
+}
+
+int launch_status(hipError_t e) {
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_ELAUNCH;
+  }
+  return MOE_OK;
+}
+
+int check_tk(int T, int k, int E) {
+  if (T < 1 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
+  if (E > 256 || k > 16) return MOE_ENOTSUP;
+  return MOE_OK;
+}
+
+int check_hidden(int H) {
+  if (H < 128 || H % 128 != 0) return H > 0 && H % 128 == 0 ? MOE_ENOTSUP : MOE_EINVAL;
+  if (H > 8192) return MOE_ENOTSUP;
+  return MOE_OK;
+}
+
+int check_weights(const moe_weights* w) {
+  if (!w) return MOE_EINVAL;
+  if (w->format != MOE_W_FP4_E2M1_UE8M0_K32 && w->format != MOE_W_FP8_E4M3_F32_B128)
+    return MOE_ENOTSUP;
+  if (w->n_experts < 1) return MOE_EINVAL;
+  if (w->n_experts > 256) return MOE_ENOTSUP;
+  int rc = check_hidden(w->hidden);
+  if (rc) return rc;
+  rc = check_hidden(w->inter);
+  if (rc) return rc;
+  const void* ps[6] = {w->gate_q, w->gate_s, w->up_q, w->up_s, w->down_q, w->down_s};
+  for (const void* p : ps)
+    if (!p) return MOE_EINVAL;
+  for (const void* p : ps)
+    if (!aligned16(p)) return MOE_EALIGN;
+  return MOE_OK;
+}
+
+int check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (!ws) return MOE_EINVAL;
+  if (((uintptr_t)ws & (kAlign - 1)) != 0) return MOE_EALIGN;
+  if (ws_bytes < need) return MOE_EWORKSPACE;
+  return MOE_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<uint8_t*>(ws) + off);
+}
+
+// ---- enqueue helpers (arguments already validated) -----------------------
+
+int enqueue_expert_ffn(const moe_weights* w, const uint8_t* xq, const float* xs, int T, int k,
+                       const int32_t* offsets, const int32_t* row_token, const int32_t* row_of,
+                       const float* topk_w, float* y_rows, void* out, int out_dtype,
+                       const Layout& L, void* ws, hipStream_t st) {
+  const int E = w->n_experts, H = w->hidden, I = w->inter;
+  if (gemv_path(w->format, T, k, H, I)) {
+    GemvArgs a;
+    a.gq = (const uint8_t*)w->gate_q;
+    a.gs = (const uint8_t*)w->gate_s;
+    a.uq = (const uint8_t*)w->up_q;
+    a.us = (const uint8_t*)w->up_s;
+    a.dq = (const uint8_t*)w->down_q;
+    a.ds = (const uint8_t*)w->down_s;
+    a.xq = xq;
+    a.xs = xs;
+    a.offsets = offsets;
+    a.row_token = row_token;
+    a.row_of = row_of;
+    a.topk_w = topk_w;
+    a.E = E, a.H = H, a.I = I, a.k = k;
+    a.n_slots = (T * k < E ? T * k : E) + 1;
+    a.h = at<float>(ws, L.h);
+    a.y_rows = y_rows;
+    a.out = out;
+    a.out_bf16 = out_dtype == MOE_DT_BF16;
+    a.hq_ws = at<uint8_t>(ws, L.hq);
+    a.hs_ws = at<float>(ws, L.hs);
+    int rc = launch_status(launch_gemv_gate_up(a, st));
+    if (rc) return rc;
+    return launch_status(launch_gemv_down(a, out != nullptr, st));
+  }
+  GemmArgs g;
+  g.fmt = w->format;
+  g.gq = (const uint8_t*)w->gate_q;
+  g.uq = (const uint8_t*)w->up_q;
+  g.dq = (const uint8_t*)w->down_q;
+  g.gs = w->gate_s;
+  g.us = w->up_s;
+  g.ds = w->down_s;
+  g.xq = xq;
+  g.xs = xs;
+  g.offsets = offsets;
+  g.row_token = row_token;
+  g.T = T, g.k = k, g.E = E, g.H = H, g.I = I;
+  g.hq = at<uint8_t>(ws, L.hq);
+  g.hs = at<float>(ws, L.hs);
+  g.y_rows = y_rows;
+  int rc = launch_status(launch_gemm_gate_up(g, st));
+  if (rc) return rc;
+  rc = launch_status(launch_gemm_down(g, st));
+  if (rc) return rc;
+  if (out) rc = launch_status(launch_combine(y_rows, row_of, topk_w, T, k, H, out,
+                                             out_dtype == MOE_DT_BF16, st));
+  return rc;
+}
+
+}  // namespace
+}  // namespace bef
+
+using namespace bef;
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_weights* w, int32_t max_tokens, int32_t top_k) {
+  if (check_weights(w) != MOE_OK) return 0;
+  if (check_tk(max_tokens, top_k, w->n_experts) != MOE_OK) return 0;
+  size_t a = layout_w(w, max_tokens, top_k).total;
+  size_t b = layout_w(w, 1, top_k).total;
+  return a > b ? a : b;
+}
+
+int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_ws(ws, ws_bytes, kCtlBytes);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  return launch_status(launch_zero_words((uint32_t*)ws, (int)(kCtlBytes / 4), (hipStream_t)stream));
+}
+
+int moe_route(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H, int32_t E,
+              int32_t k, int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+              void* stream) {
+  if (!x || !w_router || !topk_ids || !topk_w) return MOE_EINVAL;
+  int rc = check_tk(T, k, E);
+  if (rc) return rc;
+  rc = check_hidden(H);
+  if (rc) return rc;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(topk_ids) || !aligned16(topk_w))
+    return MOE_EALIGN;
+  const Layout L = layout_for(E, H, 128, T, k, false);
+  rc = check_ws(ws, ws_bytes, L.end_route);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  WsCtl* ctl = at<WsCtl>(ws, L.ctl);
+  return launch_status(launch_route(x, w_router, T, H, E, k, topk_ids, topk_w,
+                                    at<float>(ws, L.part), &ctl->route_done,
+                                    (hipStream_t)stream));
+}
+
+int act_quant_fp8(const void* x, int32_t x_dtype, int64_t rows, int32_t cols, uint8_t* q,
+                  float* scales, void* stream) {
+  if (!x || !q || !scales) return MOE_EINVAL;
+  if (x_dtype != MOE_DT_BF16 && x_dtype != MOE_DT_F32) return MOE_EINVAL;
+  if (rows < 1 || cols < 128 || cols % 128 != 0) return MOE_EINVAL;
+  if (rows * (int64_t)(cols / 128) * 16 > (int64_t)0x7fffffff * 256) return MOE_ENOTSUP;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(scales)) return MOE_EALIGN;
+  int rc = check_device();
+  if (rc) return rc;
+  return launch_status(
+      launch_act_quant(x, x_dtype == MOE_DT_BF16, rows, cols, q, scales, (hipStream_t)stream));
+}
+
+int moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* offsets,
+                int32_t* row_token, int32_t* row_of, void* ws, size_t ws_bytes, void* stream) {
+  if (!topk_ids || !offsets || !row_token || !row_of) return MOE_EINVAL;
+  int rc = check_tk(T, k, E);
+  if (rc) return rc;
+  if (!aligned16(topk_ids) || !aligned16(offsets) || !aligned16(row_token) || !aligned16(row_of))
+    return MOE_EALIGN;
+  const Layout L = layout_for(E, 128, 128, T, k, false);
+  rc = check_ws(ws, ws_bytes, L.end_permute);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  WsCtl* ctl = at<WsCtl>(ws, L.ctl);
+  return launch_status(launch_permute(topk_ids, T, k, E, offsets, row_token, row_of,
+                                      at<int32_t>(ws, L.cnt), at<int32_t>(ws, L.base),
+                                      &ctl->status, (hipStream_t)stream));
+}
+
+int moe_expert_ffn(const moe_weights* w, const uint8_t* xq, const float* xs, int32_t T, int32_t k,
+                   const int32_t* offsets, const int32_t* row_token, float* y_rows, void* ws,
+                   size_t ws_bytes, void* stream) {
+  int rc = check_weights(w);
+  if (rc) return rc;
+  if (!xq || !xs || !offsets || !row_token || !y_rows) return MOE_EINVAL;
+  rc = check_tk(T, k, w->n_experts);
+  if (rc) return rc;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(offsets) || !aligned16(row_token) ||
+      !aligned16(y_rows))
+    return MOE_EALIGN;
+  const Layout L = layout_w(w, T, k);
+  rc = check_ws(ws, ws_bytes, L.end_ffn);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  return enqueue_expert_ffn(w, xq, xs, T, k, offsets, row_token, nullptr, nullptr, y_rows,
+                            nullptr, 0, L, ws, (hipStream_t)stream);
+}
+
+int moe_combine(const float* y_rows, const int32_t* row_of, const float* topk_w, int32_t T,
+                int32_t k, int32_t H, void* out, int32_t out_dtype, void* stream) {
+  if (!y_rows || !row_of || !topk_w || !out) return MOE_EINVAL;
+  if (T < 1 || k < 1) return MOE_EINVAL;
+  if (k > 16) return MOE_ENOTSUP;
+  int rc = check_hidden(H);
+  if (rc) return rc;
+  if (out_dtype != MOE_DT_BF16 && out_dtype != MOE_DT_F32) return MOE_EINVAL;
+  if (!aligned16(y_rows) || !aligned16(row_of) || !aligned16(topk_w) || !aligned16(out))
+    return MOE_EALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  return launch_status(
+      launch_combine(y_rows, row_of, topk_w, T, k, H, out, out_dtype == MOE_DT_BF16,
+                     (hipStream_t)stream));
+}
+
+int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint16_t* x, int32_t T,
+                     int32_t k, const int32_t* routing_ids, const float* routing_w, void* out,
+                     int32_t out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_weights(w);
+  if (rc) return rc;
+  if (!x || !out) return MOE_EINVAL;
+  if ((routing_ids == nullptr) != (routing_w == nullptr)) return MOE_EINVAL;
+  if (!routing_ids && !w_router) return MOE_EINVAL;
+  if (out_dtype != MOE_DT_BF16 && out_dtype != MOE_DT_F32) return MOE_EINVAL;
+  rc = check_tk(T, k, w->n_experts);
+  if (rc) return rc;
+  if (!aligned16(x) || !aligned16(out) || (w_router && !aligned16(w_router)) ||
+      (routing_ids && (!aligned16(routing_ids) || !aligned16(routing_w))))
+    return MOE_EALIGN;
+  const Layout L = layout_w(w, T, k);
+  rc = check_ws(ws, ws_bytes, L.total);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const int E = w->n_experts, H = w->hidden;
+  WsCtl* ctl = at<WsCtl>(ws, L.ctl);
+  const int32_t* ids = routing_ids;
+  const float* tw = routing_w;
+  if (!ids) {
+    int32_t* ids_ws = at<int32_t>(ws, L.ids);
+    float* w_ws = at<float>(ws, L.w);
+    rc = launch_status(launch_route(x, w_router, T, H, E, k, ids_ws, w_ws, at<float>(ws, L.part),
+                                    &ctl->route_done, st));
+    if (rc) return rc;
+    ids = ids_ws;
+    tw = w_ws;
+  }
+  uint8_t* xq = at<uint8_t>(ws, L.xq);
+  float* xs = at<float>(ws, L.xs);
+  rc = launch_status(launch_act_quant(x, true, T, H, xq, xs, st));
+  if (rc) return rc;
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* row_token = at<int32_t>(ws, L.row_token);
+  int32_t* row_of = at<int32_t>(ws, L.row_of);
+  rc = launch_status(launch_permute(ids, T, k, E, offsets, row_token, row_of,
+                                    at<int32_t>(ws, L.cnt), at<int32_t>(ws, L.base),
+                                    &ctl->status, st));
+  if (rc) return rc;
+  return enqueue_expert_ffn(w, xq, xs, T, k, offsets, row_token, row_of, tw, at<float>(ws, L.y),
+                            out, out_dtype, L, ws, st);
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_ENOTSUP: return "not supported (device, format or size limit)";
+    case MOE_EALIGN: return "misaligned pointer";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_device_status(void* ws, void* stream, uint32_t* status, int clear) {
+  if (!ws || !status) return MOE_EINVAL;
+  if (((uintptr_t)ws & (kAlign - 1)) != 0) return MOE_EALIGN;
+  int rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if (hipMemcpyAsync(status, ws, sizeof(uint32_t), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_ELAUNCH;
+  }
+  if (clear) {
+    rc = launch_status(launch_zero_words((uint32_t*)ws, 1, st));
+    if (rc) return rc;
+    if (hipStreamSynchronize(st) != hipSuccess) {
+      (void)hipGetLastError();
+      return MOE_ELAUNCH;
+    }
+  }
+  return MOE_OK;
+}
+
+int moe_debug_intermediates(const moe_weights* w, int32_t T, int32_t k, void* ws,
+                            size_t ws_bytes, float** h, uint8_t** hq, float** hs) {
+  int rc = check_weights(w);
+  if (rc) return rc;
+  rc = check_tk(T, k, w->n_experts);
+  if (rc) return rc;
+  const Layout L = layout_w(w, T, k);
+  rc = check_ws(ws, ws_bytes, L.end_ffn);
+  if (rc) return rc;
+  const bool gv = gemv_path(w->format, T, k, w->hidden, w->inter);
+  if (h) *h = gv ? at<float>(ws, L.h) : nullptr;
+  if (hq) *hq = at<uint8_t>(ws, L.hq);
+  if (hs) *hs = at<float>(ws, L.hs);
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,191 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed-expert MoE FFN library.
+ *
+ * The layer: 256 routed experts, top-6 per token, plus one always-on shared
+ * expert (tcti.cn post on DeepSeek-V4-Flash on 4x RTX 2080 Ti, section
+ * "DeepSeek-V4-Flash的可能性"; ai-muninn.com "[洋垃圾跑大模型 #3]", section
+ * "目標不是「載得進去」...").  Expert weights are FP4 E2M1 with one UE8M0
+ * scale per 32 inputs, or FP8 E4M3 with one fp32 scale per 128x128 block;
+ * activations are FP8 E4M3 with one fp32 scale (amax/448) per 128.  The
+ * pages name the operators this ABI exposes: act_quant feeding the low-bit
+ * linears, fp4_gemm (FP8-quantised activation x FP4 packed weight) and
+ * fp8_gemm (tcti.cn post, section "补齐软件栈缺失"); the router picks the
+ * token's experts first (dpshk.com article on deepseek-v4-flash-0731-in-c,
+ * section "核心实现一"); each expert is read once for all of its tokens
+ * (same article, "核心实现三"); dequantisation happens inside the product,
+ * gate and up share one quantised input, and workspaces are allocated once
+ * and reused (same article, "核心实现四").
+ *
+ * Conventions for every call:
+ *  - Every buffer is a DEVICE pointer owned by the caller.  The library never
+ *    allocates, frees or synchronises inside these calls (the debug helpers
+ *    at the end are the only exceptions and say so).
+ *  - Arguments are validated on the host first; on any error nothing is
+ *    enqueued and a negative MOE_E* status is returned.  Otherwise the work
+ *    is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
+ *    default stream) and MOE_OK is returned.  MOE_ELAUNCH means the HIP
+ *    launch itself failed (the HIP error is cleared).
+ *  - All device pointers must be 16-byte aligned (MOE_EALIGN otherwise);
+ *    `ws` must be 256-byte aligned.
+ *  - bf16 values are passed as their uint16_t bit patterns.
+ *  - Expert ids outside [0, E) found on the device are skipped (their rows
+ *    produce zero contribution) and set bit MOE_STATUS_BAD_EXPERT_ID in the
+ *    workspace status word; no memory is accessed out of bounds.
+ *  - Calls are reentrant for distinct workspaces; two calls in flight on the
+ *    same workspace race.
+ *  - Limits: 1 <= E <= 256, 1 <= k <= min(E, 16), H and I multiples of 128,
+ *    128 <= H <= 8192, 128 <= I <= 8192, T >= 1 (MOE_ENOTSUP beyond the
+ *    size limits, MOE_EINVAL for malformed values).  The device must be a
+ *    gfx950 (MOE_ENOTSUP otherwise).
+ */
+#ifndef BEF_MOE_H
+#define BEF_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,     /* null pointer, bad size, unknown dtype            */
+  MOE_ENOTSUP = -2,    /* not a gfx950 device, unknown format, size limit   */
+  MOE_EALIGN = -3,     /* pointer not 16-byte (ws: 256-byte) aligned        */
+  MOE_EWORKSPACE = -4, /* workspace smaller than moe_workspace_bytes()      */
+  MOE_ELAUNCH = -5     /* a HIP launch failed                               */
+};
+
+/* Weight formats. */
+enum {
+  MOE_W_FP4_E2M1_UE8M0_K32 = 1, /* E2M1 codes 2/byte (element 2j in bits 0-3),
+                                   one UE8M0 byte per 32 inputs               */
+  MOE_W_FP8_E4M3_F32_B128 = 2   /* E4M3 codes, one fp32 per 128x128 block     */
+};
+
+/* Activation / output dtypes. */
+enum { MOE_DT_BF16 = 1, MOE_DT_F32 = 2 };
+
+/* Device status word bits (see moe_device_status). */
+enum { MOE_STATUS_BAD_EXPERT_ID = 1u };
+
+/* Stacked expert weights, expert-major; slot E (the last) is the shared
+ * expert, which must have the same intermediate size as the routed ones.
+ * Matrices are [out][in] row-major.
+ *   FP4: gate_q/up_q [E+1][I][H/2] u8, gate_s/up_s [E+1][I][H/32] u8,
+ *        down_q [E+1][H][I/2] u8,     down_s [E+1][H][I/32] u8.
+ *   FP8: gate_q/up_q [E+1][I][H] u8,   gate_s/up_s [E+1][I/128][H/128] f32,
+ *        down_q [E+1][H][I] u8,       down_s [E+1][H/128][I/128] f32.
+ * The descriptor itself is host memory, read during the call only. */
+typedef struct moe_weights {
+  int32_t format;    /* MOE_W_*                      */
+  int32_t n_experts; /* E, routed experts            */
+  int32_t hidden;    /* H                            */
+  int32_t inter;     /* I, expert intermediate size  */
+  const void* gate_q;
+  const void* gate_s;
+  const void* up_q;
+  const void* up_s;
+  const void* down_q;
+  const void* down_s;
+} moe_weights;
+
+/* Bytes of workspace needed by any call below for up to `max_tokens` tokens
+ * at top-k `top_k` (router partials, quantised activations, routing tables,
+ * intermediate h, y rows, status word).  0 if the arguments are invalid.
+ * Allocate once, call moe_workspace_init once, then reuse for every call
+ * (dpshk.com article, section "核心实现四": workspaces preallocated). */
+size_t moe_workspace_bytes(const moe_weights* w, int32_t max_tokens, int32_t top_k);
+
+/* Enqueue a zero-fill of the workspace's control block (status word and
+ * the counters some kernels keep; they return them to zero themselves).
+ * Call once after allocating a workspace. */
+int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* S1+S2, the router (dpshk.com article, section "核心实现一"; top-6 of 256:
+ * ai-muninn.com "[洋垃圾跑大模型 #3]").
+ *   x        [T][H] bf16 activations
+ *   w_router [H][E] bf16
+ *   topk_ids [T][k] int32 out: experts ordered by (logit desc, id asc)
+ *   topk_w   [T][k] f32 out: sigmoid(logit) renormalised over the k chosen
+ * Logits are fp32 in one fixed order: 64-wide chunk partials, each a chain
+ * of fused multiply-adds in ascending h, summed in ascending chunk order.
+ * ws: workspace of at least moe_workspace_bytes(.., T, k). */
+int moe_route(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H, int32_t E,
+              int32_t k, int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+              void* stream);
+
+/* S3, act_quant (tcti.cn post, section "补齐软件栈缺失"): per row and per
+ * 128 columns, s = amax/448 (fp32, IEEE division) and
+ * q = E4M3(x / s) rounded to nearest even, saturating at +-448, sign kept;
+ * an all-zero block gives s = 0 and q = 0.
+ *   x      [rows][cols] bf16 (x_dtype MOE_DT_BF16) or f32 (MOE_DT_F32)
+ *   q      [rows][cols] u8 E4M3 codes out
+ *   scales [rows][cols/128] f32 out
+ * cols must be a multiple of 128; rows >= 1. */
+int act_quant_fp8(const void* x, int32_t x_dtype, int64_t rows, int32_t cols, uint8_t* q,
+                  float* scales, void* stream);
+
+/* S4, permute (dpshk.com article, section "核心实现三": each expert read
+ * once for all of its tokens): a stable counting sort of the T*k
+ * (token, slot) pairs by expert, tokens ascending within an expert, then
+ * the shared-expert group (index E) holding tokens 0..T-1.
+ *   offsets   [E+2] out: group g is rows offsets[g] .. offsets[g+1]-1
+ *   row_token [T*k+T] out: token of each row
+ *   row_of    [T][k+1] out: row of (t, slot j); row_of[t][k] = shared row;
+ *             -1 for a pair whose id is outside [0, E)
+ * Rows that a dropped pair would have used are never written. */
+int moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* offsets,
+                int32_t* row_token, int32_t* row_of, void* ws, size_t ws_bytes, void* stream);
+
+/* S5+S6, the experts (tcti.cn post, section "补齐软件栈缺失": fp4_gemm and
+ * fp8_gemm; dpshk.com article, section "核心实现四": dequantise inside the
+ * product, gate and up share one quantised input).  For every row r of
+ * group g (expert g, or the shared expert for g = E) and its token t:
+ *   g = W_gate[g] . deq(xq[t]),  u = W_up[g] . deq(xq[t])   (fp32 accumulate)
+ *   h = silu(g) * u, requantised to E4M3 per 128 exactly as act_quant_fp8
+ *   y_rows[r] = W_down[g] . deq(hq)
+ *   xq [T][H] u8, xs [T][H/128] f32 (act_quant_fp8 of x)
+ *   offsets, row_token as produced by moe_permute
+ *   y_rows [T*k+T][H] f32 out (rows of dropped pairs are left untouched)
+ * T <= 1 with k+1 <= 8 and the FP4 format runs the VALU GEMV kernels; any
+ * other shape runs the MFMA grouped GEMM kernels. */
+int moe_expert_ffn(const moe_weights* w, const uint8_t* xq, const float* xs, int32_t T, int32_t k,
+                   const int32_t* offsets, const int32_t* row_token, float* y_rows, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/* S7, combine: out[t] = y_rows[row_of[t][k]] + sum_{j<k} topk_w[t][j] *
+ * y_rows[row_of[t][j]] in fp32 in that order (rows of -1 contribute 0),
+ * written as bf16 (nearest even) or f32.
+ *   out [T][H] (out_dtype MOE_DT_BF16 or MOE_DT_F32) */
+int moe_combine(const float* y_rows, const int32_t* row_of, const float* topk_w, int32_t T,
+                int32_t k, int32_t H, void* out, int32_t out_dtype, void* stream);
+
+/* The whole layer, S1..S7, on x [T][H] bf16 -> out [T][H] (bf16 or f32).
+ * routing_ids/routing_w [T][k] (both NULL, or both set) inject routing
+ * (e.g. a drawn routing, or a speculative-verification batch whose routing
+ * is known, dpshk.com article section "核心实现三"); when NULL the router
+ * runs on x. */
+int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint16_t* x, int32_t T,
+                     int32_t k, const int32_t* routing_ids, const float* routing_w, void* out,
+                     int32_t out_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* A static string naming a status code. */
+const char* moe_status_string(int status);
+
+/* DEBUG/TESTS ONLY -- synchronises `stream`.  Reads the workspace status
+ * word into *status (MOE_STATUS_* bits) and clears it when `clear` != 0. */
+int moe_device_status(void* ws, void* stream, uint32_t* status, int clear);
+
+/* DEBUG/TESTS ONLY -- device pointers to the intermediate activations that
+ * the last moe_expert_ffn / dsv4_moe_forward call with the same (w, T, k)
+ * left in `ws`: h [T*k+T][I] f32 (VALU path only, else NULL), and
+ * hq [T*k+T][I] u8 with hs [T*k+T][I/128] f32 (both paths). */
+int moe_debug_intermediates(const moe_weights* w, int32_t T, int32_t k, void* ws,
+                            size_t ws_bytes, float** h, uint8_t** hq, float** hs);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BEF_MOE_H */

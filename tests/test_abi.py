@@ -1,0 +1,149 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every entry
+point that include/moe.h declares, sizes its workspace, and rejects bad
+arguments on the host before any HIP call is made (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+moe = pytest.importorskip("bit_expert_ffn_moe_amd")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s+\**\s*([a-z_0-9]+)\s*\(", src, re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_documented_entry_points():
+    names = _declared()
+    for n in ["moe_route", "act_quant_fp8", "moe_permute", "moe_expert_ffn", "moe_combine",
+              "dsv4_moe_forward", "moe_workspace_bytes", "moe_workspace_init",
+              "moe_status_string", "moe_device_status", "moe_debug_intermediates"]:
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIBRARY_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in _declared():
+        assert n in exported, n
+        assert hasattr(moe._lib, n)
+    assert set(moe.EXPORTED) == set(_declared())
+
+
+def test_library_links_no_oracle_code():
+    out = subprocess.run(["nm", "-D", moe.LIBRARY_PATH], check=True, capture_output=True,
+                         text=True).stdout
+    assert "orc_" not in out
+    deps = subprocess.run(["ldd", moe.LIBRARY_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in deps
+
+
+def _w(fmt=1, E=256, H=4096, I=2048, ptr=0x10000):
+    return moe.moe_weights(fmt, E, H, I, ptr, ptr, ptr, ptr, ptr, ptr)
+
+
+def test_workspace_bytes_monotone_and_sized():
+    w = _w()
+    b1 = moe.moe_workspace_bytes(w, 1, 6)
+    b32 = moe.moe_workspace_bytes(w, 32, 6)
+    b8k = moe.moe_workspace_bytes(w, 8192, 6)
+    assert 0 < b1 < b32 < b8k
+    R = 8192 * 7
+    assert b8k >= R * 4096 * 4 + R * 2048 + 8192 * 4096   # y rows + hq + xq at least
+    assert moe.moe_workspace_bytes(_w(fmt=7), 1, 6) == 0
+    assert moe.moe_workspace_bytes(w, 0, 6) == 0
+    assert moe.moe_workspace_bytes(w, 1, 300) == 0
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert moe.moe_status_string(s)
+    assert "unknown" in moe.moe_status_string(42)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_x", moe.MOE_EINVAL),
+    ("bad_k", moe.MOE_EINVAL),
+    ("k_over_16", moe.MOE_ENOTSUP),
+    ("h_not_128", moe.MOE_EINVAL),
+    ("misaligned", moe.MOE_EALIGN),
+    ("small_ws", moe.MOE_EWORKSPACE),
+    ("ws_misaligned", moe.MOE_EALIGN),
+])
+def test_route_rejects_bad_arguments_on_host(case, expect):
+    p, ws = 0x100000, 0x200000
+    args = dict(x=p, wr=p, T=4, H=4096, E=256, k=6, ids=p, w=p, ws=ws, wsb=1 << 30)
+    if case == "null_x":
+        args["x"] = None
+    elif case == "bad_k":
+        args["k"] = 0
+    elif case == "k_over_16":
+        args["k"] = 17
+    elif case == "h_not_128":
+        args["H"] = 4000
+    elif case == "misaligned":
+        args["ids"] = p + 4
+    elif case == "small_ws":
+        args["wsb"] = 100
+    elif case == "ws_misaligned":
+        args["ws"] = ws + 16
+    rc = moe.raw_call("moe_route", args["x"], args["wr"], args["T"], args["H"], args["E"],
+                      args["k"], args["ids"], args["w"], args["ws"], args["wsb"], None)
+    assert rc == expect
+
+
+def test_forward_rejects_bad_arguments_on_host():
+    p, ws = 0x100000, 0x200000
+    w = _w(ptr=p)
+    big = 1 << 40
+    f = moe._lib.dsv4_moe_forward
+    # routing ids without weights
+    assert f(ctypes.byref(w), p, p, 4, 6, p, None, p, 2, ws, big, None) == moe.MOE_EINVAL
+    # unknown out dtype
+    assert f(ctypes.byref(w), p, p, 4, 6, None, None, p, 9, ws, big, None) == moe.MOE_EINVAL
+    # unknown weight format
+    w2 = _w(fmt=3, ptr=p)
+    assert f(ctypes.byref(w2), p, p, 4, 6, None, None, p, 2, ws, big, None) == moe.MOE_ENOTSUP
+    # misaligned weight pointer
+    w3 = _w(ptr=p + 8)
+    assert f(ctypes.byref(w3), p, p, 4, 6, None, None, p, 2, ws, big, None) == moe.MOE_EALIGN
+    # too-small workspace
+    assert f(ctypes.byref(w), p, p, 4, 6, None, None, p, 2, ws, 1024, None) == moe.MOE_EWORKSPACE
+    # expert count over the limit, intermediate not a multiple of 128
+    assert f(ctypes.byref(_w(E=300, ptr=p)), p, p, 4, 6, None, None, p, 2, ws, big,
+             None) == moe.MOE_ENOTSUP
+    assert f(ctypes.byref(_w(I=2000, ptr=p)), p, p, 4, 6, None, None, p, 2, ws, big,
+             None) == moe.MOE_EINVAL
+
+
+def test_act_quant_rejects_bad_arguments_on_host():
+    p = 0x100000
+    f = moe._lib.act_quant_fp8
+    assert f(p, 1, 4, 100, p, p, None) == moe.MOE_EINVAL       # cols % 128
+    assert f(p, 5, 4, 128, p, p, None) == moe.MOE_EINVAL       # dtype
+    assert f(p, 1, 0, 128, p, p, None) == moe.MOE_EINVAL       # rows
+    assert f(p + 2, 1, 4, 128, p, p, None) == moe.MOE_EALIGN
+    assert f(None, 1, 4, 128, p, p, None) == moe.MOE_EINVAL
+
+
+def test_permute_and_combine_reject_bad_arguments_on_host():
+    p, ws = 0x100000, 0x200000
+    assert moe._lib.moe_permute(p, 4, 7, 6, p, p, p, ws, 1 << 30, None) == moe.MOE_EINVAL  # k > E
+    assert moe._lib.moe_permute(p, 4, 2, 6, p, p, p, ws, 8, None) == moe.MOE_EWORKSPACE
+    assert moe._lib.moe_combine(p, p, p, 4, 2, 4096, p, 3, None) == moe.MOE_EINVAL
+    assert moe._lib.moe_combine(p, p, p, 4, 2, 4097, p, 2, None) == moe.MOE_EINVAL
+
+
+def test_python_binding_raises_on_error_status():
+    with pytest.raises(moe.MoeError) as ei:
+        moe.act_quant_fp8(0x100000, 1, 4, 100, 0x100000, 0x100000, stream=0)
+    assert ei.value.status == moe.MOE_EINVAL

@@ -1,0 +1,145 @@
+"""End-to-end GPU parity of the whole layer (dsv4_moe_forward) against the
+oracle, on every workload shape; at the full prefill sizes the oracle runs on
+a sample of tokens (chosen to include the most- and least-loaded experts and
+the ragged tails).  Tolerances: relative L2 <= 2e-3 and max-abs <=
+1e-2 * max|ref| on the fp32 output."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import Oracle, Weights
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import bit_expert_ffn_moe_amd as moe  # noqa: E402
+from gpu_util import (DevLayer, bf16_bits_to_f32, f64_to_bf16_bits, max_rel, rel_l2,  # noqa: E402
+                      to_dev, to_host)
+
+orc = Oracle()
+REL_L2, MAX_ABS = 2e-3, 1e-2
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def _check(out, ref, what):
+    e1, e2 = rel_l2(out, ref), max_rel(out, ref)
+    _print(f"{what}: rel_l2={e1:.3e} max_rel={e2:.3e}")
+    assert e1 <= REL_L2, (what, e1)
+    assert e2 <= MAX_ABS, (what, e2)
+
+
+def _sample_tokens(ids, T, n, seed=0):
+    """Tokens touching the most and least loaded experts, the first/last
+    tokens, and random ones."""
+    rng = np.random.default_rng(seed)
+    pick = {0, T - 1}
+    if ids is not None:
+        cnt = np.bincount(ids.ravel(), minlength=ids.max() + 1)
+        hot, cold = int(np.argmax(cnt)), int(np.argmin(np.where(cnt > 0, cnt, 1 << 30)))
+        for e in (hot, cold):
+            ts = np.nonzero((ids == e).any(axis=1))[0]
+            pick.update(ts[:2].tolist())
+            pick.update(ts[-1:].tolist())
+    while len(pick) < min(n, T):
+        pick.add(int(rng.integers(0, T)))
+    return np.array(sorted(pick), np.int32)
+
+
+def _run(name, sample=None, threads=0, **over):
+    L = synth.make_layer(name, **over)
+    wl = L.wl
+    D = DevLayer(L)
+    _print("layer", name, over, "T", wl.T, "fmt", wl.fmt, "routing", wl.routing)
+    out = to_host(D.forward())
+    W = Weights.from_layer(L)
+    tok = None if sample is None else _sample_tokens(L.ids, wl.T, sample)
+    ref = orc.forward(W, L.wr, L.x, wl.k, ids=L.ids, w=L.w, tokens=tok, threads=threads)
+    got = out if tok is None else out[tok]
+    _check(got, ref, f"{name} {over}")
+    return L, D, out, ref, tok
+
+
+@pytest.mark.parametrize("over", [dict(), dict(fmt="fp8"), dict(T=1), dict(T=1, fmt="fp8"),
+                                  dict(T=5), dict(T=130, routing="zipf", zipf_s=1.0),
+                                  dict(E=1, k=1, T=9), dict(E=3, k=3, T=17)])
+def test_tiny_layer(over):
+    _run("tiny_t8", **over)
+
+
+def test_tiny_layer_bf16_output_and_determinism():
+    L = synth.make_layer("tiny_t8", T=40)
+    D = DevLayer(L)
+    a = to_host(D.forward(out_dtype=moe.MOE_DT_BF16))
+    b = to_host(D.forward(out_dtype=moe.MOE_DT_BF16))
+    assert np.array_equal(a, b)
+    f1 = to_host(D.forward())
+    f2 = to_host(D.forward())
+    assert np.array_equal(f1, f2)
+    ref = orc.forward(Weights.from_layer(L), L.wr, L.x, L.wl.k)
+    refb = bf16_bits_to_f32(f64_to_bf16_bits(ref))
+    got = bf16_bits_to_f32(a)
+    assert rel_l2(got, refb) <= 3e-3
+    assert max_rel(got, refb) <= 1.5e-2
+
+
+def test_decode_t1_full_shapes_many_tokens():
+    """One token per call at hidden 4096 / intermediate 2048 / 256 experts top-6."""
+    L = synth.make_layer("decode_t1", T=24)
+    D = DevLayer(L, max_tokens=1)
+    outs = []
+    for t in range(L.wl.T):
+        outs.append(to_host(D.forward(x=D.x[t:t + 1], T=1))[0])
+    out = np.stack(outs)
+    ref = orc.forward(Weights.from_layer(L), L.wr, L.x, L.wl.k)
+    _check(out, ref, "decode_t1 x24")
+    ids = torch.empty((L.wl.T, 6), dtype=torch.int32, device="cuda")
+    w = torch.empty((L.wl.T, 6), dtype=torch.float32, device="cuda")
+    moe.moe_route(D.x, D.wr, L.wl.T, 4096, 256, 6, ids, w, D.ws, D.ws_bytes)
+    ir, _ = orc.route(L.x, L.wr, 6)
+    assert np.array_equal(to_host(ids), ir)
+
+
+def test_verify_t32_full_shapes():
+    _run("verify_t32")
+
+
+def test_prefill_fp4_partial_batch():
+    _run("prefill_fp4_t4096", T=512, sample=24)
+
+
+def test_prefill_fp4_full_sampled():
+    _run("prefill_fp4_t4096", sample=24)
+
+
+def test_prefill_fp8_full_sampled():
+    _run("prefill_fp8_t8192", sample=24)
+
+
+def test_all_tokens_on_the_same_experts():
+    L = synth.make_layer("tiny_t8", T=300, routing="zipf", zipf_s=1.0)
+    L.ids[:] = np.array([5, 2], np.int32)
+    D = DevLayer(L)
+    out = to_host(D.forward())
+    ref = orc.forward(Weights.from_layer(L), L.wr, L.x, 2, ids=L.ids, w=L.w)
+    _check(out, ref, "one group")
+
+
+def test_bad_expert_id_is_skipped_and_flagged():
+    L = synth.make_layer("tiny_t8", T=20, routing="zipf", zipf_s=1.0)
+    L.ids[3, 1] = 99
+    D = DevLayer(L)
+    out = to_host(D.forward())
+    assert moe.moe_device_status(D.ws, clear=True) & moe.MOE_STATUS_BAD_EXPERT_ID
+    assert moe.moe_device_status(D.ws) == 0
+    ids = L.ids.copy()
+    w = L.w.copy()
+    w[3, 1] = 0.0
+    ids[3, 1] = 0          # weight 0: same as skipping the slot
+    ref = orc.forward(Weights.from_layer(L), L.wr, L.x, 2, ids=ids, w=w)
+    _check(out, ref, "bad id")
