@@ -52,6 +52,9 @@ _sigs = {
     "act_quant_fp8": ([_vp, _i32, _i64, _i32, _vp, _vp, _vp], ctypes.c_int),
     "moe_permute": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "moe_expert_ffn": ([_W, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "moe_expert_gate_up": ([_W, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "moe_expert_down": ([_W, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp],
+                        ctypes.c_int),
     "moe_combine": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp], ctypes.c_int),
     "dsv4_moe_forward": ([_W, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _i32, _vp, _sz, _vp],
                          ctypes.c_int),
@@ -136,6 +139,19 @@ def moe_expert_ffn(w, xq, xs, T, k, offsets, row_token, y_rows, ws, ws_bytes, st
     return _check(_lib.moe_expert_ffn(ctypes.byref(w), _ptr(xq), _ptr(xs), T, k, _ptr(offsets),
                                       _ptr(row_token), _ptr(y_rows), _ptr(ws), ws_bytes,
                                       _stream(stream)), "moe_expert_ffn")
+
+
+def moe_expert_gate_up(w, xq, xs, T, k, offsets, row_token, ws, ws_bytes, stream=None) -> int:
+    return _check(_lib.moe_expert_gate_up(ctypes.byref(w), _ptr(xq), _ptr(xs), T, k,
+                                          _ptr(offsets), _ptr(row_token), _ptr(ws), ws_bytes,
+                                          _stream(stream)), "moe_expert_gate_up")
+
+
+def moe_expert_down(w, T, k, offsets, row_of, topk_w, y_rows, out, out_dtype, ws, ws_bytes,
+                    stream=None) -> int:
+    return _check(_lib.moe_expert_down(ctypes.byref(w), T, k, _ptr(offsets), _ptr(row_of),
+                                       _ptr(topk_w), _ptr(y_rows), _ptr(out), out_dtype,
+                                       _ptr(ws), ws_bytes, _stream(stream)), "moe_expert_down")
 
 
 def moe_combine(y_rows, row_of, topk_w, T, k, H, out, out_dtype, stream=None) -> int:

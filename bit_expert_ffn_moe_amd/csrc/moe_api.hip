@@ -168,38 +168,26 @@ T* at(void* ws, size_t off) {
 
 // ---- enqueue helpers (arguments already validated) -----------------------
 
-int enqueue_expert_ffn(const moe_weights* w, const uint8_t* xq, const float* xs, int T, int k,
-                       const int32_t* offsets, const int32_t* row_token, const int32_t* row_of,
-                       const float* topk_w, float* y_rows, void* out, int out_dtype,
-                       const Layout& L, void* ws, hipStream_t st) {
-  const int E = w->n_experts, H = w->hidden, I = w->inter;
-  if (gemv_path(w->format, T, k, H, I)) {
-    GemvArgs a;
-    a.gq = (const uint8_t*)w->gate_q;
-    a.gs = (const uint8_t*)w->gate_s;
-    a.uq = (const uint8_t*)w->up_q;
-    a.us = (const uint8_t*)w->up_s;
-    a.dq = (const uint8_t*)w->down_q;
-    a.ds = (const uint8_t*)w->down_s;
-    a.xq = xq;
-    a.xs = xs;
-    a.offsets = offsets;
-    a.row_token = row_token;
-    a.row_of = row_of;
-    a.topk_w = topk_w;
-    a.E = E, a.H = H, a.I = I, a.k = k;
-    a.n_slots = (T * k < E ? T * k : E) + 1;
-    a.h = at<float>(ws, L.h);
-    a.y_rows = y_rows;
-    a.out = out;
-    a.out_bf16 = out_dtype == MOE_DT_BF16;
-    a.hq_ws = at<uint8_t>(ws, L.hq);
-    a.hs_ws = at<float>(ws, L.hs);
-    int rc = launch_status(launch_gemv_gate_up(a, st));
-    if (rc) return rc;
-    return launch_status(launch_gemv_down(a, out != nullptr, st));
-  }
+GemvArgs gemv_args(const moe_weights* w, int T, int k, const Layout& L, void* ws) {
+  GemvArgs a;
+  memset(&a, 0, sizeof a);
+  a.gq = (const uint8_t*)w->gate_q;
+  a.gs = (const uint8_t*)w->gate_s;
+  a.uq = (const uint8_t*)w->up_q;
+  a.us = (const uint8_t*)w->up_s;
+  a.dq = (const uint8_t*)w->down_q;
+  a.ds = (const uint8_t*)w->down_s;
+  a.E = w->n_experts, a.H = w->hidden, a.I = w->inter, a.k = k;
+  a.n_slots = (T * k < w->n_experts ? T * k : w->n_experts) + 1;
+  a.h = at<float>(ws, L.h);
+  a.hq_ws = at<uint8_t>(ws, L.hq);
+  a.hs_ws = at<float>(ws, L.hs);
+  return a;
+}
+
+GemmArgs gemm_args(const moe_weights* w, int T, int k, const Layout& L, void* ws) {
   GemmArgs g;
+  memset(&g, 0, sizeof g);
   g.fmt = w->format;
   g.gq = (const uint8_t*)w->gate_q;
   g.uq = (const uint8_t*)w->up_q;
@@ -207,21 +195,42 @@ int enqueue_expert_ffn(const moe_weights* w, const uint8_t* xq, const float* xs,
   g.gs = w->gate_s;
   g.us = w->up_s;
   g.ds = w->down_s;
-  g.xq = xq;
-  g.xs = xs;
-  g.offsets = offsets;
-  g.row_token = row_token;
-  g.T = T, g.k = k, g.E = E, g.H = H, g.I = I;
+  g.T = T, g.k = k, g.E = w->n_experts, g.H = w->hidden, g.I = w->inter;
   g.hq = at<uint8_t>(ws, L.hq);
   g.hs = at<float>(ws, L.hs);
-  g.y_rows = y_rows;
-  int rc = launch_status(launch_gemm_gate_up(g, st));
-  if (rc) return rc;
-  rc = launch_status(launch_gemm_down(g, st));
-  if (rc) return rc;
-  if (out) rc = launch_status(launch_combine(y_rows, row_of, topk_w, T, k, H, out,
-                                             out_dtype == MOE_DT_BF16, st));
-  return rc;
+  return g;
+}
+
+// S5: gate + up + SwiGLU (+ requantised h in ws).
+int enqueue_gate_up(const moe_weights* w, const uint8_t* xq, const float* xs, int T, int k,
+                    const int32_t* offsets, const int32_t* row_token, const Layout& L, void* ws,
+                    hipStream_t st) {
+  if (gemv_path(w->format, T, k, w->hidden, w->inter)) {
+    GemvArgs a = gemv_args(w, T, k, L, ws);
+    a.xq = xq, a.xs = xs, a.offsets = offsets, a.row_token = row_token;
+    return launch_status(launch_gemv_gate_up(a, st));
+  }
+  GemmArgs g = gemm_args(w, T, k, L, ws);
+  g.xq = xq, g.xs = xs, g.offsets = offsets, g.row_token = row_token;
+  return launch_status(launch_gemm_gate_up(g, st));
+}
+
+// S6 (+ S7 when out is set): down projection of the h left in ws.
+int enqueue_down(const moe_weights* w, int T, int k, const int32_t* offsets,
+                 const int32_t* row_of, const float* topk_w, float* y_rows, void* out,
+                 int out_dtype, const Layout& L, void* ws, hipStream_t st) {
+  if (gemv_path(w->format, T, k, w->hidden, w->inter)) {
+    GemvArgs a = gemv_args(w, T, k, L, ws);
+    a.offsets = offsets, a.row_of = row_of, a.topk_w = topk_w;
+    a.y_rows = y_rows, a.out = out, a.out_bf16 = out_dtype == MOE_DT_BF16;
+    return launch_status(launch_gemv_down(a, out != nullptr, st));
+  }
+  GemmArgs g = gemm_args(w, T, k, L, ws);
+  g.offsets = offsets, g.y_rows = y_rows;
+  int rc = launch_status(launch_gemm_down(g, st));
+  if (rc || !out) return rc;
+  return launch_status(launch_combine(y_rows, row_of, topk_w, T, k, w->hidden, out,
+                                      out_dtype == MOE_DT_BF16, st));
 }
 
 }  // namespace
@@ -315,8 +324,53 @@ int moe_expert_ffn(const moe_weights* w, const uint8_t* xq, const float* xs, int
   if (rc) return rc;
   rc = check_device();
   if (rc) return rc;
-  return enqueue_expert_ffn(w, xq, xs, T, k, offsets, row_token, nullptr, nullptr, y_rows,
-                            nullptr, 0, L, ws, (hipStream_t)stream);
+  rc = enqueue_gate_up(w, xq, xs, T, k, offsets, row_token, L, ws, (hipStream_t)stream);
+  if (rc) return rc;
+  return enqueue_down(w, T, k, offsets, nullptr, nullptr, y_rows, nullptr, 0, L, ws,
+                      (hipStream_t)stream);
+}
+
+int moe_expert_gate_up(const moe_weights* w, const uint8_t* xq, const float* xs, int32_t T,
+                       int32_t k, const int32_t* offsets, const int32_t* row_token, void* ws,
+                       size_t ws_bytes, void* stream) {
+  int rc = check_weights(w);
+  if (rc) return rc;
+  if (!xq || !xs || !offsets || !row_token) return MOE_EINVAL;
+  rc = check_tk(T, k, w->n_experts);
+  if (rc) return rc;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(offsets) || !aligned16(row_token))
+    return MOE_EALIGN;
+  const Layout L = layout_w(w, T, k);
+  rc = check_ws(ws, ws_bytes, L.end_ffn);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  return enqueue_gate_up(w, xq, xs, T, k, offsets, row_token, L, ws, (hipStream_t)stream);
+}
+
+int moe_expert_down(const moe_weights* w, int32_t T, int32_t k, const int32_t* offsets,
+                    const int32_t* row_of, const float* topk_w, float* y_rows, void* out,
+                    int32_t out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_weights(w);
+  if (rc) return rc;
+  if (!offsets) return MOE_EINVAL;
+  rc = check_tk(T, k, w->n_experts);
+  if (rc) return rc;
+  const bool gv = gemv_path(w->format, T, k, w->hidden, w->inter);
+  if (out) {
+    if (!row_of || !topk_w) return MOE_EINVAL;
+    if (out_dtype != MOE_DT_BF16 && out_dtype != MOE_DT_F32) return MOE_EINVAL;
+    if (!aligned16(out) || !aligned16(row_of) || !aligned16(topk_w)) return MOE_EALIGN;
+  }
+  if (!y_rows && !(gv && out)) return MOE_EINVAL;
+  if (!aligned16(offsets) || (y_rows && !aligned16(y_rows))) return MOE_EALIGN;
+  const Layout L = layout_w(w, T, k);
+  rc = check_ws(ws, ws_bytes, L.end_ffn);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  return enqueue_down(w, T, k, offsets, row_of, topk_w, y_rows, out, out_dtype, L, ws,
+                      (hipStream_t)stream);
 }
 
 int moe_combine(const float* y_rows, const int32_t* row_of, const float* topk_w, int32_t T,
@@ -380,8 +434,10 @@ int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint1
                                     at<int32_t>(ws, L.cnt), at<int32_t>(ws, L.base),
                                     &ctl->status, st));
   if (rc) return rc;
-  return enqueue_expert_ffn(w, xq, xs, T, k, offsets, row_token, row_of, tw, at<float>(ws, L.y),
-                            out, out_dtype, L, ws, st);
+  rc = enqueue_gate_up(w, xq, xs, T, k, offsets, row_token, L, ws, st);
+  if (rc) return rc;
+  return enqueue_down(w, T, k, offsets, row_of, tw, at<float>(ws, L.y), out, out_dtype, L, ws,
+                      st);
 }
 
 const char* moe_status_string(int status) {

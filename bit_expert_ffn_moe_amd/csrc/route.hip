@@ -4,8 +4,8 @@
 // section "核心实现一"); 6 of 256 per token (ai-muninn.com
 // "[洋垃圾跑大模型 #3]").  Logits are fp32 in one fixed order so that the
 // chosen ids are reproducible bit for bit: 64-wide chunk partials, each a
-// chain of fused multiply-adds in ascending h starting from the first
-// product, then the partials summed in ascending chunk order (the row keeps
+// chain of fused multiply-adds in ascending h starting from +0, then the
+// partials summed in ascending chunk order (the row keeps
 // one fixed accumulation order, as dpshk.com "核心实现四" does for its rows).
 // Every kernel below computes exactly that order; they differ only in how
 // the (token, expert, chunk) work is spread over the GPU.
@@ -112,9 +112,18 @@ __global__ __launch_bounds__(256) void route_small_kernel(
   if (!s_last) return;
   __threadfence();
   if (e < E) {
+    // partials of 16 chunks are loaded together, then summed in chunk order
     for (int t = 0; t < T; ++t) {
-      float acc = __builtin_nontemporal_load(&part[(size_t)t * E + e]);
-      for (int cc = 1; cc < nc; ++cc) acc += __builtin_nontemporal_load(&part[((size_t)cc * T + t) * E + e]);
+      float acc = 0.0f;
+      for (int c0 = 0; c0 < nc; c0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          v[i] = (c0 + i < nc) ? part[((size_t)(c0 + i) * T + t) * E + e] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (c0 + i < nc) acc = (c0 + i == 0) ? v[i] : acc + v[i];
+      }
       sz[t][e] = acc;
     }
   }

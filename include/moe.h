@@ -155,6 +155,22 @@ int moe_expert_ffn(const moe_weights* w, const uint8_t* xq, const float* xs, int
                    const int32_t* offsets, const int32_t* row_token, float* y_rows, void* ws,
                    size_t ws_bytes, void* stream);
 
+/* S5 alone: gate + up + SwiGLU for every row, h requantised to E4M3 per 128
+ * and kept in `ws` for moe_expert_down (same kernels moe_expert_ffn runs
+ * first; arguments as moe_expert_ffn). */
+int moe_expert_gate_up(const moe_weights* w, const uint8_t* xq, const float* xs, int32_t T,
+                       int32_t k, const int32_t* offsets, const int32_t* row_token, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* S6 alone (+ S7): the down projection of the h that moe_expert_gate_up left
+ * in `ws` (same T, k, offsets), into y_rows [T*k+T][H] f32.  When `out` is
+ * set the combine (S7) follows, using row_of and topk_w: on the VALU GEMV
+ * path (see moe_expert_ffn) it is fused into the down kernel and y_rows may
+ * be NULL; on the MFMA path y_rows is required and a combine kernel runs. */
+int moe_expert_down(const moe_weights* w, int32_t T, int32_t k, const int32_t* offsets,
+                    const int32_t* row_of, const float* topk_w, float* y_rows, void* out,
+                    int32_t out_dtype, void* ws, size_t ws_bytes, void* stream);
+
 /* S7, combine: out[t] = y_rows[row_of[t][k]] + sum_{j<k} topk_w[t][j] *
  * y_rows[row_of[t][j]] in fp32 in that order (rows of -1 contribute 0),
  * written as bf16 (nearest even) or f32.
