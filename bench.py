@@ -1,10 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the routed-expert MoE FFN layer on one MI355X (gfx950).
 
-A step is one pass of the whole hot path over one batch of synthetic input,
-through the library's C ABI, in the order the whole-layer call enqueues it:
-router (S1-S2) -> act_quant (S3) -> permute (S4) -> gate+up+SwiGLU (S5) ->
-down (S6) + combine (S7).  Inputs are resident in HBM before timing starts.
+A step is one pass of the whole hot path over one batch of synthetic input:
+one dsv4_moe_forward call through the library's C ABI (router S1-S2,
+act_quant S3, permute S4, gate+up+SwiGLU S5, down S6, combine S7); for the
+workloads whose routing is drawn, the router still runs on x first and the
+drawn routing is then injected.  Inputs are resident in HBM before timing starts.
 For single-token decode the step rotates over 64 seeded tokens and over
 several byte-identical copies of the layer's weights at distinct addresses
 (like consecutive layers of a model), so no weight byte can be served from
@@ -12,9 +13,10 @@ the 256 MB Infinity Cache.  Steps are captured once into a HIP graph and the
 graph is replayed, so host launch overhead does not pace the GPU.
 
 Prints ONE JSON line.  `value` is tokens/s of the whole step; `roofline`
-describes the dominant kernel (gate+up): its algorithmic bytes (or flops)
-per launch divided by its average duration, measured with HIP events on the
-launch stream inside the timed replays.  `cpu_baseline` times the oracle on
+describes the dominant kernel (gate+up, S5): its algorithmic bytes (or
+flops) per launch divided by its average duration, measured with HIP events
+on the launch stream around S5 of stage-by-stage steps that run back to back
+behind a backlog of graph replays.  `cpu_baseline` times the oracle on
 a bounded sample on the host cores.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -191,8 +193,22 @@ class Bench:
             return self.x_all[t:t + 1]
         return self.x_all
 
+    def product_step(self, i):
+        """Enqueue step i as the product runs it: one dsv4_moe_forward call
+        (router on x, or -- for drawn routing -- the router on x followed by
+        the forward with the drawn routing injected)."""
+        moe, wl = self.moe, self.wl
+        T, H, E, k = self.T, wl.H, wl.E, wl.k
+        w = self.w[i % len(self.w)]
+        x = self.x_of(i)
+        if self.inj_ids is not None:
+            moe.moe_route(x, self.wr, T, H, E, k, self.ids, self.tw, self.ws, self.ws_bytes,
+                          self.sp)
+        moe.dsv4_moe_forward(w, self.wr, x, T, k, self.inj_ids, self.inj_w, self.out,
+                             moe.MOE_DT_BF16, self.ws, self.ws_bytes, self.sp)
+
     def step(self, i, ev=None):
-        """Enqueue step i on the bench stream (ev: pair recorded around S5)."""
+        """Enqueue step i stage by stage (ev: event pair recorded around S5)."""
         moe, wl = self.moe, self.wl
         T, H, E, k = self.T, wl.H, wl.E, wl.k
         w = self.w[i % len(self.w)]
@@ -226,10 +242,11 @@ def run(args):
     per_graph = max(1, min(per_graph, args.steps))
     # eager warm-up (also caches the library's one-time device check)
     for i in range(max(2, min(args.warmup, 16))):
+        B.product_step(i)
         B.step(i)
     torch.cuda.synchronize()
-    # graph of `per_graph` steps
-    g1, ex1 = B.hip.capture(B.sp, lambda: [B.step(i) for i in range(per_graph)])
+    # graph of `per_graph` product steps
+    g1, ex1 = B.hip.capture(B.sp, lambda: [B.product_step(i) for i in range(per_graph)])
     reps = max(1, args.steps // per_graph)
     steps = reps * per_graph
     wreps = max(1, args.warmup // per_graph)

@@ -90,19 +90,92 @@ __device__ __forceinline__ float dot8_fp4(uint32_t w, h2_t p0, h2_t p1, h2_t p2,
   return acc;
 }
 
-// 32 E2M1 weights (16 bytes) . 32 activations (two Act16) -> fp32.
+// 32 E2M1 weights (16 bytes) . 32 activations (two Act16) -> fp32, as two
+// independent accumulation chains (instruction-level parallelism).
 __device__ __forceinline__ float dot32_fp4(const uint4 w, const Act16& a0, const Act16& a1) {
-  float acc = 0.0f;
-  acc = dot8_fp4(w.x, a0.p[0], a0.p[1], a0.p[2], a0.p[3], acc);
-  acc = dot8_fp4(w.y, a0.p[4], a0.p[5], a0.p[6], a0.p[7], acc);
-  acc = dot8_fp4(w.z, a1.p[0], a1.p[1], a1.p[2], a1.p[3], acc);
-  acc = dot8_fp4(w.w, a1.p[4], a1.p[5], a1.p[6], a1.p[7], acc);
-  return acc;
+  float acc0 = dot8_fp4(w.x, a0.p[0], a0.p[1], a0.p[2], a0.p[3], 0.0f);
+  float acc1 = dot8_fp4(w.z, a1.p[0], a1.p[1], a1.p[2], a1.p[3], 0.0f);
+  acc0 = dot8_fp4(w.y, a0.p[4], a0.p[5], a0.p[6], a0.p[7], acc0);
+  acc1 = dot8_fp4(w.w, a1.p[4], a1.p[5], a1.p[6], a1.p[7], acc1);
+  return acc0 + acc1;
 }
 
 // 2^(b - 127) applied exactly (UE8M0 scale byte b).
 __device__ __forceinline__ float scale_ue8m0(float v, uint32_t b) {
   return __builtin_amdgcn_ldexpf(v, (int)b - 127);
+}
+
+// Cross-lane data movement through DPP (GFX9 encodings: quad_perm, row
+// mirrors, row_bcast15/31).
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, BANK_MASK, true));
+}
+
+// Sum over the 64 lanes, result valid in every lane: pairs, quads, half
+// rows, rows of 16 by DPP, then rows combined through row_bcast15/31 into
+// lane 63, read back as a scalar.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f<0xB1>(v);        // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);        // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);       // row_half_mirror
+  v += dpp_f<0x140>(v);       // row_mirror
+  v += dpp_f<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
+  v += dpp_f<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Butterfly reduce-scatter over the 64 lanes.  Each lane starts with N
+// partial sums v[0..N-1]; at each step it keeps the half of its values picked
+// by one bit of its lane id and adds the partner lane's copy of that half, the
+// partner differing in that bit and agreeing in the bits already used.  xor 32
+// and xor 16 go through ds_bpermute; the lower bits use DPP: row_mirror
+// (i <-> 15-i) flips bit 3, row_half_mirror (i <-> 7-i) flips bit 2, and the
+// quad permutations flip bits 1 and 0 -- each pairing also flips lower bits,
+// which is harmless because those have not been used yet.
+__device__ __forceinline__ float xchg32(float a) { return __shfl_xor(a, 32, kWave); }
+__device__ __forceinline__ float xchg16(float a) { return __shfl_xor(a, 16, kWave); }
+__device__ __forceinline__ float xchg_b3(float a) { return dpp_f<0x140>(a); }
+__device__ __forceinline__ float xchg_b2(float a) { return dpp_f<0x141>(a); }
+__device__ __forceinline__ float xchg_b1(float a) { return dpp_f<0x4E>(a); }
+__device__ __forceinline__ float xchg_b0(float a) { return dpp_f<0xB1>(a); }
+
+// 16 values: on return every lane holds the 64-lane total of value
+// j = 8*bit5 + 4*bit4 + 2*bit3 + bit2 of its lane id.
+__device__ __forceinline__ float butterfly16(const float (&v)[16]) {
+  const int lane = threadIdx.x & 63;
+  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8, b2 = lane & 4;
+  float a[8], b[4], c[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a[j] = (b5 ? v[8 + j] : v[j]) + xchg32(b5 ? v[j] : v[8 + j]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[j] = (b4 ? a[4 + j] : a[j]) + xchg16(b4 ? a[j] : a[4 + j]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) c[j] = (b3 ? b[2 + j] : b[j]) + xchg_b3(b3 ? b[j] : b[2 + j]);
+  float d = (b2 ? c[1] : c[0]) + xchg_b2(b2 ? c[0] : c[1]);
+  d += xchg_b1(d);
+  d += xchg_b0(d);
+  return d;
+}
+
+// 32 values: every lane ends with the total of value
+// j = 16*bit5 + 8*bit4 + 4*bit3 + 2*bit2 + bit1 of its lane id.
+__device__ __forceinline__ float butterfly32(const float (&v)[32]) {
+  const int lane = threadIdx.x & 63;
+  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+  float a[16], b[8], c[4], d[2];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) a[j] = (b5 ? v[16 + j] : v[j]) + xchg32(b5 ? v[j] : v[16 + j]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) b[j] = (b4 ? a[8 + j] : a[j]) + xchg16(b4 ? a[j] : a[8 + j]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c[j] = (b3 ? b[4 + j] : b[j]) + xchg_b3(b3 ? b[j] : b[4 + j]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) d[j] = (b2 ? c[2 + j] : c[j]) + xchg_b2(b2 ? c[j] : c[2 + j]);
+  float e = (b1 ? d[1] : d[0]) + xchg_b1(b1 ? d[0] : d[1]);
+  e += xchg_b0(e);
+  return e;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

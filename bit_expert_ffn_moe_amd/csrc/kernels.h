@@ -10,12 +10,14 @@ constexpr int kPermuteSmallPairs = 2048;  // permute: single block up to this ma
 constexpr int kPermuteTokBlock = 256;     // permute: tokens per block above that
 constexpr int kGemvMaxRows = 8;           // VALU GEMV path: rows (k + 1) per token
 constexpr int kGemmBM = 128;              // MFMA grouped GEMM: tokens per tile
+constexpr int kGemvRun = 8;               // VALU GEMV: weight rows streamed per wave
 constexpr uint32_t MOE_STATUS_BAD_EXPERT_ID_DEV = 1u;
 
 struct GemvArgs {
   const uint8_t *gq, *gs, *uq, *us, *dq, *ds;
   const uint8_t* xq;
   const float* xs;
+  const int4* active;      // set: {group, first row, end row} per slot
   const int32_t *offsets, *row_token, *row_of;
   const float* topk_w;
   int E, H, I, k, n_slots;
@@ -39,6 +41,28 @@ struct GemmArgs {
   float* hs;
   float* y_rows;
 };
+
+// Small-T front of the layer: router (+ act_quant of x when xq is set,
+// + permutation tables when offsets is set).
+struct FrontArgs {
+  const uint16_t* x;
+  const uint16_t* wr;
+  int T, H, E, k;
+  float* part;
+  uint32_t* counter;
+  int32_t* ids;
+  float* w;
+  uint8_t* xq;
+  float* xs;
+  int32_t *offsets, *row_token, *row_of;
+  int4* active;           // routed groups {group, first row, end row}, -1 padded
+  int n_active_slots;
+  // shared expert's gate+up rows run in the same kernel when sh_h is set
+  const uint8_t *sh_gq, *sh_gs, *sh_uq, *sh_us;
+  int I;
+  float* sh_h;
+};
+hipError_t launch_route_front(const FrontArgs& a, hipStream_t st);
 
 hipError_t launch_act_quant(const void* x, bool bf16, int64_t rows, int32_t cols, uint8_t* q,
                             float* s, hipStream_t st);

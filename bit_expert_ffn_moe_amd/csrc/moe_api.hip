@@ -36,7 +36,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // layer call: control | permute scratch (T, E) | router partials (T, H, E) |
 // everything else (needs the weights' shapes).
 struct Layout {
-  size_t ctl, cnt, base, part, ids, w, xq, xs, offsets, row_token, row_of, h, hq, hs, y, total;
+  size_t ctl, cnt, base, part, ids, w, xq, xs, offsets, row_token, row_of, active, h, hq, hs, y,
+      total;
   size_t end_permute, end_route, end_ffn;
 };
 
@@ -74,6 +75,8 @@ Layout layout_for(int E, int H, int I, int T, int k, bool with_h) {
   o += up(R * 4);
   L.row_of = o;
   o += up((size_t)T * (k + 1) * 4);
+  L.active = o;
+  o += up((size_t)(E + 1) * 16);
   L.h = o;
   if (with_h) o += up(R * I * 4);
   L.hq = o;
@@ -414,6 +417,50 @@ int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint1
   WsCtl* ctl = at<WsCtl>(ws, L.ctl);
   const int32_t* ids = routing_ids;
   const float* tw = routing_w;
+  uint8_t* xq = at<uint8_t>(ws, L.xq);
+  float* xs = at<float>(ws, L.xs);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* row_token = at<int32_t>(ws, L.row_token);
+  int32_t* row_of = at<int32_t>(ws, L.row_of);
+  if (!ids && T <= kRouteSmallT) {
+    FrontArgs fa = {};
+    fa.x = x, fa.wr = w_router, fa.T = T, fa.H = H, fa.E = E, fa.k = k;
+    fa.part = at<float>(ws, L.part), fa.counter = &ctl->route_done;
+    fa.ids = at<int32_t>(ws, L.ids), fa.w = at<float>(ws, L.w);
+    fa.offsets = offsets, fa.row_token = row_token, fa.row_of = row_of;
+    if (gemv_path(w->format, T, k, H, w->inter)) {
+      // one token on the VALU path: the front kernel also quantises x, runs
+      // the shared expert's gate+up (its waves quantise x themselves, same
+      // rule) and lists the routed groups for the gate+up kernel
+      fa.sh_gq = (const uint8_t*)w->gate_q;  // the kernel reads group E (the shared expert)
+      fa.sh_uq = (const uint8_t*)w->up_q;
+      fa.sh_gs = (const uint8_t*)w->gate_s;
+      fa.sh_us = (const uint8_t*)w->up_s;
+      fa.I = w->inter;
+      fa.sh_h = at<float>(ws, L.h);
+      fa.active = at<int4>(ws, L.active);
+      fa.n_active_slots = (T * k < E ? T * k : E);
+      fa.xq = xq, fa.xs = xs;  // act_quant blocks run in the same kernel
+      rc = launch_status(launch_route_front(fa, st));
+      if (rc) return rc;
+      GemvArgs a = gemv_args(w, T, k, L, ws);
+      a.xq = xq, a.xs = xs, a.offsets = offsets, a.row_token = row_token;
+      a.active = at<int4>(ws, L.active);
+      a.n_slots = fa.n_active_slots;
+      rc = launch_status(launch_gemv_gate_up(a, st));
+      if (rc) return rc;
+      return enqueue_down(w, T, k, offsets, row_of, fa.w, at<float>(ws, L.y), out, out_dtype, L,
+                          ws, st);
+    }
+    // router + act_quant + permute in one kernel
+    fa.xq = xq, fa.xs = xs;
+    rc = launch_status(launch_route_front(fa, st));
+    if (rc) return rc;
+    rc = enqueue_gate_up(w, xq, xs, T, k, offsets, row_token, L, ws, st);
+    if (rc) return rc;
+    return enqueue_down(w, T, k, offsets, row_of, fa.w, at<float>(ws, L.y), out, out_dtype, L,
+                        ws, st);
+  }
   if (!ids) {
     int32_t* ids_ws = at<int32_t>(ws, L.ids);
     float* w_ws = at<float>(ws, L.w);
@@ -423,13 +470,8 @@ int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint1
     ids = ids_ws;
     tw = w_ws;
   }
-  uint8_t* xq = at<uint8_t>(ws, L.xq);
-  float* xs = at<float>(ws, L.xs);
   rc = launch_status(launch_act_quant(x, true, T, H, xq, xs, st));
   if (rc) return rc;
-  int32_t* offsets = at<int32_t>(ws, L.offsets);
-  int32_t* row_token = at<int32_t>(ws, L.row_token);
-  int32_t* row_of = at<int32_t>(ws, L.row_of);
   rc = launch_status(launch_permute(ids, T, k, E, offsets, row_token, row_of,
                                     at<int32_t>(ws, L.cnt), at<int32_t>(ws, L.base),
                                     &ctl->status, st));

@@ -15,6 +15,7 @@
 #include <float.h>
 
 #include "common.h"
+#include "gemv_body.h"
 #include "kernels.h"
 
 namespace bef {
@@ -70,67 +71,188 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, in
 }
 
 // ---------------------------------------------------------------------------
-// Small T (decode, T <= kRouteSmallT): block c computes the chunk-c partials
-// of every (token, expert) -- thread e reads column e of the router, so a
-// block streams 64 rows x E bf16 with coalesced loads -- and the last block
-// to finish (arrival counter in the workspace) sums the partials in chunk
-// order and runs the top-k.  The counter is returned to zero by that block.
+// Small T (decode, T <= kRouteSmallT): the front of the layer in one kernel.
+//  * Blocks 0 .. H/64-1: block c computes the chunk-c partials of every
+//    (token, expert) -- thread e streams column e of the router, all 64 loads
+//    issued before the multiply-adds.
+//  * When sh_h is set (single-token FP4 path), the next I/(4 RUN) blocks per
+//    token run the shared expert's gate+up GEMV rows (it needs no routing):
+//    its 8.9 MB stream overlaps the router's reduction chain.
+//  * Then, when xq is set, act_quant blocks of x (16 lanes per 128-block).
+//  * The last router block to arrive (arrival counter in the workspace,
+//    returned to zero by that block) sums the partials in chunk order, ranks
+//    the logits (thread e counts the logits that beat its own: larger, or
+//    equal with a lower id), computes the weights and, when asked, writes the
+//    permutation tables (the single-block form of S4) and the list of active
+//    routed groups.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void route_small_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int H, int E, int k,
-    float* __restrict__ part /* [H/64][T][E] */, uint32_t* __restrict__ counter,
-    int32_t* __restrict__ ids, float* __restrict__ w) {
+template <int NB>
+__global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
+  const int nc = a.H / 64;
+  const int tid = threadIdx.x;
+  const int T = a.T, H = a.H, E = a.E, k = a.k;
+  int b = (int)blockIdx.x - nc;
+  if (b >= 0 && a.sh_h) {
+    const int bpg = a.I / (4 * kGemvRun);
+    if (b < bpg * T) {
+      const int t = b / bpg, lane = tid & 63, wv = tid >> 6;
+      const int n0 = ((b - t * bpg) * 4 + wv) * kGemvRun;
+      const GUWeights w = {a.sh_gq, a.sh_gs, a.sh_uq, a.sh_us, E, H, a.I};
+      Act16 a0[NB], a1[NB];
+      float xsc[NB];
+      act_from_bf16<NB>(a.x + (size_t)t * H, H, lane, a0, a1, xsc);
+      gate_up_rows<NB, 3>(w, E, n0, T * k + t, lane, a0, a1, xsc, a.sh_h);
+      return;
+    }
+    b -= bpg * T;
+  }
+  if (b >= 0) {
+    // act_quant of x: 16 lanes per 128-block, 8 elements per lane
+    const int64_t gt = (int64_t)b * 256 + tid;
+    const int64_t blk = gt >> 4;
+    const int64_t nblocks = (int64_t)T * (H / 128);
+    const bool valid = blk < nblocks;
+    float v[8];
+    if (valid) {
+      const uint4 r = reinterpret_cast<const uint4*>(a.x)[gt];
+      v[0] = bf16_to_f32(r.x & 0xffffu), v[1] = bf16_to_f32(r.x >> 16);
+      v[2] = bf16_to_f32(r.y & 0xffffu), v[3] = bf16_to_f32(r.y >> 16);
+      v[4] = bf16_to_f32(r.z & 0xffffu), v[5] = bf16_to_f32(r.z >> 16);
+      v[6] = bf16_to_f32(r.w & 0xffffu), v[7] = bf16_to_f32(r.w >> 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = group_max<16>(amax);
+    const float sc = amax / 448.0f;
+    uint32_t lo = 0, hi = 0;
+    if (amax != 0.0f) {
+      lo = e4m3_pack4(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
+      hi = e4m3_pack4(v[4] / sc, v[5] / sc, v[6] / sc, v[7] / sc);
+    }
+    if (valid) {
+      reinterpret_cast<uint2*>(a.xq)[gt] = make_uint2(lo, hi);
+      if ((tid & 15) == 0) a.xs[blk] = sc;
+    }
+    return;
+  }
   const int c = blockIdx.x;
-  const int nc = gridDim.x;
-  const int e = threadIdx.x;
+  const int e = tid;
   __shared__ float sx[kRouteSmallT][64];
-  __shared__ float sz[kRouteSmallT][256];
+  __shared__ __align__(16) float sz[kRouteSmallT][256];
+  __shared__ int s_ids[kRouteSmallT][16];
+  __shared__ float s_zs[kRouteSmallT][16];
+  __shared__ int stmp[8];
   __shared__ int s_last;
-  for (int i = threadIdx.x; i < T * 64; i += 256)
-    sx[i / 64][i % 64] = bf16_to_f32(x[(size_t)(i / 64) * H + 64 * c + (i % 64)]);
+  for (int i = tid; i < T * 64; i += 256)
+    sx[i / 64][i % 64] = bf16_to_f32(a.x[(size_t)(i / 64) * H + 64 * c + (i % 64)]);
+  uint32_t wv[64];
+  if (e < E) {
+    const uint16_t* col = a.wr + (size_t)(64 * c) * E + e;
+#pragma unroll
+    for (int h = 0; h < 64; ++h) wv[h] = col[(size_t)h * E];
+  }
   __syncthreads();
   if (e < E) {
-    float p[kRouteSmallT];
+    for (int t = 0; t < T; ++t) {
+      float p = 0.0f;
 #pragma unroll
-    for (int t = 0; t < kRouteSmallT; ++t) p[t] = 0.0f;
-    const uint16_t* col = wr + (size_t)(64 * c) * E + e;
-#pragma unroll 8
-    for (int h = 0; h < 64; ++h) {
-      const float wv = bf16_to_f32(col[(size_t)h * E]);
-#pragma unroll
-      for (int t = 0; t < kRouteSmallT; ++t)
-        if (t < T) p[t] = fmaf(sx[t][h], wv, p[t]);
+      for (int h = 0; h < 64; ++h) p = fmaf(sx[t][h], bf16_to_f32(wv[h]), p);
+      a.part[((size_t)c * T + t) * E + e] = p;
     }
-#pragma unroll
-    for (int t = 0; t < kRouteSmallT; ++t)
-      if (t < T) part[((size_t)c * T + t) * E + e] = p[t];
   }
   __threadfence();
   __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(counter, 1u) == (uint32_t)(nc - 1));
+  if (tid == 0) s_last = (atomicAdd(a.counter, 1u) == (uint32_t)(nc - 1));
   __syncthreads();
   if (!s_last) return;
   __threadfence();
-  if (e < E) {
-    // partials of 16 chunks are loaded together, then summed in chunk order
-    for (int t = 0; t < T; ++t) {
-      float acc = 0.0f;
-      for (int c0 = 0; c0 < nc; c0 += 16) {
-        float v[16];
+  for (int t = 0; t < T; ++t) {
+    float acc = -INFINITY;  // experts beyond E never rank
+    if (e < E) {
+      acc = 0.0f;
+      for (int c0 = 0; c0 < nc; c0 += 64) {
+        float v[64];
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          v[i] = (c0 + i < nc) ? part[((size_t)(c0 + i) * T + t) * E + e] : 0.0f;
+        for (int i = 0; i < 64; ++i)
+          v[i] = (c0 + i < nc) ? a.part[((size_t)(c0 + i) * T + t) * E + e] : 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
+        for (int i = 0; i < 64; ++i)
           if (c0 + i < nc) acc = (c0 + i == 0) ? v[i] : acc + v[i];
       }
-      sz[t][e] = acc;
+    }
+    sz[t][e] = acc;
+  }
+  __syncthreads();
+  // ranks: order (logit desc, id asc); the comparisons read 4 logits at a time
+  if (e < E) {
+    const int E4 = (E + 3) >> 2;
+    for (int t = 0; t < T; ++t) {
+      const float z = sz[t][e];
+      const float4* z4 = reinterpret_cast<const float4*>(sz[t]);
+      int rank = 0;
+#pragma unroll 8
+      for (int f4 = 0; f4 < E4; ++f4) {
+        const float4 q = z4[f4];
+        const int f = 4 * f4;
+        rank += (q.x > z) || (q.x == z && f < e);
+        rank += (q.y > z) || (q.y == z && f + 1 < e);
+        rank += (q.z > z) || (q.z == z && f + 2 < e);
+        rank += (q.w > z) || (q.w == z && f + 3 < e);
+      }
+      if (rank < k) {
+        s_ids[t][rank] = e;
+        s_zs[t][rank] = z;
+      }
     }
   }
   __syncthreads();
-  const int wv = threadIdx.x >> 6;
-  if (wv < T) topk_wave(sz[wv], E, k, ids + (size_t)wv * k, w + (size_t)wv * k);
-  if (threadIdx.x == 0) *counter = 0u;
+  if (tid < T * k) {
+    const int t = tid / k, j = tid % k;
+    float sum = 0.0f;
+    for (int i = 0; i < k; ++i) sum += 1.0f / (1.0f + expf(-s_zs[t][i]));
+    const float sg = 1.0f / (1.0f + expf(-s_zs[t][j]));
+    a.ids[tid] = s_ids[t][j];
+    a.w[tid] = sg / sum;
+  }
+  if (a.offsets) {
+    // permutation tables (all ids valid here: they come from the ranking)
+    int cnt = 0;
+    if (e < E)
+      for (int p = 0; p < T * k; ++p) cnt += (s_ids[p / k][p % k] == e);
+    int total;
+    const int pre = block256_exclusive_scan(e < E ? cnt : 0, stmp, &total);
+    if (e < E) a.offsets[e] = pre;
+    if (tid == 0) {
+      a.offsets[E] = total;
+      a.offsets[E + 1] = total + T;
+    }
+    if (e < E && cnt > 0) {
+      int r = pre;
+      for (int p = 0; p < T * k; ++p) {
+        if (s_ids[p / k][p % k] == e) {
+          a.row_token[r] = p / k;
+          a.row_of[(size_t)(p / k) * (k + 1) + (p % k)] = r;
+          ++r;
+        }
+      }
+    }
+    if (tid < T) {
+      a.row_token[total + tid] = tid;
+      a.row_of[(size_t)tid * (k + 1) + k] = total + tid;
+    }
+    if (a.active) {
+      int n_act;
+      const int slot = block256_exclusive_scan((e < E && cnt > 0) ? 1 : 0, stmp, &n_act);
+      if (e < E && cnt > 0) a.active[slot] = make_int4(e, pre, pre + cnt, 0);
+      for (int i = n_act + tid; i < a.n_active_slots; i += 256)
+        a.active[i] = make_int4(-1, 0, 0, 0);
+    }
+  }
+  if (tid == 0) *a.counter = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -225,11 +347,27 @@ __global__ __launch_bounds__(256) void route_tile_kernel(const uint16_t* __restr
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int H, int E, int k,
                         int32_t* ids, float* w, float* part, uint32_t* counter, hipStream_t st) {
   if (T <= kRouteSmallT) {
-    route_small_kernel<<<dim3(H / 64), dim3(256), 0, st>>>(x, wr, T, H, E, k, part, counter, ids,
-                                                           w);
-  } else {
-    route_tile_kernel<<<dim3((T + 31) / 32), dim3(256), 0, st>>>(x, wr, T, H, E, k, ids, w);
+    FrontArgs a = {};
+    a.x = x, a.wr = wr, a.T = T, a.H = H, a.E = E, a.k = k;
+    a.part = part, a.counter = counter, a.ids = ids, a.w = w;
+    return launch_route_front(a, st);
   }
+  route_tile_kernel<<<dim3((T + 31) / 32), dim3(256), 0, st>>>(x, wr, T, H, E, k, ids, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_front(const FrontArgs& a, hipStream_t st) {
+  int nq = 0, nsh = 0;
+  if (a.xq) nq = (int)(((int64_t)a.T * (a.H / 128) * 16 + 255) / 256);
+  if (a.sh_h) nsh = (a.I / (4 * kGemvRun)) * a.T;
+  const dim3 grid(a.H / 64 + nsh + nq);
+  const int nb = (a.H / 32 + 63) / 64;
+  if (nb <= 1)
+    route_front_kernel<1><<<grid, dim3(256), 0, st>>>(a);
+  else if (nb <= 2)
+    route_front_kernel<2><<<grid, dim3(256), 0, st>>>(a);
+  else
+    route_front_kernel<4><<<grid, dim3(256), 0, st>>>(a);
   return hipGetLastError();
 }
 
