@@ -88,7 +88,7 @@ def src_hash():
 
 class Hip:
     def __init__(self):
-        L = ctypes.CDLL("libamdhip64.so")
+        L = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch loaded
         vp, pvp = ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)
         for name, args in [("hipStreamBeginCapture", [vp, ctypes.c_int]),
                            ("hipStreamEndCapture", [vp, pvp]),

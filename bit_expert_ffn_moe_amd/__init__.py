@@ -20,11 +20,17 @@ _SO = os.path.join(_PKG, "libbefmoe.so")
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EALIGN, MOE_EWORKSPACE, MOE_ELAUNCH = 0, -1, -2, -3, -4, -5
 MOE_W_FP4_E2M1_UE8M0_K32, MOE_W_FP8_E4M3_F32_B128 = 1, 2
 MOE_DT_BF16, MOE_DT_F32 = 1, 2
-MOE_STATUS_BAD_EXPERT_ID = 1
+MOE_STATUS_BAD_EXPERT_ID, MOE_STATUS_SYNC_TIMEOUT = 1, 2
 
 if not os.path.exists(_SO):
     raise ImportError(
         f"{_SO} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+# torch first: its HIP runtime (libamdhip64.so.7) must be the one the library
+# binds to.  Loaded the other way round, torch's own libraries (which ask for
+# the unversioned name) would bring in a second runtime beside ours, and
+# device pointers and streams of one would be invalid in the other.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(_SO)
 LIBRARY_PATH = _SO
 

@@ -205,6 +205,12 @@ struct WsCtl {
   uint32_t status;
   uint32_t route_done;  // arrival counter of the small-T router
   uint32_t pad[62];
+  // one-token GEMV path: arrival counters of the blocks that produce each
+  // 128-wide block of h, [row 8][4096/128], then the tagged h slots
+  // [row 8][4096] (see publish_h)
+  uint32_t hq_arrive[8 * 32];
+  uint32_t pad2[256];
+  uint64_t h_slots[8 * 4096];
 };
 
 __device__ __forceinline__ void set_status(uint32_t* st, uint32_t bit) { atomicOr(st, bit); }

@@ -25,16 +25,19 @@ namespace bef {
 // group and rows come from `active` ({group, first row, end row}, written by
 // the front kernel) or, without it, from the offsets table (no host round
 // trip either way).  Wave w streams RUN rows from n0 = (4 (b mod bpg) + w) RUN
-// for every activation row of the group, activations from xq/xs.
+// for every activation row of the group, activations from xq/xs; the last
+// block of each 128-wide block of h requantises it (publish_h).
 // ---------------------------------------------------------------------------
 template <int NB, int DEPTH>
 __global__ __launch_bounds__(256) void gemv_gate_up_fp4_kernel(
     GUWeights w, const uint8_t* __restrict__ xq, const float* __restrict__ xs,
     const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ row_token, const int4* __restrict__ active,
-    float* __restrict__ h) {
+    HExchange hx) {
   __shared__ int stmp[8];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  __shared__ uint32_t s_ticket;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
   constexpr int RUN = kGemvRun;
   const int bpg = w.I / (4 * RUN);
   const int slot = blockIdx.x / bpg;
@@ -49,37 +52,36 @@ __global__ __launch_bounds__(256) void gemv_gate_up_fp4_kernel(
     if (g >= 0) r0 = offsets[g], r1 = offsets[g + 1];
   }
   if (g < 0) return;
-  const int n0 = ((blockIdx.x - slot * bpg) * 4 + wv) * RUN;
+  const int n0b = (blockIdx.x - slot * bpg) * 4 * RUN;
+  const int n0 = n0b + wv * RUN;
   for (int r = r0; r < r1; ++r) {
     const int t = row_token[r];
     Act16 a0[NB], a1[NB];
     float xsc[NB];
     act_from_codes<NB>(xq + (size_t)t * w.H, xs + (size_t)t * (w.H >> 7), w.H, lane, a0, a1, xsc);
-    gate_up_rows<NB, DEPTH>(w, g, n0, r, lane, a0, a1, xsc, h);
+    const float hv = gate_up_rows<NB, DEPTH>(w, g, n0, lane, a0, a1, xsc);
+    publish_h(hx, hv, r, w.I, n0, n0b, tid, lane, &s_ticket);
   }
 }
 
 // ---------------------------------------------------------------------------
 // down (+ combine for a single token).  Wave w of block b owns output rows
 // m = (4b + w)*RUN .. +RUN-1.  Once the row -> expert map is known, every
-// W_down load of the wave (R rows x RUN outputs, one 16-byte chunk per lane
-// for I = 2048) is issued; while they fly the block requantises all R rows
-// of h to E4M3 per 128 into LDS (the act_quant rule; block 0 also stores the
-// codes/scales to the workspace for inspection).  COMBINE writes
-// out[m] = y[shared] + sum_j w_j y[row_of[j]] (T = 1); otherwise y_rows.
+// load of the wave is issued at once: the E4M3 codes and scales of h (R rows,
+// requantised by the gate+up kernel), then every W_down chunk (R rows x RUN
+// outputs, one 16-byte chunk per lane for I = 2048) with its UE8M0 scale.
+// COMBINE writes out[m] = y[shared] + sum_j w_j y[row_of[j]] (T = 1);
+// otherwise y_rows.
 // ---------------------------------------------------------------------------
 template <int NB, int RMAX, int RUN, bool COMBINE>
 __global__ __launch_bounds__(256) void gemv_down_fp4_kernel(
-    const uint8_t* __restrict__ dq, const uint8_t* __restrict__ ds, const float* __restrict__ h,
+    const uint8_t* __restrict__ dq, const uint8_t* __restrict__ ds,
+    const uint8_t* __restrict__ hq, const float* __restrict__ hs,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_of,
     const float* __restrict__ topk_w, int E, int H, int I, int k, float* __restrict__ y_rows,
-    void* __restrict__ out, int out_bf16, uint8_t* __restrict__ hq_ws,
-    float* __restrict__ hs_ws) {
-  extern __shared__ __align__(16) uint8_t smem[];
+    void* __restrict__ out, int out_bf16) {
   __shared__ int s_rowexp[RMAX];
-  const int R = offsets[E + 1];
-  uint8_t* s_hq = smem;                                            // [R][I]
-  float* s_hs = reinterpret_cast<float*>(smem + (size_t)RMAX * I);  // [R][I/128]
+  const int R = min(offsets[E + 1], RMAX);
   const int tid = threadIdx.x;
   for (int g = tid; g <= E; g += 256) {
     const int a = offsets[g], b = offsets[g + 1];
@@ -87,10 +89,27 @@ __global__ __launch_bounds__(256) void gemv_down_fp4_kernel(
   }
   __syncthreads();
 
-  const int lane = tid & 63, wv = tid >> 6;
+  const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m0 = (blockIdx.x * 4 + wv) * RUN;
   const int nch = I >> 5;
   const size_t rowq = (size_t)(I >> 1), rows_ = (size_t)nch;
+  // chunk indices clamped into the row (unconditional loads); a chunk past
+  // the end gets scale 0 and adds exactly 0
+  int ch[NB];
+#pragma unroll
+  for (int c = 0; c < NB; ++c) ch[c] = min(lane + 64 * c, nch - 1);
+  uint4 aq[RMAX][NB][2];
+  float asc[RMAX][NB];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r)
+    if (r < R)
+#pragma unroll
+      for (int c = 0; c < NB; ++c) {
+        const uint8_t* p = hq + (size_t)r * I + 32 * ch[c];
+        aq[r][c][0] = *reinterpret_cast<const uint4*>(p);
+        aq[r][c][1] = *reinterpret_cast<const uint4*>(p + 16);
+        asc[r][c] = hs[r * (I >> 7) + (ch[c] >> 2)];
+      }
   uint4 w[RMAX][RUN][NB];
   uint32_t sb[RMAX][RUN][NB];
 #pragma unroll
@@ -101,59 +120,11 @@ __global__ __launch_bounds__(256) void gemv_down_fp4_kernel(
       for (int i = 0; i < RUN; ++i)
 #pragma unroll
         for (int c = 0; c < NB; ++c) {
-          const int ch = lane + 64 * c;
-          if (ch < nch) {
-            w[r][i][c] = *reinterpret_cast<const uint4*>(dq + (row0 + i) * rowq + 16 * ch);
-            sb[r][i][c] = ds[(row0 + i) * rows_ + ch];
-          } else {
-            w[r][i][c] = make_uint4(0, 0, 0, 0);
-            sb[r][i][c] = 127;
-          }
+          w[r][i][c] = *reinterpret_cast<const uint4*>(dq + (row0 + i) * rowq + 16 * ch[c]);
+          sb[r][i][c] = ds[(row0 + i) * rows_ + ch[c]];
         }
     }
   }
-  // requantise h: 16 lanes per 128-block, 8 elements per lane; the loads of
-  // QB chunks per thread are issued together before any is quantised
-  const int nq = R * (I >> 3);
-  constexpr int QB = 8;
-  for (int base = 0; base < nq; base += 256 * QB) {
-    float4 p[QB][2];
-#pragma unroll
-    for (int q = 0; q < QB; ++q) {
-      const int idx = base + q * 256 + tid;
-      if (idx < nq) {
-        p[q][0] = reinterpret_cast<const float4*>(h)[2 * idx];
-        p[q][1] = reinterpret_cast<const float4*>(h)[2 * idx + 1];
-      } else {
-        p[q][0] = p[q][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < QB; ++q) {
-      const int idx = base + q * 256 + tid;
-      const float v[8] = {p[q][0].x, p[q][0].y, p[q][0].z, p[q][0].w,
-                          p[q][1].x, p[q][1].y, p[q][1].z, p[q][1].w};
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-      amax = group_max<16>(amax);
-      const float sc = amax / 448.0f;
-      uint32_t lo = 0, hi = 0;
-      if (amax != 0.0f) {
-        lo = e4m3_pack4(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
-        hi = e4m3_pack4(v[4] / sc, v[5] / sc, v[6] / sc, v[7] / sc);
-      }
-      if (idx < nq) {
-        reinterpret_cast<uint2*>(s_hq)[idx] = make_uint2(lo, hi);
-        if ((idx & 15) == 0) s_hs[idx >> 4] = sc;
-        if (blockIdx.x == 0) {
-          reinterpret_cast<uint2*>(hq_ws)[idx] = make_uint2(lo, hi);
-          if ((idx & 15) == 0) hs_ws[idx >> 4] = sc;
-        }
-      }
-    }
-  }
-  __syncthreads();
 
   // per-lane partials of y[r][i] (r < RMAX rows, i < RUN outputs), one
   // butterfly, then every lane holds the total of j = r*RUN + i
@@ -164,30 +135,15 @@ __global__ __launch_bounds__(256) void gemv_down_fp4_kernel(
 #pragma unroll
     for (int i = 0; i < RUN; ++i) part[r * RUN + i] = 0.0f;
     if (r < R) {
-      Act16 a0[NB], a1[NB];
-      float hsc[NB];
 #pragma unroll
       for (int c = 0; c < NB; ++c) {
-        const int ch = lane + 64 * c;
-        if (ch < nch) {
-          const uint4 q0 = *reinterpret_cast<const uint4*>(s_hq + (size_t)r * I + 32 * ch);
-          const uint4 q1 = *reinterpret_cast<const uint4*>(s_hq + (size_t)r * I + 32 * ch + 16);
-          e4m3x16_to_h2(q0, a0[c]);
-          e4m3x16_to_h2(q1, a1[c]);
-          hsc[c] = s_hs[r * (I >> 7) + (ch >> 2)];
-        } else {
-          e4m3x16_to_h2(make_uint4(0, 0, 0, 0), a0[c]);
-          e4m3x16_to_h2(make_uint4(0, 0, 0, 0), a1[c]);
-          hsc[c] = 0.0f;
-        }
-      }
+        Act16 a0, a1;
+        e4m3x16_to_h2(aq[r][c][0], a0);
+        e4m3x16_to_h2(aq[r][c][1], a1);
+        const float hsc = (lane + 64 * c < nch) ? asc[r][c] : 0.0f;
 #pragma unroll
-      for (int i = 0; i < RUN; ++i) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int c = 0; c < NB; ++c)
-          acc += scale_ue8m0(dot32_fp4(w[r][i][c], a0[c], a1[c]), sb[r][i][c]) * hsc[c];
-        part[r * RUN + i] = acc;
+        for (int i = 0; i < RUN; ++i)
+          part[r * RUN + i] += scale_ue8m0(dot32_fp4(w[r][i][c], a0, a1), sb[r][i][c]) * hsc;
       }
     }
   }
@@ -220,11 +176,12 @@ __global__ __launch_bounds__(256) void gemv_down_fp4_kernel(
 template <int NB>
 static hipError_t launch_gate_up_nb(const GemvArgs& a, hipStream_t st) {
   constexpr int RUN = kGemvRun, DEPTH = 3;
-  if (a.I % (4 * RUN) != 0) return hipErrorInvalidValue;
+  if (a.I % 128 != 0 || a.I > kHSlotStride) return hipErrorInvalidValue;
   const GUWeights w = {a.gq, a.gs, a.uq, a.us, a.E, a.H, a.I};
   const dim3 grid((a.I / (4 * RUN)) * a.n_slots);
   gemv_gate_up_fp4_kernel<NB, DEPTH><<<grid, 256, 0, st>>>(
-      w, a.xq, a.xs, a.offsets, a.row_token, a.active, a.h);
+      w, a.xq, a.xs, a.offsets, a.row_token, a.active,
+      HExchange{a.hq_arrive, a.h_slots, a.h, a.hq_ws, a.hs_ws, a.status});
   return hipGetLastError();
 }
 
@@ -233,10 +190,9 @@ static hipError_t launch_down_nb(const GemvArgs& a, hipStream_t st) {
   constexpr int RMAX = kGemvMaxRows, RUN = 2;
   if (a.H % (4 * RUN) != 0) return hipErrorInvalidValue;
   const dim3 grid(a.H / (4 * RUN));
-  const size_t lds = (size_t)RMAX * a.I + (size_t)RMAX * (a.I / 128) * sizeof(float);
-  gemv_down_fp4_kernel<NB, RMAX, RUN, COMBINE><<<grid, 256, lds, st>>>(
-      a.dq, a.ds, a.h, a.offsets, a.row_of, a.topk_w, a.E, a.H, a.I, a.k, a.y_rows, a.out,
-      a.out_bf16, a.hq_ws, a.hs_ws);
+  gemv_down_fp4_kernel<NB, RMAX, RUN, COMBINE><<<grid, 256, 0, st>>>(
+      a.dq, a.ds, a.hq_ws, a.hs_ws, a.offsets, a.row_of, a.topk_w, a.E, a.H, a.I, a.k, a.y_rows,
+      a.out, a.out_bf16);
   return hipGetLastError();
 }
 

@@ -101,35 +101,41 @@ __device__ __forceinline__ void act_from_bf16(const uint16_t* __restrict__ x_row
 // i+DEPTH-1 are in flight while row i is multiplied), keeping each row's
 // per-lane partial sums; one butterfly reduce-scatter then gives every lane
 // one of the 16 totals (8 gate, 8 up), and 8 lanes finish
-// h[r][n] = silu(g_n) * u_n in parallel.
+// h[n] = silu(g_n) * u_n in parallel (returned in those lanes).
 template <int NB, int DEPTH>
-__device__ __forceinline__ void gate_up_rows(const GUWeights& w, int g, int n0, int r, int lane,
-                                             const Act16 (&a0)[NB], const Act16 (&a1)[NB],
-                                             const float (&xsc)[NB], float* __restrict__ h) {
+__device__ __forceinline__ float gate_up_rows(const GUWeights& w, int g, int n0, int lane,
+                                              const Act16 (&a0)[NB], const Act16 (&a1)[NB],
+                                              const float (&xsc)[NB]) {
   constexpr int RUN = 8;
   const int H = w.H, I = w.I;
   const int nch = H >> 5;
   const size_t rowq = (size_t)(H >> 1), rows_ = (size_t)nch;
-  const uint8_t* gqb = w.gq + ((size_t)g * I + n0) * rowq + 16 * lane;
-  const uint8_t* uqb = w.uq + ((size_t)g * I + n0) * rowq + 16 * lane;
-  const uint8_t* gsb = w.gs + ((size_t)g * I + n0) * rows_ + lane;
-  const uint8_t* usb = w.us + ((size_t)g * I + n0) * rows_ + lane;
-  bool has[NB];
+  // chunk offsets clamped into the row: the loads are unconditional, so no
+  // select on a loaded value forces an early wait; a chunk past the row end
+  // meets activation codes of 0 and scale 0 and adds exactly 0
+  // (the lane index is made opaque so that a caller's loop cannot hoist the
+  // 64-bit row addresses out and keep them all live across iterations)
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  int co[NB], cs[NB];
 #pragma unroll
-  for (int c = 0; c < NB; ++c) has[c] = lane + 64 * c < nch;
+  for (int c = 0; c < NB; ++c) {
+    const int ch = min(ln + 64 * c, nch - 1);
+    co[c] = 16 * ch;
+    cs[c] = ch;
+  }
+  const uint8_t* gqb = w.gq + ((size_t)g * I + n0) * rowq;
+  const uint8_t* uqb = w.uq + ((size_t)g * I + n0) * rowq;
+  const uint8_t* gsb = w.gs + ((size_t)g * I + n0) * rows_;
+  const uint8_t* usb = w.us + ((size_t)g * I + n0) * rows_;
   uint4 pg[DEPTH][NB], pu[DEPTH][NB];
   uint32_t psg[DEPTH][NB], psu[DEPTH][NB];
 #define BEF_GU_LOAD(SLOT, ROW)                                                      \
   _Pragma("unroll") for (int c = 0; c < NB; ++c) {                                  \
-    if (has[c]) {                                                                   \
-      pg[SLOT][c] = *reinterpret_cast<const uint4*>(gqb + (ROW) * rowq + 1024 * c); \
-      pu[SLOT][c] = *reinterpret_cast<const uint4*>(uqb + (ROW) * rowq + 1024 * c); \
-      psg[SLOT][c] = gsb[(ROW) * rows_ + 64 * c];                                   \
-      psu[SLOT][c] = usb[(ROW) * rows_ + 64 * c];                                   \
-    } else {                                                                        \
-      pg[SLOT][c] = pu[SLOT][c] = make_uint4(0, 0, 0, 0);                           \
-      psg[SLOT][c] = psu[SLOT][c] = 127;                                            \
-    }                                                                               \
+    pg[SLOT][c] = *reinterpret_cast<const uint4*>(gqb + (ROW) * rowq + co[c]);      \
+    pu[SLOT][c] = *reinterpret_cast<const uint4*>(uqb + (ROW) * rowq + co[c]);      \
+    psg[SLOT][c] = gsb[(ROW) * rows_ + cs[c]];                                      \
+    psu[SLOT][c] = usb[(ROW) * rows_ + cs[c]];                                      \
   }
 #pragma unroll
   for (int d = 0; d < DEPTH - 1; ++d) {
@@ -158,9 +164,81 @@ __device__ __forceinline__ void gate_up_rows(const GUWeights& w, int g, int n0, 
 #undef BEF_GU_LOAD
   const float tot = butterfly16(part);  // j = 8*bit5 + 4*bit4 + 2*bit3 + bit2
   const float up = xchg32(tot);         // lanes with bit5 = 0 receive the same row's up total
-  if ((lane & 35) == 0) {               // bit5 = 0, bits 1..0 = 0: one lane per row
-    const int row = (lane >> 2) & 7;    // 4*bit4 + 2*bit3 + bit2
-    h[(size_t)r * I + n0 + row] = silu_mul_accurate(tot, up);
+  return silu_mul_accurate(tot, up);    // valid in h_lane() lanes
+}
+
+// The lanes that hold a finished h value after gate_up_rows (bit 5 = 0 and
+// bits 1..0 = 0: one per row), and the row n0 + h_row(lane) they hold.
+__device__ __forceinline__ bool h_lane(int lane) { return (lane & 35) == 0; }
+__device__ __forceinline__ int h_row(int lane) { return (lane >> 2) & 7; }
+
+// The requantisation of h ahead of the down projection, done once, with no
+// device-scope fence (on this chip a release fence writes back the whole L2
+// of the XCD).  h moves between blocks only through 64-bit atomic
+// read-modify-writes, which are coherent across the XCDs:
+//  * each block that has finished rows n0b .. n0b+31 of h row r takes a
+//    ticket from the arrival counter of the 128-wide block n0b / 128; the 4
+//    tickets of one launch share tag = ticket / 4 + 1 (never 0; the slots
+//    start zeroed);
+//  * its 32 values go out as {tag, value bits} words (atomic exchange);
+//  * the block that drew the 4th ticket reads the 128 words (atomic or with
+//    0) until every tag is its own -- a bounded wait: past kSpinLimit
+//    rounds it flags MOE_STATUS_SYNC_TIMEOUT and carries on -- and writes
+//    the E4M3 codes and scale with the act_quant rule (s = amax / 448 by IEEE
+//    division, code = E4M3(v / s), zero block -> s = 0, code 0; dpshk.com
+//    article, section "核心实现二").
+// Slots have a fixed row stride of kHSlotStride so that a slot always
+// belongs to the same counter, whatever I a call uses.
+constexpr int kHSlotStride = 4096;   // largest I on the one-token path
+constexpr int kHSlotRows = 8;
+constexpr uint32_t kSpinLimit = 1u << 16;
+constexpr uint32_t kStatusSyncTimeout = 2u;  // MOE_STATUS_SYNC_TIMEOUT
+
+struct HExchange {
+  uint32_t* arrive;    // [kHSlotRows][kHSlotStride / 128] tickets
+  uint64_t* slots;     // [kHSlotRows][kHSlotStride] {tag, value bits}
+  float* h;            // [rows][I] plain copy of h (inspection)
+  uint8_t* hq;         // [rows][I] E4M3 codes
+  float* hs;           // [rows][I/128] scales
+  uint32_t* status;
+};
+
+__device__ __forceinline__ void publish_h(const HExchange& x, float hv, int r, int I, int n0,
+                                          int n0b, int tid, int lane, uint32_t* s_ticket) {
+  constexpr uint32_t kBlocks = 128 / 32;
+  const int c = n0b >> 7;
+  __syncthreads();  // readers of the previous ticket are done with it
+  if (tid == 0) *s_ticket = atomicAdd(x.arrive + r * (kHSlotStride / 128) + c, 1u);
+  __syncthreads();
+  const uint32_t ticket = *s_ticket;
+  const uint64_t tag = (uint64_t)(ticket / kBlocks + 1) << 32;
+  unsigned long long* slot = reinterpret_cast<unsigned long long*>(x.slots) + r * kHSlotStride;
+  if (h_lane(lane)) {
+    const int n = n0 + h_row(lane);
+    x.h[(size_t)r * I + n] = hv;
+    atomicExch(slot + n, tag | __float_as_uint(hv));
+  }
+  if (ticket % kBlocks == kBlocks - 1 && tid < 64) {
+    const int n = 128 * c + 2 * tid;
+    unsigned long long w0 = 0, w1 = 0;
+    uint32_t spins = 0;
+    bool ok = false;
+    for (;;) {
+      if ((w0 & 0xffffffff00000000ull) != tag) w0 = atomicOr(slot + n, 0ull);
+      if ((w1 & 0xffffffff00000000ull) != tag) w1 = atomicOr(slot + n + 1, 0ull);
+      ok = (w0 & 0xffffffff00000000ull) == tag && (w1 & 0xffffffff00000000ull) == tag;
+      if (__all(ok) || ++spins >= kSpinLimit) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (!ok) atomicOr(x.status, kStatusSyncTimeout);
+    const float v0 = __uint_as_float((uint32_t)w0), v1 = __uint_as_float((uint32_t)w1);
+    const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+    const float sc = amax / 448.0f;
+    uint32_t q = 0;
+    if (amax != 0.0f) q = e4m3_pack4(v0 / sc, v1 / sc, 0.0f, 0.0f);
+    const size_t e = (size_t)r * I + n;
+    reinterpret_cast<uint16_t*>(x.hq + e)[0] = (uint16_t)q;
+    if (tid == 0) x.hs[(size_t)r * (I >> 7) + c] = sc;
   }
 }
 

@@ -27,6 +27,9 @@ struct GemvArgs {
   int out_bf16;
   uint8_t* hq_ws;
   float* hs_ws;
+  uint32_t* hq_arrive;  // zeroed counters and tagged slots of the h exchange
+  uint64_t* h_slots;
+  uint32_t* status;
 };
 
 struct GemmArgs {
@@ -61,6 +64,11 @@ struct FrontArgs {
   const uint8_t *sh_gq, *sh_gs, *sh_uq, *sh_us;
   int I;
   float* sh_h;
+  uint8_t* sh_hq;         // requantised h (rows of the shared expert)
+  float* sh_hs;
+  uint32_t* hq_arrive;
+  uint64_t* h_slots;
+  uint32_t* status;
 };
 hipError_t launch_route_front(const FrontArgs& a, hipStream_t st);
 

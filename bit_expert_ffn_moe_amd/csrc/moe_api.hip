@@ -25,7 +25,8 @@ hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t st) {
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr size_t kCtlBytes = 256;
+constexpr size_t kCtlBytes = sizeof(WsCtl);
+static_assert(sizeof(WsCtl) % 256 == 0, "control block");
 
 size_t up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
@@ -185,6 +186,9 @@ GemvArgs gemv_args(const moe_weights* w, int T, int k, const Layout& L, void* ws
   a.h = at<float>(ws, L.h);
   a.hq_ws = at<uint8_t>(ws, L.hq);
   a.hs_ws = at<float>(ws, L.hs);
+  a.hq_arrive = at<WsCtl>(ws, L.ctl)->hq_arrive;
+  a.h_slots = at<WsCtl>(ws, L.ctl)->h_slots;
+  a.status = &at<WsCtl>(ws, L.ctl)->status;
   return a;
 }
 
@@ -438,6 +442,11 @@ int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint1
       fa.sh_us = (const uint8_t*)w->up_s;
       fa.I = w->inter;
       fa.sh_h = at<float>(ws, L.h);
+      fa.sh_hq = at<uint8_t>(ws, L.hq);
+      fa.sh_hs = at<float>(ws, L.hs);
+      fa.hq_arrive = ctl->hq_arrive;
+      fa.h_slots = ctl->h_slots;
+      fa.status = &ctl->status;
       fa.active = at<int4>(ws, L.active);
       fa.n_active_slots = (T * k < E ? T * k : E);
       fa.xq = xq, fa.xs = xs;  // act_quant blocks run in the same kernel

@@ -77,7 +77,8 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, in
 //    issued before the multiply-adds.
 //  * When sh_h is set (single-token FP4 path), the next I/(4 RUN) blocks per
 //    token run the shared expert's gate+up GEMV rows (it needs no routing):
-//    its 8.9 MB stream overlaps the router's reduction chain.
+//    its 8.9 MB stream overlaps the router's reduction chain; the last block
+//    of each 128-wide block of h requantises it.
 //  * Then, when xq is set, act_quant blocks of x (16 lanes per 128-block).
 //  * The last router block to arrive (arrival counter in the workspace,
 //    returned to zero by that block) sums the partials in chunk order, ranks
@@ -95,13 +96,17 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
   if (b >= 0 && a.sh_h) {
     const int bpg = a.I / (4 * kGemvRun);
     if (b < bpg * T) {
-      const int t = b / bpg, lane = tid & 63, wv = tid >> 6;
-      const int n0 = ((b - t * bpg) * 4 + wv) * kGemvRun;
+      __shared__ uint32_t s_ticket;
+      const int t = b / bpg, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+      const int n0b = (b - t * bpg) * 4 * kGemvRun;
       const GUWeights w = {a.sh_gq, a.sh_gs, a.sh_uq, a.sh_us, E, H, a.I};
       Act16 a0[NB], a1[NB];
       float xsc[NB];
       act_from_bf16<NB>(a.x + (size_t)t * H, H, lane, a0, a1, xsc);
-      gate_up_rows<NB, 3>(w, E, n0, T * k + t, lane, a0, a1, xsc, a.sh_h);
+      const int n0 = n0b + wv * kGemvRun;
+      const float hv = gate_up_rows<NB, 3>(w, E, n0, lane, a0, a1, xsc);
+      publish_h(HExchange{a.hq_arrive, a.h_slots, a.sh_h, a.sh_hq, a.sh_hs, a.status}, hv,
+                T * k + t, a.I, n0, n0b, tid, lane, &s_ticket);
       return;
     }
     b -= bpg * T;
@@ -359,7 +364,11 @@ hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int H, int
 hipError_t launch_route_front(const FrontArgs& a, hipStream_t st) {
   int nq = 0, nsh = 0;
   if (a.xq) nq = (int)(((int64_t)a.T * (a.H / 128) * 16 + 255) / 256);
-  if (a.sh_h) nsh = (a.I / (4 * kGemvRun)) * a.T;
+  if (a.sh_h) {
+    if (a.I % 128 != 0 || a.I > kHSlotStride || a.T * (a.k + 1) > kHSlotRows)
+      return hipErrorInvalidValue;
+    nsh = (a.I / (4 * kGemvRun)) * a.T;
+  }
   const dim3 grid(a.H / 64 + nsh + nq);
   const int nb = (a.H / 32 + 63) / 64;
   if (nb <= 1)

@@ -67,8 +67,10 @@ enum {
 /* Activation / output dtypes. */
 enum { MOE_DT_BF16 = 1, MOE_DT_F32 = 2 };
 
-/* Device status word bits (see moe_device_status). */
-enum { MOE_STATUS_BAD_EXPERT_ID = 1u };
+/* Device status word bits (see moe_device_status).  MOE_STATUS_SYNC_TIMEOUT:
+ * on the one-token path, a block waiting for the h values of other blocks
+ * gave up after its bounded wait; the results of that call are invalid. */
+enum { MOE_STATUS_BAD_EXPERT_ID = 1u, MOE_STATUS_SYNC_TIMEOUT = 2u };
 
 /* Stacked expert weights, expert-major; slot E (the last) is the shared
  * expert, which must have the same intermediate size as the routed ones.

@@ -63,7 +63,7 @@ def d2h(ptr: int, shape, dtype) -> np.ndarray:
     import ctypes
     global _hip
     if _hip is None:
-        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch loaded
         _hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                    ctypes.c_int]
         _hip.hipMemcpy.restype = ctypes.c_int

@@ -62,6 +62,7 @@ def _run(name, sample=None, threads=0, **over):
     ref = orc.forward(W, L.wr, L.x, wl.k, ids=L.ids, w=L.w, tokens=tok, threads=threads)
     got = out if tok is None else out[tok]
     _check(got, ref, f"{name} {over}")
+    assert moe.moe_device_status(D.ws) == 0
     return L, D, out, ref, tok
 
 
@@ -98,11 +99,35 @@ def test_decode_t1_full_shapes_many_tokens():
     out = np.stack(outs)
     ref = orc.forward(Weights.from_layer(L), L.wr, L.x, L.wl.k)
     _check(out, ref, "decode_t1 x24")
+    assert moe.moe_device_status(D.ws) == 0
     ids = torch.empty((L.wl.T, 6), dtype=torch.int32, device="cuda")
     w = torch.empty((L.wl.T, 6), dtype=torch.float32, device="cuda")
     moe.moe_route(D.x, D.wr, L.wl.T, 4096, 256, 6, ids, w, D.ws, D.ws_bytes)
     ir, _ = orc.route(L.x, L.wr, 6)
     assert np.array_equal(to_host(ids), ir)
+
+
+def test_decode_t1_repeated_expert_ids():
+    """One token whose injected ids repeat experts: a group then holds
+    several rows, and the gate+up blocks publish h for each of them in turn;
+    a second shape (I = 1024) on the same workspace follows."""
+    L = synth.make_layer("decode_t1", T=1, routing="zipf", zipf_s=1.0)
+    L.ids[0] = np.array([7, 7, 7, 100, 100, 9], np.int32)
+    D = DevLayer(L)
+    ref = orc.forward(Weights.from_layer(L), L.wr, L.x, 6, ids=L.ids, w=L.w)
+    for _ in range(3):
+        _check(to_host(D.forward()), ref, "decode repeated ids")
+    # another intermediate size through the same workspace, then back
+    L2 = synth.make_layer("decode_t1", T=1, I=1024, seed=2001)
+    D2 = DevLayer(L2)
+    assert D2.ws_bytes <= D.ws_bytes
+    out2 = torch.empty((1, 4096), dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        moe.dsv4_moe_forward(D2.w, D2.wr, D2.x, 1, 6, None, None, out2, moe.MOE_DT_F32, D.ws,
+                             D.ws_bytes)
+        _check(to_host(out2), orc.forward(Weights.from_layer(L2), L2.wr, L2.x, 6), "decode I=1024")
+    _check(to_host(D.forward()), ref, "decode repeated ids, after I=1024")
+    assert moe.moe_device_status(D.ws) == 0
 
 
 def test_verify_t32_full_shapes():
