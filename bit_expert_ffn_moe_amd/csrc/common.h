@@ -203,14 +203,17 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 // Workspace control block: word 0 = status bits, then counters.
 struct WsCtl {
   uint32_t status;
-  uint32_t route_done;  // arrival counter of the small-T router
-  uint32_t pad[62];
+  uint32_t route_done;   // arrival counter of the small-T router
+  uint32_t route_epoch;  // launches of the small-T router so far (tags its partials)
+  uint32_t pad[61];
   // one-token GEMV path: arrival counters of the blocks that produce each
   // 128-wide block of h, [row 8][4096/128], then the tagged h slots
   // [row 8][4096] (see publish_h)
   uint32_t hq_arrive[8 * 32];
   uint32_t pad2[256];
   uint64_t h_slots[8 * 4096];
+  // small-T router: tagged chunk partials [H/64 <= 128][T <= 4][E <= 256]
+  uint64_t route_slots[128 * 4 * 256];
 };
 
 __device__ __forceinline__ void set_status(uint32_t* st, uint32_t bit) { atomicOr(st, bit); }

@@ -6,6 +6,7 @@
 namespace bef {
 
 constexpr int kRouteSmallT = 4;           // router: per-chunk blocks + last-block top-k
+constexpr int kRouteMaxChunks = 128;      // router: H / 64 for H <= 8192
 constexpr int kPermuteSmallPairs = 2048;  // permute: single block up to this many pairs
 constexpr int kPermuteTokBlock = 256;     // permute: tokens per block above that
 constexpr int kGemvMaxRows = 8;           // VALU GEMV path: rows (k + 1) per token
@@ -47,12 +48,14 @@ struct GemmArgs {
 
 // Small-T front of the layer: router (+ act_quant of x when xq is set,
 // + permutation tables when offsets is set).
+struct WsCtl;
 struct FrontArgs {
   const uint16_t* x;
   const uint16_t* wr;
   int T, H, E, k;
-  float* part;
-  uint32_t* counter;
+  uint32_t* counter;      // router arrival counter (zero between launches)
+  uint32_t* epoch;        // launch epoch of the tagged partials
+  uint64_t* slots;        // [H/64][T][E] tagged chunk partials
   int32_t* ids;
   float* w;
   uint8_t* xq;
@@ -70,12 +73,13 @@ struct FrontArgs {
   uint64_t* h_slots;
   uint32_t* status;
 };
+void set_route_sync(FrontArgs& a, WsCtl* ctl);
 hipError_t launch_route_front(const FrontArgs& a, hipStream_t st);
 
 hipError_t launch_act_quant(const void* x, bool bf16, int64_t rows, int32_t cols, uint8_t* q,
                             float* s, hipStream_t st);
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int H, int E, int k,
-                        int32_t* ids, float* w, float* part, uint32_t* counter, hipStream_t st);
+                        int32_t* ids, float* w, WsCtl* ctl, hipStream_t st);
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
                           int32_t* row_token, int32_t* row_of, int32_t* cnt, int32_t* base,
                           uint32_t* status, hipStream_t st);

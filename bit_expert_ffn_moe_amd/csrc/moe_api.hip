@@ -37,7 +37,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // layer call: control | permute scratch (T, E) | router partials (T, H, E) |
 // everything else (needs the weights' shapes).
 struct Layout {
-  size_t ctl, cnt, base, part, ids, w, xq, xs, offsets, row_token, row_of, active, h, hq, hs, y,
+  size_t ctl, cnt, base, ids, w, xq, xs, offsets, row_token, row_of, active, h, hq, hs, y,
       total;
   size_t end_permute, end_route, end_ffn;
 };
@@ -59,8 +59,6 @@ Layout layout_for(int E, int H, int I, int T, int k, bool with_h) {
   L.base = o;
   o += up(nblk * E * 4);
   L.end_permute = o;
-  L.part = o;
-  if (T <= kRouteSmallT) o += up((size_t)(H / 64) * T * E * 4);
   L.end_route = o;
   L.ids = o;
   o += up((size_t)T * k * 4);
@@ -279,9 +277,8 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H,
   rc = check_device();
   if (rc) return rc;
   WsCtl* ctl = at<WsCtl>(ws, L.ctl);
-  return launch_status(launch_route(x, w_router, T, H, E, k, topk_ids, topk_w,
-                                    at<float>(ws, L.part), &ctl->route_done,
-                                    (hipStream_t)stream));
+  return launch_status(
+      launch_route(x, w_router, T, H, E, k, topk_ids, topk_w, ctl, (hipStream_t)stream));
 }
 
 int act_quant_fp8(const void* x, int32_t x_dtype, int64_t rows, int32_t cols, uint8_t* q,
@@ -429,7 +426,7 @@ int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint1
   if (!ids && T <= kRouteSmallT) {
     FrontArgs fa = {};
     fa.x = x, fa.wr = w_router, fa.T = T, fa.H = H, fa.E = E, fa.k = k;
-    fa.part = at<float>(ws, L.part), fa.counter = &ctl->route_done;
+    set_route_sync(fa, ctl);
     fa.ids = at<int32_t>(ws, L.ids), fa.w = at<float>(ws, L.w);
     fa.offsets = offsets, fa.row_token = row_token, fa.row_of = row_of;
     if (gemv_path(w->format, T, k, H, w->inter)) {
@@ -446,7 +443,6 @@ int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint1
       fa.sh_hs = at<float>(ws, L.hs);
       fa.hq_arrive = ctl->hq_arrive;
       fa.h_slots = ctl->h_slots;
-      fa.status = &ctl->status;
       fa.active = at<int4>(ws, L.active);
       fa.n_active_slots = (T * k < E ? T * k : E);
       fa.xq = xq, fa.xs = xs;  // act_quant blocks run in the same kernel
@@ -473,8 +469,7 @@ int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint1
   if (!ids) {
     int32_t* ids_ws = at<int32_t>(ws, L.ids);
     float* w_ws = at<float>(ws, L.w);
-    rc = launch_status(launch_route(x, w_router, T, H, E, k, ids_ws, w_ws, at<float>(ws, L.part),
-                                    &ctl->route_done, st));
+    rc = launch_status(launch_route(x, w_router, T, H, E, k, ids_ws, w_ws, ctl, st));
     if (rc) return rc;
     ids = ids_ws;
     tw = w_ws;

@@ -24,7 +24,7 @@ namespace bef {
 // ids / weights.  Lane e owns experts e, e+64, e+128, e+192.
 __device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, int k,
                                           int32_t* __restrict__ ids_out,
-                                          float* __restrict__ w_out) {
+                                          float* __restrict__ w_out, int* ids_lds = nullptr) {
   const int lane = threadIdx.x & 63;
   float v[4];
 #pragma unroll
@@ -67,6 +67,7 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, in
   if (lane < k) {
     ids_out[lane] = my_id;
     w_out[lane] = sg / sum;
+    if (ids_lds) ids_lds[lane] = my_id;
   }
 }
 
@@ -147,11 +148,14 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
   const int c = blockIdx.x;
   const int e = tid;
   __shared__ float sx[kRouteSmallT][64];
-  __shared__ __align__(16) float sz[kRouteSmallT][256];
-  __shared__ int s_ids[kRouteSmallT][16];
-  __shared__ float s_zs[kRouteSmallT][16];
-  __shared__ int stmp[8];
-  __shared__ int s_last;
+  __shared__ float sz[kRouteSmallT][256];
+  __shared__ int s_ids[kRouteSmallT * 16];
+  __shared__ int s_sorted[kRouteSmallT * 16];
+  __shared__ uint32_t s_ticket;
+  // this launch's tag; the epoch word changes only at the very end of a
+  // launch, after every block has read it (each reads it before its ticket)
+  const uint32_t epoch = __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t tag = (uint64_t)(epoch + 1u) << 32;
   for (int i = tid; i < T * 64; i += 256)
     sx[i / 64][i % 64] = bf16_to_f32(a.x[(size_t)(i / 64) * H + 64 * c + (i % 64)]);
   uint32_t wv[64];
@@ -161,103 +165,118 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
     for (int h = 0; h < 64; ++h) wv[h] = col[(size_t)h * E];
   }
   __syncthreads();
+  unsigned long long* slots = reinterpret_cast<unsigned long long*>(a.slots);
   if (e < E) {
     for (int t = 0; t < T; ++t) {
       float p = 0.0f;
 #pragma unroll
       for (int h = 0; h < 64; ++h) p = fmaf(sx[t][h], bf16_to_f32(wv[h]), p);
-      a.part[((size_t)c * T + t) * E + e] = p;
+      atomicExch(slots + ((size_t)c * T + t) * E + e, tag | __float_as_uint(p));
     }
   }
-  __threadfence();
   __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(a.counter, 1u) == (uint32_t)(nc - 1));
+  if (tid == 0) s_ticket = atomicAdd(a.counter, 1u);
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+  if (s_ticket != (uint32_t)(nc - 1)) return;
+
+  // the last block: logits in the fixed order (chunk partials summed in
+  // ascending chunk order), waiting -- bounded -- until every partial of this
+  // launch is visible
+  bool ok = true;
   for (int t = 0; t < T; ++t) {
     float acc = -INFINITY;  // experts beyond E never rank
     if (e < E) {
       acc = 0.0f;
-      for (int c0 = 0; c0 < nc; c0 += 64) {
-        float v[64];
+      for (int c0 = 0; c0 < nc; c0 += 32) {
+        unsigned long long v[32];
 #pragma unroll
-        for (int i = 0; i < 64; ++i)
-          v[i] = (c0 + i < nc) ? a.part[((size_t)(c0 + i) * T + t) * E + e] : 0.0f;
+        for (int i = 0; i < 32; ++i)
+          v[i] = (c0 + i < nc) ? __hip_atomic_load(slots + ((size_t)(c0 + i) * T + t) * E + e,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                               : tag;
+        for (uint32_t spins = 0;;) {
+          bool all = true;
 #pragma unroll
-        for (int i = 0; i < 64; ++i)
-          if (c0 + i < nc) acc = (c0 + i == 0) ? v[i] : acc + v[i];
+          for (int i = 0; i < 32; ++i)
+            if ((v[i] & 0xffffffff00000000ull) != tag) {
+              all = false;
+              v[i] = __hip_atomic_load(slots + ((size_t)(c0 + i) * T + t) * E + e,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+          if (all) break;
+          if (++spins >= kSpinLimit) {
+            ok = false;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          if (c0 + i < nc) acc = (c0 + i == 0) ? __uint_as_float((uint32_t)v[i])
+                                               : acc + __uint_as_float((uint32_t)v[i]);
       }
     }
     sz[t][e] = acc;
   }
+  if (!ok) atomicOr(a.status, kStatusSyncTimeout);
   __syncthreads();
-  // ranks: order (logit desc, id asc); the comparisons read 4 logits at a time
-  if (e < E) {
-    const int E4 = (E + 3) >> 2;
-    for (int t = 0; t < T; ++t) {
-      const float z = sz[t][e];
-      const float4* z4 = reinterpret_cast<const float4*>(sz[t]);
-      int rank = 0;
-#pragma unroll 8
-      for (int f4 = 0; f4 < E4; ++f4) {
-        const float4 q = z4[f4];
-        const int f = 4 * f4;
-        rank += (q.x > z) || (q.x == z && f < e);
-        rank += (q.y > z) || (q.y == z && f + 1 < e);
-        rank += (q.z > z) || (q.z == z && f + 2 < e);
-        rank += (q.w > z) || (q.w == z && f + 3 < e);
-      }
-      if (rank < k) {
-        s_ids[t][rank] = e;
-        s_zs[t][rank] = z;
-      }
-    }
-  }
+  // top-k: wave t ranks token t (order: logit desc, id asc)
+  const int w = tid >> 6, lane = tid & 63;
+  if (w < T) topk_wave(sz[w], E, k, a.ids + w * k, a.w + w * k, s_ids + w * k);
   __syncthreads();
-  if (tid < T * k) {
-    const int t = tid / k, j = tid % k;
-    float sum = 0.0f;
-    for (int i = 0; i < k; ++i) sum += 1.0f / (1.0f + expf(-s_zs[t][i]));
-    const float sg = 1.0f / (1.0f + expf(-s_zs[t][j]));
-    a.ids[tid] = s_ids[t][j];
-    a.w[tid] = sg / sum;
-  }
   if (a.offsets) {
-    // permutation tables (all ids valid here: they come from the ranking)
-    int cnt = 0;
-    if (e < E)
-      for (int p = 0; p < T * k; ++p) cnt += (s_ids[p / k][p % k] == e);
-    int total;
-    const int pre = block256_exclusive_scan(e < E ? cnt : 0, stmp, &total);
-    if (e < E) a.offsets[e] = pre;
-    if (tid == 0) {
-      a.offsets[E] = total;
-      a.offsets[E + 1] = total + T;
-    }
-    if (e < E && cnt > 0) {
-      int r = pre;
-      for (int p = 0; p < T * k; ++p) {
-        if (s_ids[p / k][p % k] == e) {
-          a.row_token[r] = p / k;
-          a.row_of[(size_t)(p / k) * (k + 1) + (p % k)] = r;
-          ++r;
-        }
+    // permutation tables: the P = T*k <= 64 pairs sorted by (expert, pair
+    // index) in wave 0 -- the stable counting-sort order of the general path
+    const int P = T * k;
+    if (w == 0) {
+      const int id = (lane < P) ? s_ids[lane] : 0x7fffffff;
+      int rank = 0;
+      for (int q = 0; q < P; ++q) {
+        const int iq = s_ids[q];
+        rank += (iq < id) | ((iq == id) & (q < lane));
+      }
+      if (lane < P) {
+        s_sorted[rank] = id;
+        a.row_token[rank] = lane / k;
+        a.row_of[(size_t)(lane / k) * (k + 1) + (lane % k)] = rank;
+      }
+      if (lane < T) {
+        a.row_token[P + lane] = lane;
+        a.row_of[(size_t)lane * (k + 1) + k] = P + lane;
       }
     }
-    if (tid < T) {
-      a.row_token[total + tid] = tid;
-      a.row_of[(size_t)tid * (k + 1) + k] = total + tid;
+    __syncthreads();
+    // offsets[g] = number of pairs with expert < g (lower bound in the
+    // sorted ids); the shared group E holds one row per token
+    for (int g = tid; g <= E + 1; g += 256) {
+      int v = P + T;
+      if (g <= E) {
+        int lo = 0, hi = P;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (s_sorted[mid] < g) lo = mid + 1; else hi = mid;
+        }
+        v = lo;
+      }
+      a.offsets[g] = v;
     }
-    if (a.active) {
-      int n_act;
-      const int slot = block256_exclusive_scan((e < E && cnt > 0) ? 1 : 0, stmp, &n_act);
-      if (e < E && cnt > 0) a.active[slot] = make_int4(e, pre, pre + cnt, 0);
-      for (int i = n_act + tid; i < a.n_active_slots; i += 256)
+    if (a.active && w == 0) {
+      // one entry per distinct routed expert, in expert order
+      const bool start = lane < P && (lane == 0 || s_sorted[lane] != s_sorted[lane - 1]);
+      const uint64_t m = __ballot(start);
+      if (start) {
+        const uint64_t after = m & ~((2ull << lane) - 1ull);
+        const int end = after ? __ffsll((long long)after) - 1 : P;
+        a.active[__popcll(m & ((1ull << lane) - 1ull))] = make_int4(s_sorted[lane], lane, end, 0);
+      }
+      for (int i = __popcll(m) + lane; i < a.n_active_slots; i += 64)
         a.active[i] = make_int4(-1, 0, 0, 0);
     }
   }
-  if (tid == 0) *a.counter = 0u;
+  if (tid == 0) {
+    *a.counter = 0u;
+    atomicAdd(a.epoch, 1u);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -350,18 +369,29 @@ __global__ __launch_bounds__(256) void route_tile_kernel(const uint16_t* __restr
 }
 
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int H, int E, int k,
-                        int32_t* ids, float* w, float* part, uint32_t* counter, hipStream_t st) {
+                        int32_t* ids, float* w, WsCtl* ctl, hipStream_t st) {
   if (T <= kRouteSmallT) {
     FrontArgs a = {};
     a.x = x, a.wr = wr, a.T = T, a.H = H, a.E = E, a.k = k;
-    a.part = part, a.counter = counter, a.ids = ids, a.w = w;
+    a.ids = ids, a.w = w;
+    set_route_sync(a, ctl);
     return launch_route_front(a, st);
   }
   route_tile_kernel<<<dim3((T + 31) / 32), dim3(256), 0, st>>>(x, wr, T, H, E, k, ids, w);
   return hipGetLastError();
 }
 
+void set_route_sync(FrontArgs& a, WsCtl* ctl) {
+  a.counter = &ctl->route_done;
+  a.epoch = &ctl->route_epoch;
+  a.slots = ctl->route_slots;
+  a.status = &ctl->status;
+}
+
 hipError_t launch_route_front(const FrontArgs& a, hipStream_t st) {
+  if (a.T < 1 || a.T > kRouteSmallT || a.k > 16 || a.E > 256 || a.H % 64 != 0 ||
+      a.H / 64 > kRouteMaxChunks || !a.counter || !a.epoch || !a.slots || !a.status)
+    return hipErrorInvalidValue;
   int nq = 0, nsh = 0;
   if (a.xq) nq = (int)(((int64_t)a.T * (a.H / 128) * 16 + 255) / 256);
   if (a.sh_h) {

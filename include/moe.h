@@ -100,9 +100,13 @@ typedef struct moe_weights {
  * (dpshk.com article, section "核心实现四": workspaces preallocated). */
 size_t moe_workspace_bytes(const moe_weights* w, int32_t max_tokens, int32_t top_k);
 
-/* Enqueue a zero-fill of the workspace's control block (status word and
- * the counters some kernels keep; they return them to zero themselves).
- * Call once after allocating a workspace. */
+/* Enqueue a zero-fill of the workspace's control block (about 1.3 MB: the
+ * status word, the counters some kernels keep, and the tagged slots through
+ * which blocks of one launch hand each other router partials and h values
+ * without device-scope fences; a slot's tag names the launch that wrote it,
+ * so the slots must start zeroed).  Call once after allocating a workspace,
+ * before its first use; the kernels keep the control block consistent from
+ * then on. */
 int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* S1+S2, the router (dpshk.com article, section "核心实现一"; top-6 of 256:

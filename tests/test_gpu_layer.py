@@ -67,6 +67,7 @@ def _run(name, sample=None, threads=0, **over):
 
 
 @pytest.mark.parametrize("over", [dict(), dict(fmt="fp8"), dict(T=1), dict(T=1, fmt="fp8"),
+                                  dict(T=2), dict(T=3, E=3, k=3), dict(T=4, fmt="fp8"),
                                   dict(T=5), dict(T=130, routing="zipf", zipf_s=1.0),
                                   dict(E=1, k=1, T=9), dict(E=3, k=3, T=17)])
 def test_tiny_layer(over):
