@@ -126,6 +126,31 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// The same DPP pattern for max / min: lanes whose source is out of range or
+// whose row is masked keep their own value (DPP "old" operand = the value).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_keep(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, __int_as_float(dpp_keep<0xB1>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_keep<0x4E>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_keep<0x141>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_keep<0x140>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_keep<0x142, 0xA>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_keep<0x143, 0xC>(__float_as_int(v))));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ int wave_min_dpp(int v) {
+  v = min(v, dpp_keep<0xB1>(v));
+  v = min(v, dpp_keep<0x4E>(v));
+  v = min(v, dpp_keep<0x141>(v));
+  v = min(v, dpp_keep<0x140>(v));
+  v = min(v, dpp_keep<0x142, 0xA>(v));
+  v = min(v, dpp_keep<0x143, 0xC>(v));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
 // Butterfly reduce-scatter over the 64 lanes.  Each lane starts with N
 // partial sums v[0..N-1]; at each step it keeps the half of its values picked
 // by one bit of its lane id and adds the partner lane's copy of that half, the
@@ -157,6 +182,23 @@ __device__ __forceinline__ float butterfly16(const float (&v)[16]) {
   d += xchg_b1(d);
   d += xchg_b0(d);
   return d;
+}
+
+// 8 values: every lane ends with the total of value
+// j = 4*bit5 + 2*bit4 + bit3 of its lane id.
+__device__ __forceinline__ float butterfly8(const float (&v)[8]) {
+  const int lane = threadIdx.x & 63;
+  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+  float a[4], b[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a[j] = (b5 ? v[4 + j] : v[j]) + xchg32(b5 ? v[j] : v[4 + j]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) b[j] = (b4 ? a[2 + j] : a[j]) + xchg16(b4 ? a[j] : a[2 + j]);
+  float c = (b3 ? b[1] : b[0]) + xchg_b3(b3 ? b[0] : b[1]);
+  c += xchg_b2(c);
+  c += xchg_b1(c);
+  c += xchg_b0(c);
+  return c;
 }
 
 // 32 values: every lane ends with the total of value
@@ -206,14 +248,13 @@ struct WsCtl {
   uint32_t route_done;   // arrival counter of the small-T router
   uint32_t route_epoch;  // launches of the small-T router so far (tags its partials)
   uint32_t pad[61];
-  // one-token GEMV path: arrival counters of the blocks that produce each
-  // 128-wide block of h, [row 8][4096/128], then the tagged h slots
-  // [row 8][4096] (see publish_h)
+  // one-token GEMV path: epoch words of each 128-wide block of h,
+  // [row 8][4096/128], then the tagged h slots [row 8][4096] (publish_h)
   uint32_t hq_arrive[8 * 32];
   uint32_t pad2[256];
   uint64_t h_slots[8 * 4096];
-  // small-T router: tagged chunk partials [H/64 <= 128][T <= 4][E <= 256]
-  uint64_t route_slots[128 * 4 * 256];
+  // small-T router: tagged group sums [H/256 <= 32][T <= 4][E <= 256]
+  uint64_t route_slots[32 * 4 * 256];
 };
 
 __device__ __forceinline__ void set_status(uint32_t* st, uint32_t bit) { atomicOr(st, bit); }

@@ -28,17 +28,16 @@ namespace bef {
 // for every activation row of the group, activations from xq/xs; the last
 // block of each 128-wide block of h requantises it (publish_h).
 // ---------------------------------------------------------------------------
-template <int NB, int DEPTH>
+template <int NB>
 __global__ __launch_bounds__(256) void gemv_gate_up_fp4_kernel(
     GUWeights w, const uint8_t* __restrict__ xq, const float* __restrict__ xs,
     const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ row_token, const int4* __restrict__ active,
     HExchange hx) {
   __shared__ int stmp[8];
-  __shared__ uint32_t s_ticket;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
-  constexpr int RUN = kGemvRun;
+  constexpr int RUN = kGuRun;
   const int bpg = w.I / (4 * RUN);
   const int slot = blockIdx.x / bpg;
   int g, r0 = 0, r1 = 0;
@@ -55,131 +54,130 @@ __global__ __launch_bounds__(256) void gemv_gate_up_fp4_kernel(
   const int n0b = (blockIdx.x - slot * bpg) * 4 * RUN;
   const int n0 = n0b + wv * RUN;
   for (int r = r0; r < r1; ++r) {
+    const uint32_t epoch = h_epoch(hx, r, n0b);
     const int t = row_token[r];
-    Act16 a0[NB], a1[NB];
+    uint4 aq[NB][2];
     float xsc[NB];
-    act_from_codes<NB>(xq + (size_t)t * w.H, xs + (size_t)t * (w.H >> 7), w.H, lane, a0, a1, xsc);
-    const float hv = gate_up_rows<NB, DEPTH>(w, g, n0, lane, a0, a1, xsc);
-    publish_h(hx, hv, r, w.I, n0, n0b, tid, lane, &s_ticket);
+    load_act_codes<NB>(xq + (size_t)t * w.H, xs + (size_t)t * (w.H >> 7), w.H, lane, aq, xsc);
+    const float hv = gate_up_rows<NB>(w, g, n0, lane, aq, xsc);
+    publish_h(hx, hv, r, w.I, n0, n0b, tid, lane, epoch);
   }
 }
 
 // ---------------------------------------------------------------------------
-// down (+ combine for a single token).  Wave w of block b owns output rows
-// m = (4b + w)*RUN .. +RUN-1.  Once the row -> expert map is known, every
-// load of the wave is issued at once: the E4M3 codes and scales of h (R rows,
-// requantised by the gate+up kernel), then every W_down chunk (R rows x RUN
-// outputs, one 16-byte chunk per lane for I = 2048) with its UE8M0 scale.
-// COMBINE writes out[m] = y[shared] + sum_j w_j y[row_of[j]] (T = 1);
-// otherwise y_rows.
+// down (+ combine for a single token).  Block b owns output rows m0 = 8b ..
+// 8b+7, one wave per routed row r < R <= 8: wave r multiplies row r of the
+// requantised h (E4M3 codes + scales from the gate+up kernel; only its own
+// row, 2 KB for I = 2048) by rows m0..m0+7 of its group's W_down, streamed
+// through a 3-deep register pipeline held in order by a dependency-carrying
+// empty asm statement (as in gate_up_rows).  A butterfly gives the 8 totals;
+// COMBINE then adds them per output row in LDS -- the shared row first, then
+// the routed slots in rank order, out[m] = y[shared] + sum_j w_j y[row_of[j]]
+// (T = 1); otherwise the totals go to y_rows.
 // ---------------------------------------------------------------------------
-template <int NB, int RMAX, int RUN, bool COMBINE>
-__global__ __launch_bounds__(256) void gemv_down_fp4_kernel(
+template <int NB, bool COMBINE>
+__global__ __launch_bounds__(512) void gemv_down_fp4_kernel(
     const uint8_t* __restrict__ dq, const uint8_t* __restrict__ ds,
     const uint8_t* __restrict__ hq, const float* __restrict__ hs,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_of,
     const float* __restrict__ topk_w, int E, int H, int I, int k, float* __restrict__ y_rows,
     void* __restrict__ out, int out_bf16) {
+  constexpr int RMAX = kGemvMaxRows, RUN = 8, DEPTH = 3;
   __shared__ int s_rowexp[RMAX];
+  __shared__ float s_y[RMAX][RUN];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int r = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int R = min(offsets[E + 1], RMAX);
-  const int tid = threadIdx.x;
-  for (int g = tid; g <= E; g += 256) {
+  for (int g = tid; g <= E; g += 512) {
     const int a = offsets[g], b = offsets[g + 1];
-    for (int r = a; r < b && r < RMAX; ++r) s_rowexp[r] = g;
+    for (int rr = a; rr < b && rr < RMAX; ++rr) s_rowexp[rr] = g;
   }
   __syncthreads();
-
-  const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int m0 = (blockIdx.x * 4 + wv) * RUN;
-  const int nch = I >> 5;
-  const size_t rowq = (size_t)(I >> 1), rows_ = (size_t)nch;
-  // chunk indices clamped into the row (unconditional loads); a chunk past
-  // the end gets scale 0 and adds exactly 0
-  int ch[NB];
+  const int m0 = blockIdx.x * RUN;
+  if (r < R) {
+    const int nch = I >> 5;
+    const size_t rowq = (size_t)(I >> 1), rows_ = (size_t)nch;
+    // chunk indices clamped into the row (unconditional loads); a chunk past
+    // the end gets scale 0 and adds exactly 0
+    int ch[NB];
+    uint4 aq[NB][2];
+    float hs_raw[NB];
 #pragma unroll
-  for (int c = 0; c < NB; ++c) ch[c] = min(lane + 64 * c, nch - 1);
-  uint4 aq[RMAX][NB][2];
-  float asc[RMAX][NB];
-#pragma unroll
-  for (int r = 0; r < RMAX; ++r)
-    if (r < R)
-#pragma unroll
-      for (int c = 0; c < NB; ++c) {
-        const uint8_t* p = hq + (size_t)r * I + 32 * ch[c];
-        aq[r][c][0] = *reinterpret_cast<const uint4*>(p);
-        aq[r][c][1] = *reinterpret_cast<const uint4*>(p + 16);
-        asc[r][c] = hs[r * (I >> 7) + (ch[c] >> 2)];
-      }
-  uint4 w[RMAX][RUN][NB];
-  uint32_t sb[RMAX][RUN][NB];
-#pragma unroll
-  for (int r = 0; r < RMAX; ++r) {
-    if (r < R) {
-      const size_t row0 = (size_t)s_rowexp[r] * H + m0;
-#pragma unroll
-      for (int i = 0; i < RUN; ++i)
-#pragma unroll
-        for (int c = 0; c < NB; ++c) {
-          w[r][i][c] = *reinterpret_cast<const uint4*>(dq + (row0 + i) * rowq + 16 * ch[c]);
-          sb[r][i][c] = ds[(row0 + i) * rows_ + ch[c]];
-        }
+    for (int c = 0; c < NB; ++c) {
+      ch[c] = min(lane + 64 * c, nch - 1);
+      const uint8_t* p = hq + (size_t)r * I + 32 * ch[c];
+      aq[c][0] = *reinterpret_cast<const uint4*>(p);
+      aq[c][1] = *reinterpret_cast<const uint4*>(p + 16);
+      hs_raw[c] = hs[(size_t)r * (I >> 7) + (ch[c] >> 2)];
     }
+    const size_t row0 = (size_t)s_rowexp[r] * H + m0;
+    const uint8_t* wb = dq + row0 * rowq;
+    const uint8_t* sbb = ds + row0 * rows_;
+    uint4 w[DEPTH][NB];
+    uint32_t sb[DEPTH][NB];
+    int dep = 0;
+#define BEF_DN_LOAD(SLOT, ROW)                                                         \
+  _Pragma("unroll") for (int c = 0; c < NB; ++c) {                                     \
+    w[SLOT][c] = *reinterpret_cast<const uint4*>(wb + (ROW) * rowq + 16 * ch[c] + dep); \
+    sb[SLOT][c] = sbb[(ROW) * rows_ + ch[c] + dep];                                    \
   }
-
-  // per-lane partials of y[r][i] (r < RMAX rows, i < RUN outputs), one
-  // butterfly, then every lane holds the total of j = r*RUN + i
-  static_assert(RMAX * RUN == 16, "butterfly16 layout");
-  float part[RMAX * RUN];
 #pragma unroll
-  for (int r = 0; r < RMAX; ++r) {
-#pragma unroll
-    for (int i = 0; i < RUN; ++i) part[r * RUN + i] = 0.0f;
-    if (r < R) {
-#pragma unroll
-      for (int c = 0; c < NB; ++c) {
-        Act16 a0, a1;
-        e4m3x16_to_h2(aq[r][c][0], a0);
-        e4m3x16_to_h2(aq[r][c][1], a1);
-        const float hsc = (lane + 64 * c < nch) ? asc[r][c] : 0.0f;
-#pragma unroll
-        for (int i = 0; i < RUN; ++i)
-          part[r * RUN + i] += scale_ue8m0(dot32_fp4(w[r][i][c], a0, a1), sb[r][i][c]) * hsc;
-      }
+    for (int d = 0; d < DEPTH - 1; ++d) {
+      BEF_DN_LOAD(d, d)
     }
+    // the activations, once the first rows are in flight
+    Act16 a0[NB], a1[NB];
+    float hsc[NB];
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      e4m3x16_to_h2(aq[c][0], a0[c]);
+      e4m3x16_to_h2(aq[c][1], a1[c]);
+      hsc[c] = (lane + 64 * c < nch) ? hs_raw[c] : 0.0f;
+    }
+    float part[RUN];
+#pragma unroll
+    for (int i = 0; i < RUN; ++i) {
+      if (i + DEPTH - 1 < RUN) {
+        BEF_DN_LOAD((i + DEPTH - 1) % DEPTH, i + DEPTH - 1)
+      }
+      float acc = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NB; ++c)
+        acc += scale_ue8m0(dot32_fp4(w[i % DEPTH][c], a0[c], a1[c]), sb[i % DEPTH][c]) * hsc[c];
+      part[i] = acc;
+      asm volatile("" : "+v"(dep) : "v"(acc));
+    }
+#undef BEF_DN_LOAD
+    const float tot = butterfly8(part);  // j = 4*bit5 + 2*bit4 + bit3
+    if ((lane & 7) == 0) s_y[r][lane >> 3] = tot;
   }
-  const float tot = butterfly16(part);       // j = 8*bit5 + 4*bit4 + 2*bit3 + bit2
-  const int jr = (lane >> 3) & 7, ji = (lane >> 2) & 1;  // j = 2*jr + ji
+  __syncthreads();
   if (COMBINE) {
-    __shared__ float s_y[4][RMAX][RUN];
-    if ((lane & 3) == 0) s_y[wv][jr][ji] = tot;
-    __syncthreads();
-    if (lane < RUN) {
-      // lane i finishes output row m0 + i (T = 1: token 0), shared first, then
-      // the routed slots in rank order
+    if (tid < RUN) {
       const int rs = row_of[k];
-      float o = (rs >= 0) ? s_y[wv][rs][lane] : 0.0f;
+      float o = (rs >= 0 && rs < RMAX) ? s_y[rs][tid] : 0.0f;
       for (int j = 0; j < k; ++j) {
         const int rj = row_of[j];
-        if (rj >= 0) o = fmaf(topk_w[j], s_y[wv][rj][lane], o);
+        if (rj >= 0 && rj < RMAX) o = fmaf(topk_w[j], s_y[rj][tid], o);
       }
-      const int m = m0 + lane;
+      const int m = m0 + tid;
       if (out_bf16)
         reinterpret_cast<uint16_t*>(out)[m] = f32_to_bf16(o);
       else
         reinterpret_cast<float*>(out)[m] = o;
     }
-  } else {
-    if ((lane & 3) == 0 && jr < R) y_rows[(size_t)jr * H + m0 + ji] = tot;
+  } else if (tid < R * RUN) {
+    y_rows[(size_t)(tid / RUN) * H + m0 + (tid % RUN)] = s_y[tid / RUN][tid % RUN];
   }
 }
 
 template <int NB>
 static hipError_t launch_gate_up_nb(const GemvArgs& a, hipStream_t st) {
-  constexpr int RUN = kGemvRun, DEPTH = 3;
+  constexpr int RUN = kGuRun;
   if (a.I % 128 != 0 || a.I > kHSlotStride) return hipErrorInvalidValue;
   const GUWeights w = {a.gq, a.gs, a.uq, a.us, a.E, a.H, a.I};
   const dim3 grid((a.I / (4 * RUN)) * a.n_slots);
-  gemv_gate_up_fp4_kernel<NB, DEPTH><<<grid, 256, 0, st>>>(
+  gemv_gate_up_fp4_kernel<NB><<<grid, 256, 0, st>>>(
       w, a.xq, a.xs, a.offsets, a.row_token, a.active,
       HExchange{a.hq_arrive, a.h_slots, a.h, a.hq_ws, a.hs_ws, a.status});
   return hipGetLastError();
@@ -187,10 +185,8 @@ static hipError_t launch_gate_up_nb(const GemvArgs& a, hipStream_t st) {
 
 template <int NB, bool COMBINE>
 static hipError_t launch_down_nb(const GemvArgs& a, hipStream_t st) {
-  constexpr int RMAX = kGemvMaxRows, RUN = 2;
-  if (a.H % (4 * RUN) != 0) return hipErrorInvalidValue;
-  const dim3 grid(a.H / (4 * RUN));
-  gemv_down_fp4_kernel<NB, RMAX, RUN, COMBINE><<<grid, 256, 0, st>>>(
+  if (a.H % 8 != 0) return hipErrorInvalidValue;
+  gemv_down_fp4_kernel<NB, COMBINE><<<dim3(a.H / 8), 512, 0, st>>>(
       a.dq, a.ds, a.hq_ws, a.hs_ws, a.offsets, a.row_of, a.topk_w, a.E, a.H, a.I, a.k, a.y_rows,
       a.out, a.out_bf16);
   return hipGetLastError();

@@ -19,32 +19,22 @@ struct GUWeights {
   int E, H, I;
 };
 
-// Loads a 32-code E4M3 chunk and converts it to fp16 pairs.
-__device__ __forceinline__ void load_act32(const uint8_t* __restrict__ p, Act16& a0, Act16& a1) {
-  const uint4 q0 = *reinterpret_cast<const uint4*>(p);
-  const uint4 q1 = *reinterpret_cast<const uint4*>(p + 16);
-  e4m3x16_to_h2(q0, a0);
-  e4m3x16_to_h2(q1, a1);
-}
-
-// This lane's activation chunks from already-quantised codes and scales.
+// This lane's activation chunks as raw E4M3 codes (two 16-byte halves per
+// chunk) and their block scales, loaded unconditionally (chunk index clamped
+// into the row; gate_up_rows masks the chunks past the end): the conversion
+// happens in gate_up_rows after the first weight row's loads are issued, so
+// the wait for these loads overlaps the weight stream.
 template <int NB>
-__device__ __forceinline__ void act_from_codes(const uint8_t* __restrict__ xq_row,
+__device__ __forceinline__ void load_act_codes(const uint8_t* __restrict__ xq_row,
                                                const float* __restrict__ xs_row, int H, int lane,
-                                               Act16 (&a0)[NB], Act16 (&a1)[NB],
-                                               float (&xsc)[NB]) {
+                                               uint4 (&aq)[NB][2], float (&xsc)[NB]) {
   const int nch = H >> 5;
 #pragma unroll
   for (int c = 0; c < NB; ++c) {
-    const int ch = lane + 64 * c;
-    if (ch < nch) {
-      load_act32(xq_row + 32 * ch, a0[c], a1[c]);
-      xsc[c] = xs_row[ch >> 2];
-    } else {
-      xsc[c] = 0.0f;
-      e4m3x16_to_h2(make_uint4(0, 0, 0, 0), a0[c]);
-      e4m3x16_to_h2(make_uint4(0, 0, 0, 0), a1[c]);
-    }
+    const int ch = min(lane + 64 * c, nch - 1);
+    aq[c][0] = *reinterpret_cast<const uint4*>(xq_row + 32 * ch);
+    aq[c][1] = *reinterpret_cast<const uint4*>(xq_row + 32 * ch + 16);
+    xsc[c] = xs_row[ch >> 2];
   }
 }
 
@@ -54,9 +44,8 @@ __device__ __forceinline__ void act_from_codes(const uint8_t* __restrict__ xq_ro
 // (IEEE division), code = E4M3(x/s), a zero block gives s = 0 and code 0.
 // Requires H/32 to be a multiple of 4 per 64-lane pass (H % 128 == 0).
 template <int NB>
-__device__ __forceinline__ void act_from_bf16(const uint16_t* __restrict__ x_row, int H, int lane,
-                                              Act16 (&a0)[NB], Act16 (&a1)[NB],
-                                              float (&xsc)[NB]) {
+__device__ __forceinline__ void quant_act_codes(const uint16_t* __restrict__ x_row, int H, int lane,
+                                                uint4 (&aq)[NB][2], float (&xsc)[NB]) {
   const int nch = H >> 5;
 #pragma unroll
   for (int c = 0; c < NB; ++c) {
@@ -90,23 +79,27 @@ __device__ __forceinline__ void act_from_bf16(const uint16_t* __restrict__ x_row
       q1.z = e4m3_pack4(v[24] / sc, v[25] / sc, v[26] / sc, v[27] / sc);
       q1.w = e4m3_pack4(v[28] / sc, v[29] / sc, v[30] / sc, v[31] / sc);
     }
-    e4m3x16_to_h2(q0, a0[c]);
-    e4m3x16_to_h2(q1, a1[c]);
-    xsc[c] = (ch < nch) ? sc : 0.0f;
+    aq[c][0] = q0;
+    aq[c][1] = q1;
+    xsc[c] = sc;
   }
 }
 
-// Streams 8 consecutive rows n0.. of group g's gate and up matrices for one
-// activation row with a DEPTH-deep register pipeline (the loads of row
-// i+DEPTH-1 are in flight while row i is multiplied), keeping each row's
-// per-lane partial sums; one butterfly reduce-scatter then gives every lane
-// one of the 16 totals (8 gate, 8 up), and 8 lanes finish
-// h[n] = silu(g_n) * u_n in parallel (returned in those lanes).
-template <int NB, int DEPTH>
+// Streams 4 consecutive rows n0.. of group g's gate and up matrices for one
+// activation row through a 2-deep register pipeline: the loads of row i+1
+// are issued after row i's products, which an empty asm statement enforces
+// by passing a zero that depends on row i's sums into row i+1's addresses
+// (without it the compiler hoists every load to the top, and the higher
+// register count costs more than the deeper pipeline gains).  One butterfly
+// reduce-scatter then gives every lane one of the 8 totals (4 gate, 4 up),
+// and 4 lanes finish h[n] = silu(g_n) * u_n in parallel (returned in those
+// lanes).
+constexpr int kGuRun = 4;
+template <int NB>
 __device__ __forceinline__ float gate_up_rows(const GUWeights& w, int g, int n0, int lane,
-                                              const Act16 (&a0)[NB], const Act16 (&a1)[NB],
-                                              const float (&xsc)[NB]) {
-  constexpr int RUN = 8;
+                                              const uint4 (&aq)[NB][2],
+                                              const float (&xs_raw)[NB]) {
+  constexpr int RUN = kGuRun, DEPTH = 2;
   const int H = w.H, I = w.I;
   const int nch = H >> 5;
   const size_t rowq = (size_t)(H >> 1), rows_ = (size_t)nch;
@@ -130,22 +123,30 @@ __device__ __forceinline__ float gate_up_rows(const GUWeights& w, int g, int n0,
   const uint8_t* usb = w.us + ((size_t)g * I + n0) * rows_;
   uint4 pg[DEPTH][NB], pu[DEPTH][NB];
   uint32_t psg[DEPTH][NB], psu[DEPTH][NB];
-#define BEF_GU_LOAD(SLOT, ROW)                                                      \
-  _Pragma("unroll") for (int c = 0; c < NB; ++c) {                                  \
-    pg[SLOT][c] = *reinterpret_cast<const uint4*>(gqb + (ROW) * rowq + co[c]);      \
-    pu[SLOT][c] = *reinterpret_cast<const uint4*>(uqb + (ROW) * rowq + co[c]);      \
-    psg[SLOT][c] = gsb[(ROW) * rows_ + cs[c]];                                      \
-    psu[SLOT][c] = usb[(ROW) * rows_ + cs[c]];                                      \
+  int dep = 0;
+#define BEF_GU_LOAD(SLOT, ROW)                                                        \
+  _Pragma("unroll") for (int c = 0; c < NB; ++c) {                                    \
+    pg[SLOT][c] = *reinterpret_cast<const uint4*>(gqb + (ROW) * rowq + co[c] + dep);  \
+    pu[SLOT][c] = *reinterpret_cast<const uint4*>(uqb + (ROW) * rowq + co[c] + dep);  \
+    psg[SLOT][c] = gsb[(ROW) * rows_ + cs[c] + dep];                                  \
+    psu[SLOT][c] = usb[(ROW) * rows_ + cs[c] + dep];                                  \
   }
+  BEF_GU_LOAD(0, 0)
+  // the activations, once the first row is in flight; chunks past the row
+  // end get scale 0
+  Act16 a0[NB], a1[NB];
+  float xsc[NB];
 #pragma unroll
-  for (int d = 0; d < DEPTH - 1; ++d) {
-    BEF_GU_LOAD(d, d)
+  for (int c = 0; c < NB; ++c) {
+    e4m3x16_to_h2(aq[c][0], a0[c]);
+    e4m3x16_to_h2(aq[c][1], a1[c]);
+    xsc[c] = (lane + 64 * c < nch) ? xs_raw[c] : 0.0f;
   }
-  float part[2 * RUN];  // [0..7] gate rows, [8..15] up rows
+  float part[2 * RUN];  // [0..3] gate rows, [4..7] up rows
 #pragma unroll
   for (int i = 0; i < RUN; ++i) {
-    if (i + DEPTH - 1 < RUN) {
-      BEF_GU_LOAD((i + DEPTH - 1) % DEPTH, i + DEPTH - 1)
+    if (i + 1 < RUN) {
+      BEF_GU_LOAD((i + 1) % DEPTH, i + 1)
     }
     const int sl = i % DEPTH;
     float ag = 0.0f, au = 0.0f;
@@ -156,46 +157,45 @@ __device__ __forceinline__ float gate_up_rows(const GUWeights& w, int g, int n0,
     }
     part[i] = ag;
     part[RUN + i] = au;
-    // keep the next row's loads from being hoisted above this row's math: the
-    // pipeline then holds DEPTH rows, not the whole run, and the arithmetic of
-    // early rows overlaps the transfer of later ones
-    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" : "+v"(dep) : "v"(ag), "v"(au));
   }
 #undef BEF_GU_LOAD
-  const float tot = butterfly16(part);  // j = 8*bit5 + 4*bit4 + 2*bit3 + bit2
-  const float up = xchg32(tot);         // lanes with bit5 = 0 receive the same row's up total
-  return silu_mul_accurate(tot, up);    // valid in h_lane() lanes
+  const float tot = butterfly8(part);  // j = 4*bit5 + 2*bit4 + bit3
+  const float up = xchg32(tot);        // lanes with bit5 = 0 receive the same row's up total
+  return silu_mul_accurate(tot, up);   // valid in h_lane() lanes
 }
 
 // The lanes that hold a finished h value after gate_up_rows (bit 5 = 0 and
-// bits 1..0 = 0: one per row), and the row n0 + h_row(lane) they hold.
-__device__ __forceinline__ bool h_lane(int lane) { return (lane & 35) == 0; }
-__device__ __forceinline__ int h_row(int lane) { return (lane >> 2) & 7; }
+// bits 2..0 = 0: one per row), and the row n0 + h_row(lane) they hold.
+__device__ __forceinline__ bool h_lane(int lane) { return (lane & 39) == 0; }
+__device__ __forceinline__ int h_row(int lane) { return (lane >> 3) & 3; }
 
 // The requantisation of h ahead of the down projection, done once, with no
 // device-scope fence (on this chip a release fence writes back the whole L2
-// of the XCD).  h moves between blocks only through 64-bit atomic
-// read-modify-writes, which are coherent across the XCDs:
-//  * each block that has finished rows n0b .. n0b+31 of h row r takes a
-//    ticket from the arrival counter of the 128-wide block n0b / 128; the 4
-//    tickets of one launch share tag = ticket / 4 + 1 (never 0; the slots
-//    start zeroed);
-//  * its 32 values go out as {tag, value bits} words (atomic exchange);
-//  * the block that drew the 4th ticket reads the 128 words (atomic or with
-//    0) until every tag is its own -- a bounded wait: past kSpinLimit
-//    rounds it flags MOE_STATUS_SYNC_TIMEOUT and carries on -- and writes
-//    the E4M3 codes and scale with the act_quant rule (s = amax / 448 by IEEE
-//    division, code = E4M3(v / s), zero block -> s = 0, code 0; dpshk.com
-//    article, section "核心实现二").
+// of the XCD) and no round trip for the blocks that only write.  h moves
+// between blocks through 64-bit atomics, which are coherent across the XCDs.
+// Each (row r, 128-wide block c of h) has an epoch word, advanced once per
+// launch that produces it:
+//  * every block producing rows of (r, c) reads the epoch e before it
+//    publishes (h_epoch, early, so the load overlaps the weight stream) and
+//    sends its values out as {e + 1, value bits} words (atomic exchange;
+//    never tag 0: the slots start zeroed);
+//  * the last of the 8 blocks of (r, c) in launch order reads the 128 words
+//    (atomic loads) until every tag is e + 1 -- a bounded wait: past
+//    kSpinLimit rounds it flags MOE_STATUS_SYNC_TIMEOUT and carries on --,
+//    writes the E4M3 codes and scale with the act_quant rule (s = amax / 448
+//    by IEEE division, code = E4M3(v / s), zero block -> s = 0, code 0;
+//    dpshk.com article, section "核心实现二"), then advances the epoch: every
+//    block of (r, c) read it before publishing, so none can miss the change.
 // Slots have a fixed row stride of kHSlotStride so that a slot always
-// belongs to the same counter, whatever I a call uses.
+// belongs to the same epoch word, whatever I a call uses.
 constexpr int kHSlotStride = 4096;   // largest I on the one-token path
 constexpr int kHSlotRows = 8;
 constexpr uint32_t kSpinLimit = 1u << 16;
 constexpr uint32_t kStatusSyncTimeout = 2u;  // MOE_STATUS_SYNC_TIMEOUT
 
 struct HExchange {
-  uint32_t* arrive;    // [kHSlotRows][kHSlotStride / 128] tickets
+  uint32_t* epochs;    // [kHSlotRows][kHSlotStride / 128]
   uint64_t* slots;     // [kHSlotRows][kHSlotStride] {tag, value bits}
   float* h;            // [rows][I] plain copy of h (inspection)
   uint8_t* hq;         // [rows][I] E4M3 codes
@@ -203,42 +203,51 @@ struct HExchange {
   uint32_t* status;
 };
 
+__device__ __forceinline__ uint32_t h_epoch(const HExchange& x, int r, int n0b) {
+  return __hip_atomic_load(x.epochs + r * (kHSlotStride / 128) + (n0b >> 7), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Called by every thread of a block whose waves hold h values hv (in the
+// h_lane lanes) for rows n0 .. n0+3 of h row r; the block's rows start at
+// n0b.  epoch: h_epoch(x, r, n0b), read by this block before.
 __device__ __forceinline__ void publish_h(const HExchange& x, float hv, int r, int I, int n0,
-                                          int n0b, int tid, int lane, uint32_t* s_ticket) {
-  constexpr uint32_t kBlocks = 128 / 32;
+                                          int n0b, int tid, int lane, uint32_t epoch) {
+  constexpr int kRowsPerBlock = 4 * kGuRun;
   const int c = n0b >> 7;
-  __syncthreads();  // readers of the previous ticket are done with it
-  if (tid == 0) *s_ticket = atomicAdd(x.arrive + r * (kHSlotStride / 128) + c, 1u);
-  __syncthreads();
-  const uint32_t ticket = *s_ticket;
-  const uint64_t tag = (uint64_t)(ticket / kBlocks + 1) << 32;
+  const uint64_t tag = (uint64_t)(epoch + 1u) << 32;
   unsigned long long* slot = reinterpret_cast<unsigned long long*>(x.slots) + r * kHSlotStride;
   if (h_lane(lane)) {
     const int n = n0 + h_row(lane);
     x.h[(size_t)r * I + n] = hv;
     atomicExch(slot + n, tag | __float_as_uint(hv));
   }
-  if (ticket % kBlocks == kBlocks - 1 && tid < 64) {
-    const int n = 128 * c + 2 * tid;
-    unsigned long long w0 = 0, w1 = 0;
-    uint32_t spins = 0;
-    bool ok = false;
-    for (;;) {
-      if ((w0 & 0xffffffff00000000ull) != tag) w0 = atomicOr(slot + n, 0ull);
-      if ((w1 & 0xffffffff00000000ull) != tag) w1 = atomicOr(slot + n + 1, 0ull);
-      ok = (w0 & 0xffffffff00000000ull) == tag && (w1 & 0xffffffff00000000ull) == tag;
-      if (__all(ok) || ++spins >= kSpinLimit) break;
-      __builtin_amdgcn_s_sleep(1);
-    }
-    if (!ok) atomicOr(x.status, kStatusSyncTimeout);
-    const float v0 = __uint_as_float((uint32_t)w0), v1 = __uint_as_float((uint32_t)w1);
-    const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-    const float sc = amax / 448.0f;
-    uint32_t q = 0;
-    if (amax != 0.0f) q = e4m3_pack4(v0 / sc, v1 / sc, 0.0f, 0.0f);
-    const size_t e = (size_t)r * I + n;
-    reinterpret_cast<uint16_t*>(x.hq + e)[0] = (uint16_t)q;
-    if (tid == 0) x.hs[(size_t)r * (I >> 7) + c] = sc;
+  if (n0b + kRowsPerBlock != 128 * (c + 1) || tid >= 64) return;
+  // the reader: the last block of this 128-wide block of h
+  const int n = 128 * c + 2 * tid;
+  unsigned long long w0 = 0, w1 = 0;
+  uint32_t spins = 0;
+  bool ok = false;
+  for (;;) {
+    if ((w0 & 0xffffffff00000000ull) != tag)
+      w0 = __hip_atomic_load(slot + n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((w1 & 0xffffffff00000000ull) != tag)
+      w1 = __hip_atomic_load(slot + n + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ok = (w0 & 0xffffffff00000000ull) == tag && (w1 & 0xffffffff00000000ull) == tag;
+    if (__all(ok) || ++spins >= kSpinLimit) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (!ok) atomicOr(x.status, kStatusSyncTimeout);
+  const float v0 = __uint_as_float((uint32_t)w0), v1 = __uint_as_float((uint32_t)w1);
+  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+  const float sc = amax / 448.0f;
+  uint32_t q = 0;
+  if (amax != 0.0f) q = e4m3_pack4(v0 / sc, v1 / sc, 0.0f, 0.0f);
+  const size_t e = (size_t)r * I + n;
+  reinterpret_cast<uint16_t*>(x.hq + e)[0] = (uint16_t)q;
+  if (tid == 0) {
+    x.hs[(size_t)r * (I >> 7) + c] = sc;
+    atomicAdd(x.epochs + r * (kHSlotStride / 128) + c, 1u);
   }
 }
 

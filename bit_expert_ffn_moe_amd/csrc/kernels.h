@@ -6,12 +6,11 @@
 namespace bef {
 
 constexpr int kRouteSmallT = 4;           // router: per-chunk blocks + last-block top-k
-constexpr int kRouteMaxChunks = 128;      // router: H / 64 for H <= 8192
+constexpr int kRouteMaxGroups = 32;       // router: 256-row groups, H <= 8192
 constexpr int kPermuteSmallPairs = 2048;  // permute: single block up to this many pairs
 constexpr int kPermuteTokBlock = 256;     // permute: tokens per block above that
 constexpr int kGemvMaxRows = 8;           // VALU GEMV path: rows (k + 1) per token
 constexpr int kGemmBM = 128;              // MFMA grouped GEMM: tokens per tile
-constexpr int kGemvRun = 8;               // VALU GEMV: weight rows streamed per wave
 constexpr uint32_t MOE_STATUS_BAD_EXPERT_ID_DEV = 1u;
 
 struct GemvArgs {
@@ -55,7 +54,7 @@ struct FrontArgs {
   int T, H, E, k;
   uint32_t* counter;      // router arrival counter (zero between launches)
   uint32_t* epoch;        // launch epoch of the tagged partials
-  uint64_t* slots;        // [H/64][T][E] tagged chunk partials
+  uint64_t* slots;        // [H/256][T][E] tagged group sums
   int32_t* ids;
   float* w;
   uint8_t* xq;

@@ -4,11 +4,12 @@
 // section "核心实现一"); 6 of 256 per token (ai-muninn.com
 // "[洋垃圾跑大模型 #3]").  Logits are fp32 in one fixed order so that the
 // chosen ids are reproducible bit for bit: 64-wide chunk partials, each a
-// chain of fused multiply-adds in ascending h starting from +0, then the
-// partials summed in ascending chunk order (the row keeps
-// one fixed accumulation order, as dpshk.com "核心实现四" does for its rows).
-// Every kernel below computes exactly that order; they differ only in how
-// the (token, expert, chunk) work is spread over the GPU.
+// chain of fused multiply-adds in ascending h starting from +0; sums of 4
+// consecutive chunks (256 rows) in ascending chunk order; then those group
+// sums in ascending group order (the row keeps one fixed accumulation order,
+// as dpshk.com "核心实现四" does for its rows; the pages leave the order
+// open).  Every kernel below computes exactly that order; they differ only
+// in how the (token, expert, chunk) work is spread over the GPU.
 //
 // Selection: order by (logit desc, id asc), keep k in rank order; weights
 // sigmoid(logit) renormalised over the chosen k (fp32, device expf).
@@ -21,45 +22,49 @@
 namespace bef {
 
 // One wavefront picks the top-k of E <= 256 logits held in LDS and writes
-// ids / weights.  Lane e owns experts e, e+64, e+128, e+192.
+// ids / weights.  Lane l owns experts l, l+64, l+128, l+192.  Each of the k
+// rounds takes every lane's best remaining expert (its lowest id among its
+// largest), the wave maximum by DPP, and -- when several lanes hold that
+// value -- the lowest of their ids by a DPP minimum; the winner's lane marks
+// it taken.
 __device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, int k,
                                           int32_t* __restrict__ ids_out,
-                                          float* __restrict__ w_out, int* ids_lds = nullptr) {
+                                          float* __restrict__ w_out) {
+  constexpr int kNone = 0x7fffffff;
   const int lane = threadIdx.x & 63;
   float v[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    v[i] = (e < E) ? z[e] : -FLT_MAX;
+    v[i] = (e < E) ? z[e] : 0.0f;
   }
   uint32_t taken = 0;
   float my_z = 0.0f;
   int my_id = 0;
   for (int j = 0; j < k; ++j) {
     float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    int bi = kNone;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
-      const bool ok = (e < E) && !((taken >> i) & 1u);
-      if (ok && (v[i] > bv || (v[i] == bv && e < bi))) {
+      if (e < E && !((taken >> i) & 1u) && (bi == kNone || v[i] > bv)) {
         bv = v[i];
         bi = e;
       }
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = __shfl_xor(bv, m, kWave);
-      const int oi = __shfl_xor(bi, m, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    const float m = wave_max_dpp(bv);
+    uint64_t cand = __ballot(bi != kNone && bv == m);
+    if (cand == 0) cand = __ballot(bi != kNone);  // only NaNs left
+    int win;
+    if (__popcll(cand) == 1)
+      win = __builtin_amdgcn_readlane(bi, __ffsll((long long)cand) - 1);
+    else
+      win = wave_min_dpp(((cand >> lane) & 1ull) ? bi : kNone);
+    const float wz = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), win & 63));
+    if (lane == (win & 63)) taken |= 1u << (win >> 6);
     if (lane == j) {
-      my_z = bv;
-      my_id = bi;
+      my_z = wz;
+      my_id = win;
     }
   }
   const float sg = (lane < k) ? 1.0f / (1.0f + expf(-my_z)) : 0.0f;
@@ -67,47 +72,54 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, in
   if (lane < k) {
     ids_out[lane] = my_id;
     w_out[lane] = sg / sum;
-    if (ids_lds) ids_lds[lane] = my_id;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Small T (decode, T <= kRouteSmallT): the front of the layer in one kernel.
-//  * Blocks 0 .. H/64-1: block c computes the chunk-c partials of every
-//    (token, expert) -- thread e streams column e of the router, all 64 loads
-//    issued before the multiply-adds.
+//  * Router blocks (group g, quarter q), g < H/256, q < E/64: wave j computes
+//    the chunk 4g+j partials of experts 64q .. 64q+63 for every token -- lane
+//    l streams 64 rows of column 64q+l, all loads issued before the
+//    multiply-adds -- and the block publishes the group sums, tagged with
+//    the launch's epoch, through 64-bit atomic exchanges (no device-scope
+//    fence).
 //  * When sh_h is set (single-token FP4 path), the next I/(4 RUN) blocks per
 //    token run the shared expert's gate+up GEMV rows (it needs no routing):
 //    its 8.9 MB stream overlaps the router's reduction chain; the last block
 //    of each 128-wide block of h requantises it.
 //  * Then, when xq is set, act_quant blocks of x (16 lanes per 128-block).
 //  * The last router block to arrive (arrival counter in the workspace,
-//    returned to zero by that block) sums the partials in chunk order, ranks
-//    the logits (thread e counts the logits that beat its own: larger, or
-//    equal with a lower id), computes the weights and, when asked, writes the
-//    permutation tables (the single-block form of S4) and the list of active
-//    routed groups.
+//    returned to zero by that block) reads the group sums with atomic loads
+//    until each carries this launch's tag (a bounded wait), adds them in
+//    group order, runs the top-k (one wave per token), computes the weights
+//    and, when asked, writes the permutation tables (the single-block form
+//    of S4) and the list of active routed groups; last, it advances the
+//    epoch.
 // ---------------------------------------------------------------------------
 template <int NB>
 __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
-  const int nc = a.H / 64;
+  const int nc = a.H / 64;                 // 64-row chunks
+  const int ng = (nc + 3) / 4;             // groups of 4 chunks
+  const int nq4 = (a.E + 63) / 64;         // 64-expert quarters
+  const int nr = ng * nq4;                 // router blocks
   const int tid = threadIdx.x;
   const int T = a.T, H = a.H, E = a.E, k = a.k;
-  int b = (int)blockIdx.x - nc;
+  int b = (int)blockIdx.x - nr;
   if (b >= 0 && a.sh_h) {
-    const int bpg = a.I / (4 * kGemvRun);
+    const int bpg = a.I / (4 * kGuRun);
     if (b < bpg * T) {
-      __shared__ uint32_t s_ticket;
-      const int t = b / bpg, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-      const int n0b = (b - t * bpg) * 4 * kGemvRun;
+      const int t = b / bpg, lane = tid & 63;
+      const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+      const int n0b = (b - t * bpg) * 4 * kGuRun;
       const GUWeights w = {a.sh_gq, a.sh_gs, a.sh_uq, a.sh_us, E, H, a.I};
-      Act16 a0[NB], a1[NB];
+      const HExchange hx = {a.hq_arrive, a.h_slots, a.sh_h, a.sh_hq, a.sh_hs, a.status};
+      const uint32_t epoch = h_epoch(hx, T * k + t, n0b);
+      uint4 aq[NB][2];
       float xsc[NB];
-      act_from_bf16<NB>(a.x + (size_t)t * H, H, lane, a0, a1, xsc);
-      const int n0 = n0b + wv * kGemvRun;
-      const float hv = gate_up_rows<NB, 3>(w, E, n0, lane, a0, a1, xsc);
-      publish_h(HExchange{a.hq_arrive, a.h_slots, a.sh_h, a.sh_hq, a.sh_hs, a.status}, hv,
-                T * k + t, a.I, n0, n0b, tid, lane, &s_ticket);
+      quant_act_codes<NB>(a.x + (size_t)t * H, H, lane, aq, xsc);
+      const int n0 = n0b + wv * kGuRun;
+      const float hv = gate_up_rows<NB>(w, E, n0, lane, aq, xsc);
+      publish_h(hx, hv, T * k + t, a.I, n0, n0b, tid, lane, epoch);
       return;
     }
     b -= bpg * T;
@@ -145,53 +157,73 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
     }
     return;
   }
-  const int c = blockIdx.x;
-  const int e = tid;
-  __shared__ float sx[kRouteSmallT][64];
+  // router block (group g, quarter q): rows 256g .. 256g+255 (chunks 4g ..
+  // 4g+3, one per wave) x experts 64q .. 64q+63 (one per lane)
+  const int w = tid >> 6, lane = tid & 63;
+  const int g = (int)blockIdx.x / nq4, q = (int)blockIdx.x - g * nq4;
+  const int c = 4 * g + w, e = 64 * q + lane;
+  __shared__ float sx[kRouteSmallT][256];
+  __shared__ float sp[4][kRouteSmallT][64];
   __shared__ float sz[kRouteSmallT][256];
   __shared__ int s_ids[kRouteSmallT * 16];
+  __shared__ float s_w[kRouteSmallT * 16];
   __shared__ int s_sorted[kRouteSmallT * 16];
+  __shared__ int s_rank[kRouteSmallT * 16];
   __shared__ uint32_t s_ticket;
   // this launch's tag; the epoch word changes only at the very end of a
   // launch, after every block has read it (each reads it before its ticket)
   const uint32_t epoch = __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint64_t tag = (uint64_t)(epoch + 1u) << 32;
-  for (int i = tid; i < T * 64; i += 256)
-    sx[i / 64][i % 64] = bf16_to_f32(a.x[(size_t)(i / 64) * H + 64 * c + (i % 64)]);
+  for (int i = tid; i < T * 256; i += 256) {
+    const int t = i >> 8, h = 256 * g + (i & 255);
+    sx[t][i & 255] = (h < H) ? bf16_to_f32(a.x[(size_t)t * H + h]) : 0.0f;
+  }
+  const bool mine = c < nc && e < E;
   uint32_t wv[64];
-  if (e < E) {
+  if (mine) {
     const uint16_t* col = a.wr + (size_t)(64 * c) * E + e;
 #pragma unroll
     for (int h = 0; h < 64; ++h) wv[h] = col[(size_t)h * E];
   }
   __syncthreads();
-  unsigned long long* slots = reinterpret_cast<unsigned long long*>(a.slots);
-  if (e < E) {
+  if (mine) {
     for (int t = 0; t < T; ++t) {
       float p = 0.0f;
 #pragma unroll
-      for (int h = 0; h < 64; ++h) p = fmaf(sx[t][h], bf16_to_f32(wv[h]), p);
-      atomicExch(slots + ((size_t)c * T + t) * E + e, tag | __float_as_uint(p));
+      for (int h = 0; h < 64; ++h) p = fmaf(sx[t][64 * w + h], bf16_to_f32(wv[h]), p);
+      sp[w][t][lane] = p;
+    }
+  }
+  __syncthreads();
+  unsigned long long* slots = reinterpret_cast<unsigned long long*>(a.slots);
+  if (tid < T * 64) {
+    // the group sum of this (token, expert), published with this launch's tag
+    const int t = tid >> 6, eg = 64 * q + lane;
+    if (eg < E) {
+      float G = sp[0][t][lane];
+      for (int jc = 1; jc < 4 && 4 * g + jc < nc; ++jc) G = G + sp[jc][t][lane];
+      atomicExch(slots + ((size_t)g * T + t) * E + eg, tag | __float_as_uint(G));
     }
   }
   __syncthreads();
   if (tid == 0) s_ticket = atomicAdd(a.counter, 1u);
   __syncthreads();
-  if (s_ticket != (uint32_t)(nc - 1)) return;
+  if (s_ticket != (uint32_t)(nr - 1)) return;
 
-  // the last block: logits in the fixed order (chunk partials summed in
-  // ascending chunk order), waiting -- bounded -- until every partial of this
-  // launch is visible
+  // the last block: logits in the fixed order (group sums added in
+  // ascending group order), waiting -- bounded -- until every group sum of
+  // this launch is visible; thread ez owns expert ez
+  const int ez = tid;
   bool ok = true;
   for (int t = 0; t < T; ++t) {
     float acc = -INFINITY;  // experts beyond E never rank
-    if (e < E) {
+    if (ez < E) {
       acc = 0.0f;
-      for (int c0 = 0; c0 < nc; c0 += 32) {
+      for (int c0 = 0; c0 < ng; c0 += 32) {
         unsigned long long v[32];
 #pragma unroll
         for (int i = 0; i < 32; ++i)
-          v[i] = (c0 + i < nc) ? __hip_atomic_load(slots + ((size_t)(c0 + i) * T + t) * E + e,
+          v[i] = (c0 + i < ng) ? __hip_atomic_load(slots + ((size_t)(c0 + i) * T + t) * E + ez,
                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                : tag;
         for (uint32_t spins = 0;;) {
@@ -200,7 +232,7 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
           for (int i = 0; i < 32; ++i)
             if ((v[i] & 0xffffffff00000000ull) != tag) {
               all = false;
-              v[i] = __hip_atomic_load(slots + ((size_t)(c0 + i) * T + t) * E + e,
+              v[i] = __hip_atomic_load(slots + ((size_t)(c0 + i) * T + t) * E + ez,
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
           if (all) break;
@@ -212,55 +244,63 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < 32; ++i)
-          if (c0 + i < nc) acc = (c0 + i == 0) ? __uint_as_float((uint32_t)v[i])
+          if (c0 + i < ng) acc = (c0 + i == 0) ? __uint_as_float((uint32_t)v[i])
                                                : acc + __uint_as_float((uint32_t)v[i]);
       }
     }
-    sz[t][e] = acc;
+    sz[t][ez] = acc;
   }
   if (!ok) atomicOr(a.status, kStatusSyncTimeout);
   __syncthreads();
-  // top-k: wave t ranks token t (order: logit desc, id asc)
-  const int w = tid >> 6, lane = tid & 63;
-  if (w < T) topk_wave(sz[w], E, k, a.ids + w * k, a.w + w * k, s_ids + w * k);
+  // top-k: wave t ranks token t (order: logit desc, id asc).  Results stay
+  // in LDS until the last barrier: a barrier after global stores would wait
+  // for them to complete.
+  if (w < T) topk_wave(sz[w], E, k, s_ids + w * k, s_w + w * k);
   __syncthreads();
-  if (a.offsets) {
-    // permutation tables: the P = T*k <= 64 pairs sorted by (expert, pair
-    // index) in wave 0 -- the stable counting-sort order of the general path
-    const int P = T * k;
-    if (w == 0) {
-      const int id = (lane < P) ? s_ids[lane] : 0x7fffffff;
-      int rank = 0;
-      for (int q = 0; q < P; ++q) {
-        const int iq = s_ids[q];
-        rank += (iq < id) | ((iq == id) & (q < lane));
-      }
-      if (lane < P) {
-        s_sorted[rank] = id;
-        a.row_token[rank] = lane / k;
-        a.row_of[(size_t)(lane / k) * (k + 1) + (lane % k)] = rank;
-      }
-      if (lane < T) {
-        a.row_token[P + lane] = lane;
-        a.row_of[(size_t)lane * (k + 1) + k] = P + lane;
-      }
+  const int P = T * k;
+  if (a.offsets && w == 0) {
+    // permutation order: the P = T*k <= 64 pairs sorted by (expert, pair
+    // index) -- the stable counting-sort order of the general path
+    const int id = (lane < P) ? s_ids[lane] : 0x7fffffff;
+    int rank = 0;
+    for (int qq = 0; qq < P; ++qq) {
+      const int iq = s_ids[qq];
+      rank += (iq < id) | ((iq == id) & (qq < lane));
     }
-    __syncthreads();
+    if (lane < P) {
+      s_sorted[rank] = id;
+      s_rank[lane] = rank;
+    }
+  }
+  __syncthreads();
+  if (tid < P) {
+    a.ids[tid] = s_ids[tid];
+    a.w[tid] = s_w[tid];
+  }
+  if (a.offsets) {
+    if (tid < P) {
+      a.row_token[s_rank[tid]] = tid / k;
+      a.row_of[(size_t)(tid / k) * (k + 1) + (tid % k)] = s_rank[tid];
+    }
+    if (tid < T) {
+      a.row_token[P + tid] = tid;
+      a.row_of[(size_t)tid * (k + 1) + k] = P + tid;
+    }
     // offsets[g] = number of pairs with expert < g (lower bound in the
     // sorted ids); the shared group E holds one row per token
-    for (int g = tid; g <= E + 1; g += 256) {
+    for (int g2 = tid; g2 <= E + 1; g2 += 256) {
       int v = P + T;
-      if (g <= E) {
+      if (g2 <= E) {
         int lo = 0, hi = P;
         while (lo < hi) {
           const int mid = (lo + hi) >> 1;
-          if (s_sorted[mid] < g) lo = mid + 1; else hi = mid;
+          if (s_sorted[mid] < g2) lo = mid + 1; else hi = mid;
         }
         v = lo;
       }
-      a.offsets[g] = v;
+      a.offsets[g2] = v;
     }
-    if (a.active && w == 0) {
+    if (a.active && w == 1) {
       // one entry per distinct routed expert, in expert order
       const bool start = lane < P && (lane == 0 || s_sorted[lane] != s_sorted[lane - 1]);
       const uint64_t m = __ballot(start);
@@ -297,11 +337,11 @@ __global__ __launch_bounds__(256) void route_tile_kernel(const uint16_t* __restr
   const int t0 = blockIdx.x * 32;
   const int tid = threadIdx.x;
   const int ty = tid >> 5, tx = tid & 31;
-  float acc[4][8];
+  float acc[4][8], grp[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+    for (int j = 0; j < 8; ++j) acc[i][j] = grp[i][j] = 0.0f;
   const int nc = H / 64;
   for (int c = 0; c < nc; ++c) {
     {
@@ -353,7 +393,13 @@ __global__ __launch_bounds__(256) void route_tile_kernel(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = (c == 0) ? p[i][j] : acc[i][j] + p[i][j];
+      for (int j = 0; j < 8; ++j) grp[i][j] = (c % 4 == 0) ? p[i][j] : grp[i][j] + p[i][j];
+    if (c % 4 == 3 || c == nc - 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = (c < 4) ? grp[i][j] : acc[i][j] + grp[i][j];
+    }
     __syncthreads();
   }
 #pragma unroll
@@ -390,16 +436,17 @@ void set_route_sync(FrontArgs& a, WsCtl* ctl) {
 
 hipError_t launch_route_front(const FrontArgs& a, hipStream_t st) {
   if (a.T < 1 || a.T > kRouteSmallT || a.k > 16 || a.E > 256 || a.H % 64 != 0 ||
-      a.H / 64 > kRouteMaxChunks || !a.counter || !a.epoch || !a.slots || !a.status)
+      (a.H / 64 + 3) / 4 > kRouteMaxGroups || !a.counter || !a.epoch || !a.slots || !a.status)
     return hipErrorInvalidValue;
   int nq = 0, nsh = 0;
   if (a.xq) nq = (int)(((int64_t)a.T * (a.H / 128) * 16 + 255) / 256);
   if (a.sh_h) {
     if (a.I % 128 != 0 || a.I > kHSlotStride || a.T * (a.k + 1) > kHSlotRows)
       return hipErrorInvalidValue;
-    nsh = (a.I / (4 * kGemvRun)) * a.T;
+    nsh = (a.I / (4 * kGuRun)) * a.T;
   }
-  const dim3 grid(a.H / 64 + nsh + nq);
+  const int nr = (a.H / 64 + 3) / 4 * ((a.E + 63) / 64);
+  const dim3 grid(nr + nsh + nq);
   const int nb = (a.H / 32 + 63) / 64;
   if (nb <= 1)
     route_front_kernel<1><<<grid, dim3(256), 0, st>>>(a);

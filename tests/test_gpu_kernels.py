@@ -138,6 +138,28 @@ def test_route_ties_pick_lower_ids(T):
     assert np.array_equal(ir, np.tile(np.arange(k), (T, 1)))
 
 
+@pytest.mark.parametrize("T", [1, 4, 9])
+def test_route_ties_within_and_across_lanes(T):
+    """Experts 3, 67, 131, 195 (one wave lane owns all four) and 10 tie at
+    the top; the lower ids must win, in order."""
+    H, E, k = 256, 256, 8
+    x = synth.normal_bf16(33, 1, (T, H), 1.0) & np.uint16(0x7FFF)   # |x|: sign bit cleared
+    wr = synth.normal_bf16(33, 2, (H, E), 0.02)
+    big = np.full(H, 0x3F80, np.uint16)    # 1.0: far above every other column's logit
+    for e in (3, 10, 67, 131, 195):
+        wr[:, e] = big
+    ws_b = 1 << 22
+    ws = torch.zeros(ws_b, dtype=torch.uint8, device="cuda")
+    moe.moe_workspace_init(ws, ws_b)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_route(to_dev(x), to_dev(wr), T, H, E, k, ids, w, ws, ws_b)
+    ir, wref = orc.route(x, wr, k)
+    assert np.array_equal(ir[:, :5], np.tile([3, 10, 67, 131, 195], (T, 1)))
+    assert np.array_equal(to_host(ids), ir)
+    assert np.allclose(to_host(w), wref, rtol=1e-5, atol=0)
+
+
 # ----------------------------------------------------------------- S4 -----
 
 def _permute_gpu(ids, E):

@@ -29,6 +29,27 @@ def test_router_logits_within_fp32_bound_of_exact_sum():
     assert np.all(np.abs(z - exact) <= bound)
 
 
+def test_router_sum_order_groups_four_chunks():
+    """Worked case of the fixed order: x = 1, H = 512 (8 chunks of 64).
+    Expert 0: chunk 0 sums to 2^24 and chunks 4..7 to 1 each.  The group of
+    chunks 4..7 reaches 4 before it meets 2^24, so z = 2^24 + 4 exactly (one
+    running sum over the chunks would drop every +1 and give 2^24).  Expert
+    1 holds the same values in the reverse order: 1 + 1 + 1 + 1 = 4 in group
+    0, then 4 + 2^24."""
+    H, E = 512, 2
+    x = np.full((1, H), 0x3F80, np.uint16)           # bf16 1.0
+    wr = np.zeros((H, E), np.uint16)
+    wr[5, 0] = 0x4B80                                  # bf16 2^24
+    for c in range(4, 8):
+        wr[64 * c + 7, 0] = 0x3F80
+    for c in range(4):
+        wr[64 * c + 3, 1] = 0x3F80
+    wr[64 * 6 + 1, 1] = 0x4B80
+    z = orc.router_logits(x, wr)
+    assert z[0, 0] == np.float32(2 ** 24 + 4)
+    assert z[0, 1] == np.float32(2 ** 24 + 4)
+
+
 def test_router_zero_weights_give_lowest_ids_and_equal_weights():
     L = _tiny()
     z = orc.router_logits(L.x, np.zeros_like(L.wr))
