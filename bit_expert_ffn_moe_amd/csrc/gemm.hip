@@ -1,6 +1,6 @@
 // gemm.hip -- S5/S6 for many tokens: grouped GEMM on the CDNA4 matrix cores.
 //
-// Prefill and batched verification are compute-bound (tcti.cn post, section
+// Prefill and batched verification are compute-heavy (tcti.cn post, section
 // "DeepSeek-V4-Flash的可能性": prefill and decode need different operators);
 // tokens are grouped by expert so that each expert's weights stream once for
 // all of its tokens (dpshk.com article, section "核心实现三").  The products
@@ -9,11 +9,11 @@
 // (dpshk.com article, section "核心实现四"):
 //   v_mfma_scale_f32_16x16x128_f8f6f4, A = E4M3 activations (scale 2^0),
 //   B = E2M1 weights with their UE8M0 scale per 32 K as the hardware B scale
-//   (FP4), or B = E4M3 weights (FP8, block scale applied below).
+//   (FP4), or B = E4M3 weights (FP8, fp32 block scale applied below).
 // The fp32 activation scale (amax/448 per 128 of K) cannot ride in the MFMA
-// scale operand, so each 128-deep K step is issued into a fresh accumulator
-// and folded into the running sum with one FMA per output: acc += s_x * d
-// (times the fp32 weight block scale for FP8).
+// scale operand, so each 128-deep K step is issued into a fresh result and
+// folded into the running sum with one FMA per output: acc += s_x * d (times
+// the weight block scale for FP8).
 //
 // Operand layout of the 16x16x128 f8f6f4 MFMA (measured on gfx950 with a
 // one-hot probe): lane l supplies row/column l%16; lane group q = l/16 holds
@@ -22,360 +22,397 @@
 // an FP8 operand (two 16-byte halves).  The result holds rows 4q..4q+3 of
 // column l%16.
 //
-// Tile: BM tokens x BN columns, K step 128, 256 threads = 4 waves, wave w
-// owning BN/4 columns for all BM rows.  A (gathered token rows) is staged in
-// LDS, double buffered, with the 16-byte chunk index XOR-swizzled by row so
-// the MFMA operand reads are conflict-free; B is read straight from HBM into
-// registers (each lane's 16 or 32 bytes are contiguous in a weight row) and
-// prefetched one K step ahead.  A group's tiles are found from the offsets
-// table inside the block; surplus blocks of the upper-bound grid exit.
+// Shapes: an expert sees ~200 tokens in a uniformly routed 8192-token
+// prefill, so its weights carry ~2x200 flops per byte -- below the chip's
+// ~600 flop/byte balance point: the weights must stream from HBM once.  A
+// tile is 128 tokens x 256 output columns (gate+up: 128 columns of I for both
+// matrices, so SwiGLU and the per-128 requant of h finish in the tile); 4
+// waves, one per SIMD, as 2 (M) x 2 (N), 64 x 128 outputs each (128 fp32
+// accumulators per lane, up to 512 registers per wave).  Per 128-deep K step
+// the block stages its A rows (gathered token rows) and B rows (weight rows)
+// in LDS with direct global->LDS loads (global_load_lds_dwordx4), three
+// stages deep in separate LDS objects so that the compiler's wait tracking
+// lets the next stages' loads fly while one is multiplied; the 16-byte chunk
+// positions are XOR-swizzled by row so the MFMA operand reads are
+// conflict-free.
+//
+// The grid is persistent (one block per CU) and XCD-aware: the work items
+// (expert M-tile, N-block), N-blocks of one M-tile adjacent, are split into 8
+// contiguous ranges, one per XCD (block b runs on XCD b mod 8).  The 32
+// blocks of an XCD thus work on neighbouring items together: the N-blocks of
+// an M-tile share its activation rows in the XCD's L2, and the M-tiles of
+// one expert (16 items apart for I = 2048) read the same weight rows at the
+// same time, so those stream from HBM about once.
 #include "common.h"
 #include "kernels.h"
 
 namespace bef {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* glb_ptr_t;
+
+constexpr int kTM = 128;      // tokens per tile
+constexpr int kTN = 256;      // output columns per tile
+constexpr int kGThreads = 256;
+
+// s_waitcnt immediates (gfx9: vmcnt [3:0] + [15:14], expcnt [6:4], lgkmcnt [11:8])
+constexpr int waitcnt_vm(int n) { return 0xF70 | (n & 0xF) | ((n >> 4) << 14); }
+constexpr int kWaitLgkm0 = 0xC07F;
+
+__device__ __forceinline__ void dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)l, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)l, 4, 0, 0);
+}
 
 __device__ __forceinline__ uint32_t e4m3_1(float v) {
   v = __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xffu;
 }
 
+// LDS byte offset of 16-byte chunk c of row r: rows of 128 bytes (E4M3, one
+// K step) swizzle by bits 3..1 of r, rows of 64 bytes (E2M1) by bits 3..2.
+__device__ __forceinline__ int sw128(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+__device__ __forceinline__ int sw64(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+
 template <int FMT>
-struct BFrag;
-template <>
-struct BFrag<1> {  // FP4: 16 bytes + one UE8M0 byte per lane
-  uint4 q;
-  uint32_t s;
-};
-template <>
-struct BFrag<2> {  // FP8: 32 bytes per lane
-  uint4 q0, q1;
+struct StageBytes {
+  static constexpr int kB = FMT == 1 ? kTN * 64 : kTN * 128;
 };
 
-// Main loop shared by both GEMMs.  Rows: a_row[j] points at the token row of
-// A chunk j (K offset 0), xs_row at that row's scale row (only threads < BM).
-// B: bsrc[j] points at this lane's first bytes of weight row j (K offset 0);
-// bscale[j] at its UE8M0 scales (FP4) -- for FP8 wsc[j] points at the fp32
-// block scales along K of the column block of sub-tile j.
-template <int BM, int NJ, int FMT>
-__device__ __forceinline__ void mfma_mainloop(const uint8_t* const (&a_row)[BM / 32],
-                                              const int (&a_dst)[BM / 32], const float* xs_row,
-                                              const uint8_t* const (&bsrc)[NJ],
-                                              const uint8_t* const (&bscale)[NJ],
-                                              const float* const (&wsc)[NJ], int KS,
-                                              uint8_t (*sA)[BM * 128], float (*sXs)[BM],
-                                              v4f_t (&acc)[BM / 16][NJ]) {
-  constexpr int MT = BM / 16;
-  constexpr int ACH = BM / 32;
+// GU = gate+up (+SwiGLU, requant of h), else down.
+template <int FMT, bool GU>
+__global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
+  constexpr int KB = StageBytes<FMT>::kB;
+  constexpr int NBI = FMT == 1 ? 4 : 8;  // B DMA instructions per wave per K step
+  constexpr int kLoads = 4 + NBI + (FMT == 1 ? 2 : 1);  // DMA instructions per wave per stage
+  __shared__ __align__(16) uint8_t sA0[kTM * 128];
+  __shared__ __align__(16) uint8_t sA1[kTM * 128];
+  __shared__ __align__(16) uint8_t sA2[kTM * 128];
+  __shared__ __align__(16) uint8_t sB0[KB];
+  __shared__ __align__(16) uint8_t sB1[KB];
+  __shared__ __align__(16) uint8_t sB2[KB];
+  __shared__ __align__(16) uint32_t sS0[FMT == 1 ? kTN : 1];  // FP4: 4 UE8M0 bytes per B row
+  __shared__ __align__(16) uint32_t sS1[FMT == 1 ? kTN : 1];
+  __shared__ __align__(16) uint32_t sS2[FMT == 1 ? kTN : 1];
+  __shared__ __align__(16) float sX0[kTM];  // activation scales of the K step
+  __shared__ __align__(16) float sX1[kTM];
+  __shared__ __align__(16) float sX2[kTM];
+  __shared__ float s_amax[2][kTM];
+  __shared__ float s_wsc[2][64];  // FP8 weight block scales of the tile, per K step
+  __shared__ int s_mtp[258];  // m-tile prefix per group
+  __shared__ int s_tok[kTM];
+  __shared__ int stmp[kGThreads / 64];
+
   const int tid = threadIdx.x, lane = tid & 63;
-  const int kq = lane >> 4;
-  uint4 a_stage[ACH];
-  float xs_stage = 0.0f;
-  BFrag<FMT> bc[NJ], bn[NJ];
-  float fc[NJ], fn[NJ];
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w & 1, wn = w >> 1, q = lane >> 4;
+  const int E = a.E, H = a.H, I = a.I;
+  const int K = GU ? H : I;  // contraction length
+  const int KS = K >> 7;
+  const int NB = GU ? (I >> 7) : (H / kTN);  // N-blocks per M-tile
 
-  auto load_a = [&](int ks) {
+  // m-tiles per group and their exclusive prefix (groups 0..E, E = shared)
+  {
+    int my_mt[2] = {0, 0}, inc[2];
 #pragma unroll
-    for (int j = 0; j < ACH; ++j) a_stage[j] = *reinterpret_cast<const uint4*>(a_row[j] + ks * 128);
-    if (tid < BM) xs_stage = xs_row[ks];
-  };
-  auto store_a = [&](int buf) {
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int gg = tid + kGThreads * h2;
+      if (gg <= E) {
+        const int c = a.offsets[gg + 1] - a.offsets[gg];
+        my_mt[h2] = (c + kTM - 1) / kTM;
+      }
+      inc[h2] = my_mt[h2];
 #pragma unroll
-    for (int j = 0; j < ACH; ++j) *reinterpret_cast<uint4*>(&sA[buf][a_dst[j]]) = a_stage[j];
-    if (tid < BM) sXs[buf][tid] = xs_stage;
-  };
-  auto load_b = [&](int ks, BFrag<FMT>(&b)[NJ], float(&f)[NJ]) {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      if constexpr (FMT == 1) {
-        b[j].q = *reinterpret_cast<const uint4*>(bsrc[j] + ks * 64);
-        b[j].s = bscale[j][ks * 4];
-        f[j] = 1.0f;
-      } else {
-        b[j].q0 = *reinterpret_cast<const uint4*>(bsrc[j] + ks * 128);
-        b[j].q1 = *reinterpret_cast<const uint4*>(bsrc[j] + ks * 128 + 64);
-        f[j] = wsc[j][ks];
+      for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(inc[h2], d, kWave);
+        if (lane >= d) inc[h2] += t;
       }
     }
-  };
-
-  load_a(0);
-  load_b(0, bc, fc);
-  store_a(0);
-  __syncthreads();
-  const v4f_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int ks = 0; ks < KS; ++ks) {
-    const int buf = ks & 1;
-    const bool more = ks + 1 < KS;
-    if (more) {
-      load_a(ks + 1);
-      load_b(ks + 1, bn, fn);
+    if (lane == 63) stmp[w] = inc[0];
+    __syncthreads();
+    int base = 0, total = 0;
+#pragma unroll
+    for (int i = 0; i < kGThreads / 64; ++i) {
+      base += (i < w) ? stmp[i] : 0;
+      total += stmp[i];
     }
+    if (tid <= E) s_mtp[tid] = base + inc[0] - my_mt[0];
+    __syncthreads();
+    // groups 256.. (only group 256 exists: E <= 256) follow in wave 0
+    if (w == 0 && kGThreads + lane <= E) s_mtp[kGThreads + lane] = total + inc[1] - my_mt[1];
+    if (tid == 0) {
+      int t2 = total;
+      for (int gg = kGThreads; gg <= E; ++gg) t2 += (a.offsets[gg + 1] - a.offsets[gg] + kTM - 1) / kTM;
+      s_mtp[E + 1] = t2;
+    }
+    __syncthreads();
+  }
+  const int total_mt = s_mtp[E + 1];
+  const int W = total_mt * NB;
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
+  const int w_lo = (int)(((long long)xcd * W) >> 3), w_hi = (int)(((long long)(xcd + 1) * W) >> 3);
+
+  for (int wi = w_lo + local; wi < w_hi; wi += per_xcd) {
+    const int mtg = __builtin_amdgcn_readfirstlane(wi / NB);
+    const int nb = __builtin_amdgcn_readfirstlane(wi - mtg * NB);
+    int lo = 0, hi = E + 2;  // first index with s_mtp > mtg
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_mtp[mid] <= mtg) lo = mid + 1; else hi = mid;
+    }
+    // block-uniform values in scalar registers (scalar loads of the scales)
+    const int g = __builtin_amdgcn_readfirstlane(lo - 1);
+    const int row0 = __builtin_amdgcn_readfirstlane(a.offsets[g] + (mtg - s_mtp[g]) * kTM);
+    const int nrows = __builtin_amdgcn_readfirstlane(min(kTM, a.offsets[g + 1] - row0));
+    if (GU) {
+      for (int i = tid; i < kTM; i += kGThreads) s_tok[i] = a.row_token[row0 + min(i, nrows - 1)];
+      __syncthreads();
+    }
+
+    // ---- per-lane DMA sources of this tile (K offset 0) ----
+    const uint8_t* srcA[4];
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi) {
-      const int r = 16 * mi + (lane & 15);
-      const uint8_t* rowp = &sA[buf][r * 128];
-      const uint4 a0 = *reinterpret_cast<const uint4*>(rowp + ((kq ^ (r & 7)) << 4));
-      const uint4 a1 = *reinterpret_cast<const uint4*>(rowp + (((kq + 4) ^ (r & 7)) << 4));
-      const v8i_t av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                        (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-      const float4 xsv = *reinterpret_cast<const float4*>(&sXs[buf][16 * mi + 4 * kq]);
+    for (int i = 0; i < 4; ++i) {
+      const int p = (w * 4 + i) * 64 + lane, r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
+      const int rr = min(r, nrows - 1);
+      srcA[i] = (GU ? a.xq + (size_t)s_tok[rr] * H : a.hq + (size_t)(row0 + rr) * I) + 16 * c;
+    }
+    const size_t brow_bytes = FMT == 1 ? (size_t)(K >> 1) : (size_t)K;
+    auto brow = [&](int r) -> size_t {  // weight row of B row r of the tile
+      if (GU) return (size_t)g * I + (size_t)nb * 128 + (r & 127);
+      return (size_t)g * H + (size_t)nb * kTN + r;
+    };
+    const uint8_t* bmat_g = GU ? a.gq : a.dq;
+    const uint8_t* bmat_u = GU ? a.uq : a.dq;
+    const uint8_t* srcB[NBI];
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        v4f_t d;
-        if constexpr (FMT == 1) {
-          const v8i_t bv = {(int)bc[j].q.x, (int)bc[j].q.y, (int)bc[j].q.z, (int)bc[j].q.w,
-                            0, 0, 0, 0};
-          d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, zero, 0, 4, 0, 127, 0,
-                                                               (int)bc[j].s);
-          acc[mi][j][0] = fmaf(xsv.x, d[0], acc[mi][j][0]);
-          acc[mi][j][1] = fmaf(xsv.y, d[1], acc[mi][j][1]);
-          acc[mi][j][2] = fmaf(xsv.z, d[2], acc[mi][j][2]);
-          acc[mi][j][3] = fmaf(xsv.w, d[3], acc[mi][j][3]);
+    for (int i = 0; i < NBI; ++i) {
+      const int p = (w * NBI + i) * 64 + lane;
+      const int r = FMT == 1 ? (p >> 2) : (p >> 3);
+      const int c = FMT == 1 ? ((p & 3) ^ ((r >> 2) & 3)) : ((p & 7) ^ ((r >> 1) & 7));
+      const uint8_t* m = (GU && r >= 128) ? bmat_u : bmat_g;
+      srcB[i] = m + brow(r) * brow_bytes + 16 * c;
+    }
+    const uint8_t* srcS = nullptr;  // FP4 scales: B row w*64 + lane
+    if (FMT == 1) {
+      const int r = w * 64 + lane;
+      const uint8_t* sm = (GU && r >= 128) ? (const uint8_t*)a.us
+                                           : (const uint8_t*)(GU ? a.gs : a.ds);
+      srcS = sm + brow(r) * (size_t)(K >> 5);
+    }
+    const float* srcX;  // activation scales: A row w*32 + lane (lanes < 32)
+    {
+      const int rr = min(w * 32 + (lane & 31), nrows - 1);
+      srcX = GU ? a.xs + (size_t)s_tok[rr] * KS : a.hs + (size_t)(row0 + rr) * KS;
+    }
+    // FP8 weight block scales of the tile into LDS, once: [0] gate (GU) or
+    // columns 0..127 (down), [1] up (GU) or columns 128..255 (down)
+    if (FMT == 2) {
+      for (int t = tid; t < 2 * KS; t += kGThreads) {
+        const int hsel = t >= KS, ks = t - hsel * KS;
+        const float* src = GU ? (const float*)(hsel ? a.us : a.gs) + ((size_t)g * (I >> 7) + nb) * KS
+                              : (const float*)a.ds + ((size_t)g * (H >> 7) + nb * 2 + hsel) * KS;
+        s_wsc[hsel][ks] = src[ks];
+      }
+      __syncthreads();
+    }
+
+    auto issue = [&](int ks, uint8_t* sA, uint8_t* sB, uint32_t* sS, float* sX) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma16(srcA[i] + ks * 128, sA + (w * 4 + i) * 1024);
+#pragma unroll
+      for (int i = 0; i < NBI; ++i)
+        dma16(srcB[i] + ks * (FMT == 1 ? 64 : 128), sB + (w * NBI + i) * 1024);
+      if (FMT == 1) dma4(srcS + ks * 4, sS + w * 64);
+      if (lane < 32) dma4(srcX + ks, sX + w * 32);
+    };
+
+    v4f_t acc[4][8];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[mi][j] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
+    // a wave whose 64 rows hold no token skips the multiplies (the rows of a
+    // partly filled 64-row band are multiplied anyway: clamped copies of a
+    // real row, never stored)
+    const bool live = nrows > wm * 64;
+
+    auto compute = [&](int ks, const uint8_t* sA, const uint8_t* sB, const uint32_t* sS,
+                       const float* sX) {
+      if (!live) return;
+      v8i_t av[4];
+      float4 xv[4];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const int r = wm * 64 + 16 * mi + (lane & 15);
+        const uint4 a0 = *reinterpret_cast<const uint4*>(sA + sw128(r, q));
+        const uint4 a1 = *reinterpret_cast<const uint4*>(sA + sw128(r, q + 4));
+        av[mi] = (v8i_t){(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                         (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        xv[mi] = *reinterpret_cast<const float4*>(sX + wm * 64 + 16 * mi + 4 * q);
+      }
+      float f0 = 1.0f, f1 = 1.0f;
+      if (FMT == 2) {
+        f0 = s_wsc[GU ? 0 : wn][ks];
+        f1 = GU ? s_wsc[1][ks] : f0;
+      }
+      const v4f_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int n = GU ? ((j < 4 ? 0 : 128) + 64 * wn + 16 * (j & 3) + (lane & 15))
+                         : (128 * wn + 16 * j + (lane & 15));
+        v8i_t bv;
+        int sb = 127;
+        if (FMT == 1) {
+          const uint4 b0 = *reinterpret_cast<const uint4*>(sB + sw64(n, q));
+          bv = (v8i_t){(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
+          sb = (int)((sS[n] >> (8 * q)) & 0xffu);
         } else {
-          const v8i_t bv = {(int)bc[j].q0.x, (int)bc[j].q0.y, (int)bc[j].q0.z, (int)bc[j].q0.w,
-                            (int)bc[j].q1.x, (int)bc[j].q1.y, (int)bc[j].q1.z, (int)bc[j].q1.w};
-          d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, zero, 0, 0, 0, 127, 0, 127);
-          const float f = fc[j];
-          acc[mi][j][0] = fmaf(xsv.x * f, d[0], acc[mi][j][0]);
-          acc[mi][j][1] = fmaf(xsv.y * f, d[1], acc[mi][j][1]);
-          acc[mi][j][2] = fmaf(xsv.z * f, d[2], acc[mi][j][2]);
-          acc[mi][j][3] = fmaf(xsv.w * f, d[3], acc[mi][j][3]);
+          const uint4 b0 = *reinterpret_cast<const uint4*>(sB + sw128(n, q));
+          const uint4 b1 = *reinterpret_cast<const uint4*>(sB + sw128(n, q + 4));
+          bv = (v8i_t){(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                       (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+        }
+        const float f = (GU && j >= 4) ? f1 : f0;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+          const v4f_t d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              av[mi], bv, zero, 0, FMT == 1 ? 4 : 0, 0, 127, 0, sb);
+          acc[mi][j][0] = fmaf(xv[mi].x * f, d[0], acc[mi][j][0]);
+          acc[mi][j][1] = fmaf(xv[mi].y * f, d[1], acc[mi][j][1]);
+          acc[mi][j][2] = fmaf(xv[mi].z * f, d[2], acc[mi][j][2]);
+          acc[mi][j][3] = fmaf(xv[mi].w * f, d[3], acc[mi][j][3]);
         }
       }
+    };
+
+    // ---- K loop: three stages in separate LDS objects.  Step ks waits for
+    // its stage (the loads of step ks+1 may stay in flight), passes one
+    // barrier -- after which every wave is done with step ks-1's stage --,
+    // issues step ks+2 into that stage, then multiplies. ----
+    issue(0, sA0, sB0, sS0, sX0);
+    if (KS > 1) issue(1, sA1, sB1, sS1, sX1);
+#define BEF_GEMM_STEP(KS_, SA, SB, SS, SX, NA, NB_, NS, NX)                   \
+    {                                                                        \
+      if ((KS_) + 1 < KS) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads));    \
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                        \
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);                                \
+      __builtin_amdgcn_s_barrier();                                          \
+      if ((KS_) + 2 < KS) issue((KS_) + 2, NA, NB_, NS, NX);                 \
+      compute((KS_), SA, SB, SS, SX);                                        \
     }
-    if (more) store_a(buf ^ 1);
-    __syncthreads();
-    if (more) {
+    for (int ks = 0; ks < KS; ks += 3) {
+      BEF_GEMM_STEP(ks, sA0, sB0, sS0, sX0, sA2, sB2, sS2, sX2)
+      if (ks + 1 >= KS) break;
+      BEF_GEMM_STEP(ks + 1, sA1, sB1, sS1, sX1, sA0, sB0, sS0, sX0)
+      if (ks + 2 >= KS) break;
+      BEF_GEMM_STEP(ks + 2, sA2, sB2, sS2, sX2, sA1, sB1, sS1, sX1)
+    }
+#undef BEF_GEMM_STEP
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+
+    if (GU) {
+      // ---- epilogue: h = silu(g) * u, per-row amax over the tile's 128
+      // columns of I, E4M3 codes and scale (the act_quant rule) ----
+      float hv[4][4][4];
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        bc[j] = bn[j];
-        fc[j] = fn[j];
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            hv[mi][jj][v] = silu_mul_accurate(acc[mi][jj][v], acc[mi][jj + 4][v]);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float m = 0.0f;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) m = fmaxf(m, fabsf(hv[mi][jj][v]));
+          m = group_max<16>(m);
+          const int R = wm * 64 + 16 * mi + 4 * q + v;
+          if ((lane & 15) == 0) s_amax[wn][R] = m;
+        }
+      __syncthreads();
+      uint8_t* s_out = sA0;
+      const int I128 = I >> 7;
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int R = wm * 64 + 16 * mi + 4 * q + v;
+          const float am = fmaxf(s_amax[0][R], s_amax[1][R]);
+          const float sc = am / 448.0f;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int col = 64 * wn + 16 * jj + (lane & 15);
+            s_out[R * 128 + col] = (uint8_t)((am != 0.0f) ? e4m3_1(hv[mi][jj][v] / sc) : 0u);
+          }
+          if (wn == 0 && (lane & 15) == 0 && R < nrows)
+            a.hs[(size_t)(row0 + R) * I128 + nb] = sc;
+        }
+      __syncthreads();
+      for (int t = tid; t < kTM * 8; t += kGThreads) {
+        const int R = t >> 3, c16 = t & 7;
+        if (R < nrows)
+          *reinterpret_cast<uint4*>(a.hq + (size_t)(row0 + R) * I + nb * 128 + 16 * c16) =
+              *reinterpret_cast<const uint4*>(&s_out[R * 128 + 16 * c16]);
       }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// gate + up + SwiGLU + requantisation of h.  BN = 128 columns of I for both
-// gate and up: wave w owns columns 32w..32w+31 of each, as sub-tiles
-// j = 0,1 (gate) and j = 2,3 (up) of the same columns, so h = silu(g)*u is
-// formed in registers.  A 128-column tile is exactly one quantisation block
-// of h, so the E4M3 requantisation (amax/448 per 128, as act_quant) finishes
-// inside the tile: per-row max across the 16 lanes of a column group, then
-// across the 4 waves through LDS.  grid = (I/128, m-tile slots).
-// ---------------------------------------------------------------------------
-template <int BM, int FMT>
-__global__ __launch_bounds__(256) void gemm_gate_up_kernel(
-    const uint8_t* __restrict__ gq, const void* __restrict__ gsv, const uint8_t* __restrict__ uq,
-    const void* __restrict__ usv, const uint8_t* __restrict__ xq, const float* __restrict__ xs,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_token, int E, int H,
-    int I, uint8_t* __restrict__ hq, float* __restrict__ hs) {
-  constexpr int MT = BM / 16, ACH = BM / 32, NJ = 4;
-  __shared__ int stmp[8];
-  __shared__ int s_tok[BM];
-  __shared__ __align__(16) uint8_t sA[2][BM * 128];
-  __shared__ __align__(16) float sXs[2][BM];
-  __shared__ float s_amax[4][BM];
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, kq = lane >> 4;
-  int mt;
-  const int g = find_group_item(
-      offsets, E + 1, blockIdx.y, [](int c) { return (c + BM - 1) / BM; }, stmp, &mt);
-  if (g < 0) return;
-  const int nb = blockIdx.x;
-  const int row0 = offsets[g] + mt * BM;
-  const int nrows = min(BM, offsets[g + 1] - row0);
-  for (int i = tid; i < BM; i += 256) s_tok[i] = row_token[row0 + (i < nrows ? i : 0)];
-  __syncthreads();
-
-  const int KS = H >> 7;
-  const uint8_t* a_row[ACH];
-  int a_dst[ACH];
-#pragma unroll
-  for (int j = 0; j < ACH; ++j) {
-    const int q = tid + 256 * j, row = q >> 3, c16 = q & 7;
-    a_row[j] = xq + (size_t)s_tok[row] * H + 16 * c16;
-    a_dst[j] = row * 128 + ((c16 ^ (row & 7)) << 4);
-  }
-  const float* xs_row = xs + (size_t)s_tok[tid < BM ? tid : 0] * KS;
-
-  const uint8_t* bsrc[NJ];
-  const uint8_t* bscale[NJ];
-  const float* wsc[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const uint8_t* mat = (j < 2) ? gq : uq;
-    const void* sc = (j < 2) ? gsv : usv;
-    const int n = nb * 128 + 32 * wv + 16 * (j & 1) + (lane & 15);
-    if constexpr (FMT == 1) {
-      bsrc[j] = mat + ((size_t)g * I + n) * (H >> 1) + 16 * kq;
-      bscale[j] = reinterpret_cast<const uint8_t*>(sc) + ((size_t)g * I + n) * (H >> 5) + kq;
-      wsc[j] = nullptr;
+      __syncthreads();
     } else {
-      bsrc[j] = mat + ((size_t)g * I + n) * H + 16 * kq;
-      bscale[j] = nullptr;
-      wsc[j] = reinterpret_cast<const float*>(sc) + ((size_t)g * (I >> 7) + nb) * KS;
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int R = wm * 64 + 16 * mi + 4 * q + v;
+          if (R < nrows) {
+            float* yp = a.y_rows + (size_t)(row0 + R) * H + nb * kTN + 128 * wn + (lane & 15);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) yp[16 * j] = acc[mi][j][v];
+          }
+        }
     }
-  }
-
-  v4f_t acc[MT][NJ];
-#pragma unroll
-  for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[mi][j] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
-  mfma_mainloop<BM, NJ, FMT>(a_row, a_dst, xs_row, bsrc, bscale, wsc, KS, sA, sXs, acc);
-
-  // epilogue: h, per-row amax over the 128 columns, E4M3 codes
-  float hv[MT][2][4];
-#pragma unroll
-  for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) hv[mi][jj][v] = silu_mul_accurate(acc[mi][jj][v], acc[mi][jj + 2][v]);
-#pragma unroll
-  for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float m = fmaxf(fabsf(hv[mi][0][v]), fabsf(hv[mi][1][v]));
-      m = group_max<16>(m);
-      if ((lane & 15) == 0) s_amax[wv][16 * mi + 4 * kq + v] = m;
-    }
-  __syncthreads();
-  uint8_t* s_out = sA[0];
-  const int I128 = I >> 7;
-#pragma unroll
-  for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = 16 * mi + 4 * kq + v;
-      const float am = fmaxf(fmaxf(s_amax[0][row], s_amax[1][row]), fmaxf(s_amax[2][row], s_amax[3][row]));
-      const float sc = am / 448.0f;
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int col = 32 * wv + 16 * jj + (lane & 15);
-        s_out[row * 128 + col] = (uint8_t)((am != 0.0f) ? e4m3_1(hv[mi][jj][v] / sc) : 0u);
-      }
-      if (wv == 0 && (lane & 15) == 0 && row < nrows) hs[(size_t)(row0 + row) * I128 + nb] = sc;
-    }
-  __syncthreads();
-  for (int q = tid; q < BM * 8; q += 256) {
-    const int row = q >> 3, c16 = q & 7;
-    if (row < nrows)
-      *reinterpret_cast<uint4*>(hq + (size_t)(row0 + row) * I + nb * 128 + 16 * c16) =
-          *reinterpret_cast<const uint4*>(&s_out[row * 128 + 16 * c16]);
   }
 }
 
-// ---------------------------------------------------------------------------
-// down: y_rows[r] = W_down[g] . deq(hq[r]).  Rows of a group are contiguous
-// in hq (no gather).  BN columns of H per block, wave w owning BN/4 of them
-// as NJ = BN/64 sub-tiles.  grid = (H/BN, m-tile slots).
-// ---------------------------------------------------------------------------
-template <int BM, int BN, int FMT>
-__global__ __launch_bounds__(256) void gemm_down_kernel(
-    const uint8_t* __restrict__ dq, const void* __restrict__ dsv, const uint8_t* __restrict__ hq,
-    const float* __restrict__ hs, const int32_t* __restrict__ offsets, int E, int H, int I,
-    float* __restrict__ y_rows) {
-  constexpr int MT = BM / 16, ACH = BM / 32, NJ = BN / 64;
-  __shared__ int stmp[8];
-  __shared__ __align__(16) uint8_t sA[2][BM * 128];
-  __shared__ __align__(16) float sXs[2][BM];
+// Blocks of the persistent grid: one per CU, a multiple of 8 (the XCDs).
+static int g_cu_count[64];
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, kq = lane >> 4;
-  int mt;
-  const int g = find_group_item(
-      offsets, E + 1, blockIdx.y, [](int c) { return (c + BM - 1) / BM; }, stmp, &mt);
-  if (g < 0) return;
-  const int nb = blockIdx.x;
-  const int row0 = offsets[g] + mt * BM;
-  const int nrows = min(BM, offsets[g + 1] - row0);
-  const int KS = I >> 7;
-
-  const uint8_t* a_row[ACH];
-  int a_dst[ACH];
-#pragma unroll
-  for (int j = 0; j < ACH; ++j) {
-    const int q = tid + 256 * j, row = q >> 3, c16 = q & 7;
-    a_row[j] = hq + (size_t)(row0 + (row < nrows ? row : 0)) * I + 16 * c16;
-    a_dst[j] = row * 128 + ((c16 ^ (row & 7)) << 4);
+static int grid_blocks() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
   }
-  const int xr = (tid < BM && tid < nrows) ? tid : 0;
-  const float* xs_row = hs + (size_t)(row0 + xr) * KS;
-
-  const uint8_t* bsrc[NJ];
-  const uint8_t* bscale[NJ];
-  const float* wsc[NJ];
-  int cols[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int c = nb * BN + (BN / 4) * wv + 16 * j + (lane & 15);
-    cols[j] = c;
-    if constexpr (FMT == 1) {
-      bsrc[j] = dq + ((size_t)g * H + c) * (I >> 1) + 16 * kq;
-      bscale[j] = reinterpret_cast<const uint8_t*>(dsv) + ((size_t)g * H + c) * (I >> 5) + kq;
-      wsc[j] = nullptr;
-    } else {
-      bsrc[j] = dq + ((size_t)g * H + c) * I + 16 * kq;
-      bscale[j] = nullptr;
-      wsc[j] = reinterpret_cast<const float*>(dsv) + ((size_t)g * (H >> 7) + (c >> 7)) * KS;
+  if (g_cu_count[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      n = 256;
     }
+    g_cu_count[dev] = n >= 8 ? (n & ~7) : 8;
   }
-  v4f_t acc[MT][NJ];
-#pragma unroll
-  for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[mi][j] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
-  mfma_mainloop<BM, NJ, FMT>(a_row, a_dst, xs_row, bsrc, bscale, wsc, KS, sA, sXs, acc);
-
-#pragma unroll
-  for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = 16 * mi + 4 * kq + v;
-      if (row < nrows) {
-        float* yp = y_rows + (size_t)(row0 + row) * H;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) yp[cols[j]] = acc[mi][j][v];
-      }
-    }
+  return g_cu_count[dev];
 }
 
-int gemm_mtile_slots(int T, int k, int E, int BM) {
-  const long long routed = (long long)T * k;
-  const long long partial = routed < E ? routed : E;
-  return (int)(routed / BM + partial + (T + BM - 1) / BM + 1);
-}
-
-template <int BM, int FMT>
-static hipError_t launch_gu(const GemmArgs& a, hipStream_t st) {
-  const dim3 grid(a.I / 128, gemm_mtile_slots(a.T, a.k, a.E, BM));
-  gemm_gate_up_kernel<BM, FMT><<<grid, 256, 0, st>>>(a.gq, a.gs, a.uq, a.us, a.xq, a.xs,
-                                                     a.offsets, a.row_token, a.E, a.H, a.I, a.hq,
-                                                     a.hs);
-  return hipGetLastError();
-}
-
-template <int BM, int BN, int FMT>
-static hipError_t launch_dn(const GemmArgs& a, hipStream_t st) {
-  const dim3 grid(a.H / BN, gemm_mtile_slots(a.T, a.k, a.E, BM));
-  gemm_down_kernel<BM, BN, FMT><<<grid, 256, 0, st>>>(a.dq, a.ds, a.hq, a.hs, a.offsets, a.E,
-                                                      a.H, a.I, a.y_rows);
+template <int FMT, bool GU>
+static hipError_t launch_g(const GemmArgs& a, hipStream_t st) {
+  if (a.E + 1 > 257 || (GU ? (a.I % 128) : (a.H % kTN)) != 0) return hipErrorInvalidValue;
+  gemm_kernel<FMT, GU><<<dim3(grid_blocks()), dim3(kGThreads), 0, st>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_gate_up(const GemmArgs& a, hipStream_t st) {
-  if (a.fmt == 1) return launch_gu<kGemmBM, 1>(a, st);
-  return launch_gu<kGemmBM, 2>(a, st);
+  if (a.fmt == 1) return launch_g<1, true>(a, st);
+  return launch_g<2, true>(a, st);
 }
 
 hipError_t launch_gemm_down(const GemmArgs& a, hipStream_t st) {
-  if (a.H % 256 == 0) {
-    if (a.fmt == 1) return launch_dn<kGemmBM, 256, 1>(a, st);
-    return launch_dn<kGemmBM, 256, 2>(a, st);
-  }
-  if (a.fmt == 1) return launch_dn<kGemmBM, 128, 1>(a, st);
-  return launch_dn<kGemmBM, 128, 2>(a, st);
+  if (a.fmt == 1) return launch_g<1, false>(a, st);
+  return launch_g<2, false>(a, st);
 }
 
 }  // namespace bef

@@ -10,7 +10,6 @@ constexpr int kRouteMaxGroups = 32;       // router: 256-row groups, H <= 8192
 constexpr int kPermuteSmallPairs = 2048;  // permute: single block up to this many pairs
 constexpr int kPermuteTokBlock = 256;     // permute: tokens per block above that
 constexpr int kGemvMaxRows = 8;           // VALU GEMV path: rows (k + 1) per token
-constexpr int kGemmBM = 128;              // MFMA grouped GEMM: tokens per tile
 constexpr uint32_t MOE_STATUS_BAD_EXPERT_ID_DEV = 1u;
 
 struct GemvArgs {
@@ -89,6 +88,5 @@ hipError_t launch_gemv_down(const GemvArgs& a, bool combine, hipStream_t st);
 hipError_t launch_gemm_gate_up(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_down(const GemmArgs& a, hipStream_t st);
 hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t st);
-int gemm_mtile_slots(int T, int k, int E, int BM);
 
 }  // namespace bef
