@@ -3,6 +3,9 @@
 All HIP sources are compiled for gfx950 only, with IEEE fp32 division and
 square root (the hipcc default, stated explicitly) and without fast-math or
 denormal flushing, and with packed-fp32 instruction selection turned off.
+MFMA results are kept in ordinary VGPRs (-amdgpu-mfma-vgpr-form): the
+grouped GEMM folds every MFMA result into its accumulators with VALU FMAs,
+which cannot read AGPRs.
 """
 from __future__ import annotations
 
@@ -23,6 +26,7 @@ FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
     "-ffp-contract=fast",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]

@@ -53,7 +53,7 @@ typedef __attribute__((address_space(1))) void* glb_ptr_t;
 
 constexpr int kTM = 128;      // tokens per tile
 constexpr int kTN = 256;      // output columns per tile
-constexpr int kGThreads = 256;
+constexpr int kGThreads = 512;
 
 // s_waitcnt immediates (gfx9: vmcnt [3:0] + [15:14], expcnt [6:4], lgkmcnt [11:8])
 constexpr int waitcnt_vm(int n) { return 0xF70 | (n & 0xF) | ((n >> 4) << 14); }
@@ -85,8 +85,9 @@ struct StageBytes {
 template <int FMT, bool GU>
 __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
   constexpr int KB = StageBytes<FMT>::kB;
-  constexpr int NBI = FMT == 1 ? 4 : 8;  // B DMA instructions per wave per K step
-  constexpr int kLoads = 4 + NBI + (FMT == 1 ? 2 : 1);  // DMA instructions per wave per stage
+  constexpr int NAI = 2;                 // A DMA instructions per wave per K step
+  constexpr int NBI = FMT == 1 ? 2 : 4;  // B DMA instructions per wave per K step
+  constexpr int kLoads = NAI + NBI + (FMT == 1 ? 2 : 1);  // DMA instructions per wave per stage
   __shared__ __align__(16) uint8_t sA0[kTM * 128];
   __shared__ __align__(16) uint8_t sA1[kTM * 128];
   __shared__ __align__(16) uint8_t sA2[kTM * 128];
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
   __shared__ __align__(16) float sX0[kTM];  // activation scales of the K step
   __shared__ __align__(16) float sX1[kTM];
   __shared__ __align__(16) float sX2[kTM];
-  __shared__ float s_amax[2][kTM];
+  __shared__ float s_amax[4][kTM];
   __shared__ float s_wsc[2][64];  // FP8 weight block scales of the tile, per K step
   __shared__ int s_mtp[258];  // m-tile prefix per group
   __shared__ int s_tok[kTM];
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w & 1, wn = w >> 1, q = lane >> 4;
+  const int wm = w & 1, wn = w >> 1, q = lane >> 4;  // 2 (M) x 4 (N) waves of 64 x 64
   const int E = a.E, H = a.H, I = a.I;
   const int K = GU ? H : I;  // contraction length
   const int KS = K >> 7;
@@ -115,22 +116,18 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
 
   // m-tiles per group and their exclusive prefix (groups 0..E, E = shared)
   {
-    int my_mt[2] = {0, 0}, inc[2];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int gg = tid + kGThreads * h2;
-      if (gg <= E) {
-        const int c = a.offsets[gg + 1] - a.offsets[gg];
-        my_mt[h2] = (c + kTM - 1) / kTM;
-      }
-      inc[h2] = my_mt[h2];
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_up(inc[h2], d, kWave);
-        if (lane >= d) inc[h2] += t;
-      }
+    int my_mt = 0;
+    if (tid <= E) {
+      const int c = a.offsets[tid + 1] - a.offsets[tid];
+      my_mt = (c + kTM - 1) / kTM;
     }
-    if (lane == 63) stmp[w] = inc[0];
+    int inc = my_mt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(inc, d, kWave);
+      if (lane >= d) inc += t;
+    }
+    if (lane == 63) stmp[w] = inc;
     __syncthreads();
     int base = 0, total = 0;
 #pragma unroll
@@ -138,15 +135,8 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
       base += (i < w) ? stmp[i] : 0;
       total += stmp[i];
     }
-    if (tid <= E) s_mtp[tid] = base + inc[0] - my_mt[0];
-    __syncthreads();
-    // groups 256.. (only group 256 exists: E <= 256) follow in wave 0
-    if (w == 0 && kGThreads + lane <= E) s_mtp[kGThreads + lane] = total + inc[1] - my_mt[1];
-    if (tid == 0) {
-      int t2 = total;
-      for (int gg = kGThreads; gg <= E; ++gg) t2 += (a.offsets[gg + 1] - a.offsets[gg] + kTM - 1) / kTM;
-      s_mtp[E + 1] = t2;
-    }
+    if (tid <= E) s_mtp[tid] = base + inc - my_mt;
+    if (tid == 0) s_mtp[E + 1] = total;
     __syncthreads();
   }
   const int total_mt = s_mtp[E + 1];
@@ -171,41 +161,47 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
       __syncthreads();
     }
 
-    // ---- per-lane DMA sources of this tile (K offset 0) ----
-    const uint8_t* srcA[4];
+    // ---- DMA sources of this tile (K offset 0): a wave-uniform 64-bit base
+    // (scalar registers) and a 32-bit per-lane offset ----
+    const uint8_t* baseA = GU ? a.xq : a.hq + (size_t)row0 * I;
+    uint32_t offA[NAI];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = (w * 4 + i) * 64 + lane, r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
+    for (int i = 0; i < NAI; ++i) {
+      const int p = (w * NAI + i) * 64 + lane, r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
       const int rr = min(r, nrows - 1);
-      srcA[i] = (GU ? a.xq + (size_t)s_tok[rr] * H : a.hq + (size_t)(row0 + rr) * I) + 16 * c;
+      offA[i] = (GU ? (uint32_t)s_tok[rr] * (uint32_t)H : (uint32_t)rr * (uint32_t)I) + 16u * c;
     }
-    const size_t brow_bytes = FMT == 1 ? (size_t)(K >> 1) : (size_t)K;
-    auto brow = [&](int r) -> size_t {  // weight row of B row r of the tile
-      if (GU) return (size_t)g * I + (size_t)nb * 128 + (r & 127);
-      return (size_t)g * H + (size_t)nb * kTN + r;
-    };
-    const uint8_t* bmat_g = GU ? a.gq : a.dq;
-    const uint8_t* bmat_u = GU ? a.uq : a.dq;
-    const uint8_t* srcB[NBI];
+    const uint32_t brow_bytes = FMT == 1 ? (uint32_t)(K >> 1) : (uint32_t)K;
+    // B row r of the tile: gate rows 0..127 and up rows 128..255 of I-block
+    // nb (gate+up), or rows nb*256 + r of W_down (down)
+    const size_t rows_per_expert = GU ? (size_t)I : (size_t)H;
+    const uint8_t* baseG = (GU ? a.gq : a.dq) + (size_t)g * rows_per_expert * brow_bytes;
+    const uint8_t* baseU = (GU ? a.uq : a.dq) + (size_t)g * rows_per_expert * brow_bytes;
+    const uint32_t row_base = GU ? (uint32_t)nb * 128u : (uint32_t)nb * kTN;
+    uint32_t offB[NBI];
 #pragma unroll
     for (int i = 0; i < NBI; ++i) {
       const int p = (w * NBI + i) * 64 + lane;
       const int r = FMT == 1 ? (p >> 2) : (p >> 3);
       const int c = FMT == 1 ? ((p & 3) ^ ((r >> 2) & 3)) : ((p & 7) ^ ((r >> 1) & 7));
-      const uint8_t* m = (GU && r >= 128) ? bmat_u : bmat_g;
-      srcB[i] = m + brow(r) * brow_bytes + 16 * c;
+      offB[i] = (row_base + (uint32_t)(GU ? (r & 127) : r)) * brow_bytes + 16u * c;
     }
-    const uint8_t* srcS = nullptr;  // FP4 scales: B row w*64 + lane
+    // FP4 scales: B row w*32 + lane (lanes < 32; uniform matrix per wave)
+    const uint32_t sbytes = (uint32_t)(K >> 5);
+    const uint8_t* baseS = nullptr;
+    uint32_t offS = 0;
     if (FMT == 1) {
-      const int r = w * 64 + lane;
-      const uint8_t* sm = (GU && r >= 128) ? (const uint8_t*)a.us
-                                           : (const uint8_t*)(GU ? a.gs : a.ds);
-      srcS = sm + brow(r) * (size_t)(K >> 5);
+      const uint8_t* sm = (GU && w >= 4) ? (const uint8_t*)a.us : (const uint8_t*)(GU ? a.gs : a.ds);
+      baseS = sm + (size_t)g * rows_per_expert * sbytes;
+      const int r = w * 32 + (lane & 31);
+      offS = (row_base + (uint32_t)(GU ? (r & 127) : r)) * sbytes;
     }
-    const float* srcX;  // activation scales: A row w*32 + lane (lanes < 32)
+    // activation scales: A row w*16 + lane (lanes < 16)
+    const float* baseX = GU ? a.xs : a.hs + (size_t)row0 * KS;
+    uint32_t offX;
     {
-      const int rr = min(w * 32 + (lane & 31), nrows - 1);
-      srcX = GU ? a.xs + (size_t)s_tok[rr] * KS : a.hs + (size_t)(row0 + rr) * KS;
+      const int rr = min(w * 16 + (lane & 15), nrows - 1);
+      offX = (GU ? (uint32_t)s_tok[rr] : (uint32_t)rr) * (uint32_t)KS;
     }
     // FP8 weight block scales of the tile into LDS, once: [0] gate (GU) or
     // columns 0..127 (down), [1] up (GU) or columns 128..255 (down)
@@ -221,19 +217,22 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
 
     auto issue = [&](int ks, uint8_t* sA, uint8_t* sB, uint32_t* sS, float* sX) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma16(srcA[i] + ks * 128, sA + (w * 4 + i) * 1024);
+      for (int i = 0; i < NAI; ++i) dma16(baseA + (offA[i] + (uint32_t)ks * 128u), sA + (w * NAI + i) * 1024);
 #pragma unroll
-      for (int i = 0; i < NBI; ++i)
-        dma16(srcB[i] + ks * (FMT == 1 ? 64 : 128), sB + (w * NBI + i) * 1024);
-      if (FMT == 1) dma4(srcS + ks * 4, sS + w * 64);
-      if (lane < 32) dma4(srcX + ks, sX + w * 32);
+      for (int i = 0; i < NBI; ++i) {
+        // B rows >= 128 of a gate+up tile are up rows: uniform per instruction
+        const uint8_t* bb = (GU && (w * NBI + i) * 64 >= 128 * (FMT == 1 ? 4 : 8)) ? baseU : baseG;
+        dma16(bb + (offB[i] + (uint32_t)ks * (FMT == 1 ? 64u : 128u)), sB + (w * NBI + i) * 1024);
+      }
+      if (FMT == 1 && lane < 32) dma4(baseS + (offS + (uint32_t)ks * 4u), sS + w * 32);
+      if (lane < 16) dma4(baseX + (offX + (uint32_t)ks), sX + w * 16);
     };
 
-    v4f_t acc[4][8];
+    v4f_t acc[4][4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[mi][j] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
+      for (int j = 0; j < 4; ++j) acc[mi][j] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
     // a wave whose 64 rows hold no token skips the multiplies (the rows of a
     // partly filled 64-row band are multiplied anyway: clamped copies of a
     // real row, never stored)
@@ -243,7 +242,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
                        const float* sX) {
       if (!live) return;
       v8i_t av[4];
-      float4 xv[4];
+      float4 xv[4], xs_raw[4];
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
         const int r = wm * 64 + 16 * mi + (lane & 15);
@@ -251,18 +250,30 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
         const uint4 a1 = *reinterpret_cast<const uint4*>(sA + sw128(r, q + 4));
         av[mi] = (v8i_t){(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
                          (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        xv[mi] = *reinterpret_cast<const float4*>(sX + wm * 64 + 16 * mi + 4 * q);
+        xs_raw[mi] = *reinterpret_cast<const float4*>(sX + wm * 64 + 16 * mi + 4 * q);
       }
-      float f0 = 1.0f, f1 = 1.0f;
+      // activation scales times the FP8 weight block scale (gate half first)
+      float f1 = 1.0f;
       if (FMT == 2) {
-        f0 = s_wsc[GU ? 0 : wn][ks];
+        const float f0 = s_wsc[GU ? 0 : (wn >> 1)][ks];
         f1 = GU ? s_wsc[1][ks] : f0;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+          xv[mi].x = xs_raw[mi].x * f0, xv[mi].y = xs_raw[mi].y * f0;
+          xv[mi].z = xs_raw[mi].z * f0, xv[mi].w = xs_raw[mi].w * f0;
+        }
+      } else {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) xv[mi] = xs_raw[mi];
       }
       const v4f_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int n = GU ? ((j < 4 ? 0 : 128) + 64 * wn + 16 * (j & 3) + (lane & 15))
-                         : (128 * wn + 16 * j + (lane & 15));
+      for (int j = 0; j < 4; ++j) {
+        // sub-tile j: gate+up -- j < 2 gate, j >= 2 up, I-columns
+        // 32 wn + 16 (j & 1) + (lane & 15) of the block; down -- H-columns
+        // 64 wn + 16 j + (lane & 15)
+        const int n = GU ? ((j < 2 ? 0 : 128) + 32 * wn + 16 * (j & 1) + (lane & 15))
+                         : (64 * wn + 16 * j + (lane & 15));
         v8i_t bv;
         int sb = 127;
         if (FMT == 1) {
@@ -275,15 +286,25 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
           bv = (v8i_t){(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
                        (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
         }
-        const float f = (GU && j >= 4) ? f1 : f0;
+        if (FMT == 2 && GU && j == 2) {
+          // up half: activation scales times the up block scale
+#pragma unroll
+          for (int mi = 0; mi < 4; ++mi) {
+            xv[mi].x = xs_raw[mi].x * f1, xv[mi].y = xs_raw[mi].y * f1;
+            xv[mi].z = xs_raw[mi].z * f1, xv[mi].w = xs_raw[mi].w * f1;
+          }
+        }
+        v4f_t d[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+          d[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[mi], bv, zero, 0,
+                                                                   FMT == 1 ? 4 : 0, 0, 127, 0, sb);
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
-          const v4f_t d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              av[mi], bv, zero, 0, FMT == 1 ? 4 : 0, 0, 127, 0, sb);
-          acc[mi][j][0] = fmaf(xv[mi].x * f, d[0], acc[mi][j][0]);
-          acc[mi][j][1] = fmaf(xv[mi].y * f, d[1], acc[mi][j][1]);
-          acc[mi][j][2] = fmaf(xv[mi].z * f, d[2], acc[mi][j][2]);
-          acc[mi][j][3] = fmaf(xv[mi].w * f, d[3], acc[mi][j][3]);
+          acc[mi][j][0] = fmaf(xv[mi].x, d[mi][0], acc[mi][j][0]);
+          acc[mi][j][1] = fmaf(xv[mi].y, d[mi][1], acc[mi][j][1]);
+          acc[mi][j][2] = fmaf(xv[mi].z, d[mi][2], acc[mi][j][2]);
+          acc[mi][j][3] = fmaf(xv[mi].w, d[mi][3], acc[mi][j][3]);
         }
       }
     };
@@ -317,21 +338,19 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
     if (GU) {
       // ---- epilogue: h = silu(g) * u, per-row amax over the tile's 128
       // columns of I, E4M3 codes and scale (the act_quant rule) ----
-      float hv[4][4][4];
+      float hv[4][2][4];
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            hv[mi][jj][v] = silu_mul_accurate(acc[mi][jj][v], acc[mi][jj + 4][v]);
+            hv[mi][jj][v] = silu_mul_accurate(acc[mi][jj][v], acc[mi][jj + 2][v]);
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          float m = 0.0f;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) m = fmaxf(m, fabsf(hv[mi][jj][v]));
+          float m = fmaxf(fabsf(hv[mi][0][v]), fabsf(hv[mi][1][v]));
           m = group_max<16>(m);
           const int R = wm * 64 + 16 * mi + 4 * q + v;
           if ((lane & 15) == 0) s_amax[wn][R] = m;
@@ -344,11 +363,11 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int R = wm * 64 + 16 * mi + 4 * q + v;
-          const float am = fmaxf(s_amax[0][R], s_amax[1][R]);
+          const float am = fmaxf(fmaxf(s_amax[0][R], s_amax[1][R]), fmaxf(s_amax[2][R], s_amax[3][R]));
           const float sc = am / 448.0f;
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int col = 64 * wn + 16 * jj + (lane & 15);
+          for (int jj = 0; jj < 2; ++jj) {
+            const int col = 32 * wn + 16 * jj + (lane & 15);
             s_out[R * 128 + col] = (uint8_t)((am != 0.0f) ? e4m3_1(hv[mi][jj][v] / sc) : 0u);
           }
           if (wn == 0 && (lane & 15) == 0 && R < nrows)
@@ -369,9 +388,9 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
         for (int v = 0; v < 4; ++v) {
           const int R = wm * 64 + 16 * mi + 4 * q + v;
           if (R < nrows) {
-            float* yp = a.y_rows + (size_t)(row0 + R) * H + nb * kTN + 128 * wn + (lane & 15);
+            float* yp = a.y_rows + (size_t)(row0 + R) * H + nb * kTN + 64 * wn + (lane & 15);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) yp[16 * j] = acc[mi][j][v];
+            for (int j = 0; j < 4; ++j) yp[16 * j] = acc[mi][j][v];
           }
         }
     }
