@@ -42,7 +42,14 @@ METRIC = ("MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA TFLOPS (prefil
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, published (FP8 x FP4 runs at this rate)
 PROFILES = os.path.join(ROOT, "profiles")
-DOMINANT = {"gemv": "gemv_gate_up_fp4_kernel", "gemm": "gemm_gate_up_kernel"}
+DOMINANT = {"gemv": "gemv_gate_up_fp4_kernel", "gemm": "gemm_kernel_gate_up"}
+
+
+def is_dominant(kernel_name, path):
+    """Does a profiler kernel name belong to the path's dominant kernel?"""
+    if path == "gemv":
+        return "gemv_gate_up_fp4_kernel" in kernel_name
+    return "gemm_kernel<" in kernel_name and "true>" in kernel_name
 
 
 # --------------------------------------------------------------------------
@@ -59,16 +66,20 @@ def expert_bytes(wl):
     return 3 * mat, 2 * mat
 
 
-def work(wl, ids):
-    """Algorithmic bytes / flops of a step and of the dominant kernel."""
+def work(wl, ids, path):
+    """Algorithmic bytes / flops of a step and of the dominant kernel (the
+    gate+up kernel; on the one-token VALU path it streams the routed experts
+    only -- the shared expert's gate+up runs in the front kernel)."""
     T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
-    touched = len(set(ids.ravel().tolist())) + 1          # + shared expert
+    routed = len(set(ids.ravel().tolist()))
+    touched = routed + 1                                  # + shared expert
     per_exp, per_exp_gu = expert_bytes(wl)
     R = T * k + T
     step_bytes = touched * per_exp + H * E * 2 + T * H * 2 + T * H * 2
     step_flops = 2 * 3 * H * I * R + 2 * T * H * E
-    gu_bytes = touched * per_exp_gu + T * H + T * (H // 128) * 4
-    gu_flops = 2 * 2 * H * I * R
+    gu_exp, gu_rows = (routed, T * k) if path == "gemv" else (touched, R)
+    gu_bytes = gu_exp * per_exp_gu + T * H + T * (H // 128) * 4
+    gu_flops = 2 * 2 * H * I * gu_rows
     return dict(touched=touched, step_bytes=step_bytes, step_flops=step_flops,
                 gu_bytes=gu_bytes, gu_flops=gu_flops, rows=R)
 
@@ -207,26 +218,9 @@ class Bench:
         moe.dsv4_moe_forward(w, self.wr, x, T, k, self.inj_ids, self.inj_w, self.out,
                              moe.MOE_DT_BF16, self.ws, self.ws_bytes, self.sp)
 
-    def step(self, i, ev=None):
-        """Enqueue step i stage by stage (ev: event pair recorded around S5)."""
-        moe, wl = self.moe, self.wl
-        T, H, E, k = self.T, wl.H, wl.E, wl.k
-        w = self.w[i % len(self.w)]
-        x = self.x_of(i)
-        sp = self.sp
-        moe.moe_route(x, self.wr, T, H, E, k, self.ids, self.tw, self.ws, self.ws_bytes, sp)
-        ids, tw = (self.ids, self.tw) if self.inj_ids is None else (self.inj_ids, self.inj_w)
-        moe.act_quant_fp8(x, moe.MOE_DT_BF16, T, H, self.xq, self.xs, sp)
-        moe.moe_permute(ids, T, k, E, self.offsets, self.row_token, self.row_of, self.ws,
-                        self.ws_bytes, sp)
-        if ev is not None:
-            self.hip.ok(self.hip.L.hipEventRecord(ev[0], sp), "hipEventRecord")
-        moe.moe_expert_gate_up(w, self.xq, self.xs, T, k, self.offsets, self.row_token, self.ws,
-                               self.ws_bytes, sp)
-        if ev is not None:
-            self.hip.ok(self.hip.L.hipEventRecord(ev[1], sp), "hipEventRecord")
-        moe.moe_expert_down(w, T, k, self.offsets, self.row_of, tw, self.y, self.out,
-                            moe.MOE_DT_BF16, self.ws, self.ws_bytes, sp)
+
+def moe_kernel_id(moe, path):
+    return moe.MOE_KERNEL_GEMV_GATE_UP if path == "gemv" else moe.MOE_KERNEL_GEMM_GATE_UP
 
 
 def run(args):
@@ -243,7 +237,6 @@ def run(args):
     # eager warm-up (also caches the library's one-time device check)
     for i in range(max(2, min(args.warmup, 16))):
         B.product_step(i)
-        B.step(i)
     torch.cuda.synchronize()
     # graph of `per_graph` product steps
     g1, ex1 = B.hip.capture(B.sp, lambda: [B.product_step(i) for i in range(per_graph)])
@@ -260,18 +253,17 @@ def run(args):
         B.hip.ok(L.hipGraphLaunch(ex1, B.sp), "hipGraphLaunch")
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    # dominant-kernel timing: eager steps with HIP events around S5, enqueued
-    # on the same stream behind a backlog of graph replays (>= 40 ms of GPU
-    # work) so that the GPU runs them back to back and no host gap falls
-    # between an event and its kernel.
-    graph_s = elapsed / reps
-    backlog = max(2, math.ceil(0.04 / graph_s))
+    # dominant-kernel timing: the same product steps, run eagerly, with the
+    # gate+up kernel's launches recording a pair of HIP events at that
+    # kernel's own begin and end (the library's debug timing hook puts them
+    # in the kernel's dispatch: no queueing gap is counted)
     n_ev = max(1, min(256, steps))
     evs = [(B.hip.event(), B.hip.event()) for _ in range(n_ev)]
-    for _ in range(backlog):
-        B.hip.ok(L.hipGraphLaunch(ex1, B.sp), "hipGraphLaunch")
+    which = moe_kernel_id(B.moe, B.path)
     for i in range(n_ev):
-        B.step(i, evs[i])
+        B.moe.moe_debug_time_kernel(which, evs[i][0], evs[i][1])
+        B.product_step(i)
+    B.moe.moe_debug_time_kernel(which, None, None)
     torch.cuda.synchronize()
     gu_ms = [B.hip.elapsed_ms(a, b) for a, b in evs]
     L.hipGraphExecDestroy(ex1)
@@ -286,7 +278,7 @@ def run(args):
             B.moe.moe_route(x, B.wr, B.T, wl.H, wl.E, wl.k, B.ids, B.tw, B.ws, B.ws_bytes, B.sp)
             torch.cuda.synchronize()
             ids_steps.append(B.ids.cpu().numpy().copy())
-    works = [work(wl, ids) for ids in ids_steps]
+    works = [work(wl, ids, B.path) for ids in ids_steps]
     avg = {key: float(np.mean([w[key] for w in works])) for key in works[0]}
     ms_per_step = elapsed * 1e3 / steps
     value = B.T * steps / elapsed
@@ -404,8 +396,9 @@ def summarize(args):
             continue
         name = r["Kernel_Name"]
         per.setdefault(name, []).append(float(r["Counter_Value"]))
-    kern = DOMINANT["gemv" if args.workload == "decode_t1" else "gemm"]
-    kv = [v for n, vs in per.items() if kern in n for v in vs]
+    path = "gemv" if args.workload == "decode_t1" else "gemm"
+    kern = DOMINANT[path]
+    kv = [v for n, vs in per.items() if is_dominant(n, path) for v in vs]
     # calibration: the plain float32 add of --calib-mib MiB that bench.py runs
     # last (reads and writes calib_mib MiB each)
     cv = [v for n, vs in per.items() if "FunctorOnSelf_add<float>" in n for v in vs]

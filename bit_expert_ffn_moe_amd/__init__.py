@@ -21,6 +21,7 @@ MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EALIGN, MOE_EWORKSPACE, MOE_ELAUNCH = 0, -1
 MOE_W_FP4_E2M1_UE8M0_K32, MOE_W_FP8_E4M3_F32_B128 = 1, 2
 MOE_DT_BF16, MOE_DT_F32 = 1, 2
 MOE_STATUS_BAD_EXPERT_ID, MOE_STATUS_SYNC_TIMEOUT = 1, 2
+MOE_KERNEL_GEMV_GATE_UP, MOE_KERNEL_GEMM_GATE_UP = 1, 2
 
 if not os.path.exists(_SO):
     raise ImportError(
@@ -69,6 +70,7 @@ _sigs = {
                           ctypes.c_int),
     "moe_debug_intermediates": ([_W, _i32, _i32, _vp, _sz, ctypes.POINTER(_vp),
                                  ctypes.POINTER(_vp), ctypes.POINTER(_vp)], ctypes.c_int),
+    "moe_debug_time_kernel": ([_i32, _vp, _vp], ctypes.c_int),
 }
 for _name, (_args, _res) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -177,6 +179,12 @@ def moe_device_status(ws, stream=None, clear: bool = False) -> int:
     _check(_lib.moe_device_status(_ptr(ws), _stream(stream), ctypes.byref(st), int(clear)),
            "moe_device_status")
     return st.value
+
+
+def moe_debug_time_kernel(which, start_event, stop_event) -> int:
+    """Time kernel `which` with two hipEvent_t handles (None, None clears)."""
+    return _check(_lib.moe_debug_time_kernel(which, start_event, stop_event),
+                  "moe_debug_time_kernel")
 
 
 def moe_debug_intermediates(w, T, k, ws, ws_bytes):

@@ -43,6 +43,8 @@
 // an M-tile share its activation rows in the XCD's L2, and the M-tiles of
 // one expert (16 items apart for I = 2048) read the same weight rows at the
 // same time, so those stream from HBM about once.
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -420,7 +422,12 @@ static int grid_blocks() {
 template <int FMT, bool GU>
 static hipError_t launch_g(const GemmArgs& a, hipStream_t st) {
   if (a.E + 1 > 257 || (GU ? (a.I % 128) : (a.H % kTN)) != 0) return hipErrorInvalidValue;
-  gemm_kernel<FMT, GU><<<dim3(grid_blocks()), dim3(kGThreads), 0, st>>>(a);
+  const KernelTimer& tm = g_kernel_timer[MOE_KERNEL_GEMM_GATE_UP];
+  if (GU && tm.start)
+    hipExtLaunchKernelGGL(gemm_kernel<FMT, GU>, dim3(grid_blocks()), dim3(kGThreads), 0, st,
+                          tm.start, tm.stop, 0, a);
+  else
+    gemm_kernel<FMT, GU><<<dim3(grid_blocks()), dim3(kGThreads), 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -14,6 +14,8 @@
 // touches, so each 16-byte load of a weight row is exactly one UE8M0 scale
 // block, and a wave reads a 1 KiB contiguous stretch per load instruction
 // (gemv_body.h).
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "gemv_body.h"
 #include "kernels.h"
@@ -177,9 +179,14 @@ static hipError_t launch_gate_up_nb(const GemvArgs& a, hipStream_t st) {
   if (a.I % 128 != 0 || a.I > kHSlotStride) return hipErrorInvalidValue;
   const GUWeights w = {a.gq, a.gs, a.uq, a.us, a.E, a.H, a.I};
   const dim3 grid((a.I / (4 * RUN)) * a.n_slots);
-  gemv_gate_up_fp4_kernel<NB><<<grid, 256, 0, st>>>(
-      w, a.xq, a.xs, a.offsets, a.row_token, a.active,
-      HExchange{a.hq_arrive, a.h_slots, a.h, a.hq_ws, a.hs_ws, a.status});
+  const HExchange hx = {a.hq_arrive, a.h_slots, a.h, a.hq_ws, a.hs_ws, a.status};
+  const KernelTimer& tm = g_kernel_timer[MOE_KERNEL_GEMV_GATE_UP];
+  if (tm.start)
+    hipExtLaunchKernelGGL(gemv_gate_up_fp4_kernel<NB>, grid, dim3(256), 0, st, tm.start, tm.stop,
+                          0, w, a.xq, a.xs, a.offsets, a.row_token, a.active, hx);
+  else
+    gemv_gate_up_fp4_kernel<NB><<<grid, 256, 0, st>>>(w, a.xq, a.xs, a.offsets, a.row_token,
+                                                      a.active, hx);
   return hipGetLastError();
 }
 

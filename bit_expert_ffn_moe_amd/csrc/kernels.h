@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moe.h"
+
 namespace bef {
 
 constexpr int kRouteSmallT = 4;           // router: per-chunk blocks + last-block top-k
@@ -11,6 +13,13 @@ constexpr int kPermuteSmallPairs = 2048;  // permute: single block up to this ma
 constexpr int kPermuteTokBlock = 256;     // permute: tokens per block above that
 constexpr int kGemvMaxRows = 8;           // VALU GEMV path: rows (k + 1) per token
 constexpr uint32_t MOE_STATUS_BAD_EXPERT_ID_DEV = 1u;
+
+// Optional start/stop events of one kernel's launches (debug timing; set by
+// moe_debug_time_kernel, index MOE_KERNEL_*).
+struct KernelTimer {
+  hipEvent_t start, stop;
+};
+extern KernelTimer g_kernel_timer[3];
 
 struct GemvArgs {
   const uint8_t *gq, *gs, *uq, *us, *dq, *ds;

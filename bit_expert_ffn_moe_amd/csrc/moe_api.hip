@@ -12,6 +12,8 @@
 
 namespace bef {
 
+KernelTimer g_kernel_timer[3];
+
 __global__ void zero_words_kernel(uint32_t* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
@@ -517,6 +519,14 @@ int moe_device_status(void* ws, void* stream, uint32_t* status, int clear) {
       return MOE_ELAUNCH;
     }
   }
+  return MOE_OK;
+}
+
+int moe_debug_time_kernel(int32_t which, void* start_event, void* stop_event) {
+  if (which != MOE_KERNEL_GEMV_GATE_UP && which != MOE_KERNEL_GEMM_GATE_UP) return MOE_EINVAL;
+  if ((start_event == nullptr) != (stop_event == nullptr)) return MOE_EINVAL;
+  g_kernel_timer[which].start = (hipEvent_t)start_event;
+  g_kernel_timer[which].stop = (hipEvent_t)stop_event;
   return MOE_OK;
 }
 

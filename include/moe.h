@@ -116,7 +116,8 @@ int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *   topk_ids [T][k] int32 out: experts ordered by (logit desc, id asc)
  *   topk_w   [T][k] f32 out: sigmoid(logit) renormalised over the k chosen
  * Logits are fp32 in one fixed order: 64-wide chunk partials, each a chain
- * of fused multiply-adds in ascending h, summed in ascending chunk order.
+ * of fused multiply-adds in ascending h from +0; sums of 4 consecutive
+ * chunks in ascending order; those group sums in ascending order.
  * ws: workspace of at least moe_workspace_bytes(.., T, k). */
 int moe_route(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H, int32_t E,
               int32_t k, int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
@@ -206,6 +207,17 @@ int moe_device_status(void* ws, void* stream, uint32_t* status, int clear);
  * hq [T*k+T][I] u8 with hs [T*k+T][I/128] f32 (both paths). */
 int moe_debug_intermediates(const moe_weights* w, int32_t T, int32_t k, void* ws,
                             size_t ws_bytes, float** h, uint8_t** hq, float** hs);
+
+/* Kernels that moe_debug_time_kernel can time. */
+enum { MOE_KERNEL_GEMV_GATE_UP = 1, MOE_KERNEL_GEMM_GATE_UP = 2 };
+
+/* DEBUG/BENCHMARK ONLY -- kernel timing.  While set, every launch of kernel
+ * `which` (MOE_KERNEL_*) records `start_event` and `stop_event` (hipEvent_t
+ * passed as void*) at that kernel's own begin and end, as part of its
+ * dispatch (hipExtLaunchKernelGGL), so their elapsed time is the kernel's
+ * duration without queueing gaps.  Two NULL events clear it.  Process-wide
+ * and not thread-safe.  MOE_EINVAL for an unknown kernel. */
+int moe_debug_time_kernel(int32_t which, void* start_event, void* stop_event);
 
 #ifdef __cplusplus
 }
