@@ -148,9 +148,11 @@ void orc_act_quant_bf16(const uint16_t* x, int64_t rows, int32_t cols, uint8_t* 
 /* S1: router logits [dpshk "核心实现一": the router runs first and picks   */
 /* the token's experts].  z[t][e] = sum_h x[t][h] * Wr[h][e] in fp32, in    */
 /* one fixed order (reading; dpshk "核心实现四" keeps each row's            */
-/* accumulation order fixed): chunk partials P_c over h = 64c..64c+63,      */
-/* each a chain of fused multiply-adds from +0 in ascending h, then         */
-/* z = ((P_0 + P_1) + P_2) + ... in ascending c.                            */
+/* accumulation order fixed; the pages do not fix the order of the sum):    */
+/* chunk partials P_c over h = 64c..64c+63, each a chain of fused           */
+/* multiply-adds from +0 in ascending h; group sums over 4 consecutive      */
+/* chunks G_g = ((P_4g + P_4g+1) + P_4g+2) + P_4g+3 (the last group may     */
+/* hold fewer); then z = ((G_0 + G_1) + G_2) + ... in ascending g.          */
 /* ======================================================================= */
 
 void orc_router_logits(const uint16_t* x, const uint16_t* wr, int32_t T, int32_t H, int32_t E,
@@ -158,13 +160,14 @@ void orc_router_logits(const uint16_t* x, const uint16_t* wr, int32_t T, int32_t
   const int32_t nc = H / 64;
   for (int32_t t = 0; t < T; ++t) {
     for (int32_t e = 0; e < E; ++e) {
-      float acc = 0.0f;
+      float acc = 0.0f, grp = 0.0f;
       for (int32_t c = 0; c < nc; ++c) {
         float p = 0.0f;
         for (int32_t h = 64 * c; h < 64 * c + 64; ++h) {
           p = fmaf(bf16_to_f32(x[(int64_t)t * H + h]), bf16_to_f32(wr[(int64_t)h * E + e]), p);
         }
-        acc = (c == 0) ? p : acc + p;
+        grp = (c % 4 == 0) ? p : grp + p;
+        if (c % 4 == 3 || c == nc - 1) acc = (c < 4) ? grp : acc + grp;
       }
       z[(int64_t)t * E + e] = acc;
     }
