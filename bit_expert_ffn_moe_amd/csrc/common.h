@@ -141,6 +141,15 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
   v = fmaxf(v, __int_as_float(dpp_keep<0x143, 0xC>(__float_as_int(v))));
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+__device__ __forceinline__ int wave_max_dpp(int v) {
+  v = max(v, dpp_keep<0xB1>(v));
+  v = max(v, dpp_keep<0x4E>(v));
+  v = max(v, dpp_keep<0x141>(v));
+  v = max(v, dpp_keep<0x140>(v));
+  v = max(v, dpp_keep<0x142, 0xA>(v));
+  v = max(v, dpp_keep<0x143, 0xC>(v));
+  return __builtin_amdgcn_readlane(v, 63);
+}
 __device__ __forceinline__ int wave_min_dpp(int v) {
   v = min(v, dpp_keep<0xB1>(v));
   v = min(v, dpp_keep<0x4E>(v));
@@ -242,18 +251,14 @@ __device__ __forceinline__ float group_max(float v) {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
-// Workspace control block: word 0 = status bits, then counters.
+// Workspace control block: word 0 = status bits, then the tagged slots of
+// the fence-free exchanges (zero between launches).
 struct WsCtl {
   uint32_t status;
-  uint32_t route_done;   // arrival counter of the small-T router
-  uint32_t route_epoch;  // launches of the small-T router so far (tags its partials)
-  uint32_t pad[61];
-  // one-token GEMV path: epoch words of each 128-wide block of h,
-  // [row 8][4096/128], then the tagged h slots [row 8][4096] (publish_h)
-  uint32_t hq_arrive[8 * 32];
-  uint32_t pad2[256];
+  uint32_t pad[63];
+  // one-token GEMV path: h slots [row 8][4096] (publish_h)
   uint64_t h_slots[8 * 4096];
-  // small-T router: tagged group sums [H/256 <= 32][T <= 4][E <= 256]
+  // small-T router: group sums [H/256 <= 32][T <= 4][E <= 256]
   uint64_t route_slots[32 * 4 * 256];
 };
 

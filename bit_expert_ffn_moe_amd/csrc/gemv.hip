@@ -56,13 +56,12 @@ __global__ __launch_bounds__(256) void gemv_gate_up_fp4_kernel(
   const int n0b = (blockIdx.x - slot * bpg) * 4 * RUN;
   const int n0 = n0b + wv * RUN;
   for (int r = r0; r < r1; ++r) {
-    const uint32_t epoch = h_epoch(hx, r, n0b);
     const int t = row_token[r];
     uint4 aq[NB][2];
     float xsc[NB];
     load_act_codes<NB>(xq + (size_t)t * w.H, xs + (size_t)t * (w.H >> 7), w.H, lane, aq, xsc);
     const float hv = gate_up_rows<NB>(w, g, n0, lane, aq, xsc);
-    publish_h(hx, hv, r, w.I, n0, n0b, tid, lane, epoch);
+    publish_h(hx, hv, r, w.I, n0, n0b, tid, lane);
   }
 }
 
@@ -179,7 +178,7 @@ static hipError_t launch_gate_up_nb(const GemvArgs& a, hipStream_t st) {
   if (a.I % 128 != 0 || a.I > kHSlotStride) return hipErrorInvalidValue;
   const GUWeights w = {a.gq, a.gs, a.uq, a.us, a.E, a.H, a.I};
   const dim3 grid((a.I / (4 * RUN)) * a.n_slots);
-  const HExchange hx = {a.hq_arrive, a.h_slots, a.h, a.hq_ws, a.hs_ws, a.status};
+  const HExchange hx = {a.h_slots, a.h, a.hq_ws, a.hs_ws, a.status};
   const KernelTimer& tm = g_kernel_timer[MOE_KERNEL_GEMV_GATE_UP];
   if (tm.start)
     hipExtLaunchKernelGGL(gemv_gate_up_fp4_kernel<NB>, grid, dim3(256), 0, st, tm.start, tm.stop,

@@ -173,54 +173,48 @@ __device__ __forceinline__ int h_row(int lane) { return (lane >> 3) & 3; }
 // The requantisation of h ahead of the down projection, done once, with no
 // device-scope fence (on this chip a release fence writes back the whole L2
 // of the XCD) and no round trip for the blocks that only write.  h moves
-// between blocks through 64-bit atomics, which are coherent across the XCDs.
-// Each (row r, 128-wide block c of h) has an epoch word, advanced once per
-// launch that produces it:
-//  * every block producing rows of (r, c) reads the epoch e before it
-//    publishes (h_epoch, early, so the load overlaps the weight stream) and
-//    sends its values out as {e + 1, value bits} words (atomic exchange;
-//    never tag 0: the slots start zeroed);
+// between blocks through 64-bit atomics, which are coherent across the XCDs:
+//  * every block producing rows of (row r, 128-wide block c of h) sends its
+//    values out as {kSlotValid, value bits} words (atomic exchange) -- it
+//    reads nothing first, so its weight stream starts at once;
 //  * the last of the 8 blocks of (r, c) in launch order reads the 128 words
-//    (atomic loads) until every tag is e + 1 -- a bounded wait: past
-//    kSpinLimit rounds it flags MOE_STATUS_SYNC_TIMEOUT and carries on --,
-//    writes the E4M3 codes and scale with the act_quant rule (s = amax / 448
-//    by IEEE division, code = E4M3(v / s), zero block -> s = 0, code 0;
-//    dpshk.com article, section "核心实现二"), then advances the epoch: every
-//    block of (r, c) read it before publishing, so none can miss the change.
-// Slots have a fixed row stride of kHSlotStride so that a slot always
-// belongs to the same epoch word, whatever I a call uses.
+//    (atomic loads) until every one carries kSlotValid -- a bounded wait:
+//    past kSpinLimit rounds it flags MOE_STATUS_SYNC_TIMEOUT and carries on
+//    --, returns them to zero for the next launch (each slot is written once
+//    per launch, so nothing can land after that reset), and writes the E4M3
+//    codes and scale with the act_quant rule (s = amax / 448 by IEEE
+//    division, code = E4M3(v / s), zero block -> s = 0, code 0; dpshk.com
+//    article, section "核心实现二").
+// The slots start zeroed (workspace initialisation); after a timeout a late
+// write could outlive the reset, so a workspace that reported one must be
+// initialised again.
 constexpr int kHSlotStride = 4096;   // largest I on the one-token path
 constexpr int kHSlotRows = 8;
 constexpr uint32_t kSpinLimit = 1u << 16;
 constexpr uint32_t kStatusSyncTimeout = 2u;  // MOE_STATUS_SYNC_TIMEOUT
+constexpr uint64_t kSlotValid = 1ull << 32;
+constexpr uint64_t kSlotTagMask = 0xffffffff00000000ull;
 
 struct HExchange {
-  uint32_t* epochs;    // [kHSlotRows][kHSlotStride / 128]
-  uint64_t* slots;     // [kHSlotRows][kHSlotStride] {tag, value bits}
+  uint64_t* slots;     // [kHSlotRows][kHSlotStride] {kSlotValid, value bits} or 0
   float* h;            // [rows][I] plain copy of h (inspection)
   uint8_t* hq;         // [rows][I] E4M3 codes
   float* hs;           // [rows][I/128] scales
   uint32_t* status;
 };
 
-__device__ __forceinline__ uint32_t h_epoch(const HExchange& x, int r, int n0b) {
-  return __hip_atomic_load(x.epochs + r * (kHSlotStride / 128) + (n0b >> 7), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Called by every thread of a block whose waves hold h values hv (in the
 // h_lane lanes) for rows n0 .. n0+3 of h row r; the block's rows start at
-// n0b.  epoch: h_epoch(x, r, n0b), read by this block before.
+// n0b.
 __device__ __forceinline__ void publish_h(const HExchange& x, float hv, int r, int I, int n0,
-                                          int n0b, int tid, int lane, uint32_t epoch) {
+                                          int n0b, int tid, int lane) {
   constexpr int kRowsPerBlock = 4 * kGuRun;
   const int c = n0b >> 7;
-  const uint64_t tag = (uint64_t)(epoch + 1u) << 32;
   unsigned long long* slot = reinterpret_cast<unsigned long long*>(x.slots) + r * kHSlotStride;
   if (h_lane(lane)) {
     const int n = n0 + h_row(lane);
     x.h[(size_t)r * I + n] = hv;
-    atomicExch(slot + n, tag | __float_as_uint(hv));
+    atomicExch(slot + n, kSlotValid | __float_as_uint(hv));
   }
   if (n0b + kRowsPerBlock != 128 * (c + 1) || tid >= 64) return;
   // the reader: the last block of this 128-wide block of h
@@ -229,15 +223,17 @@ __device__ __forceinline__ void publish_h(const HExchange& x, float hv, int r, i
   uint32_t spins = 0;
   bool ok = false;
   for (;;) {
-    if ((w0 & 0xffffffff00000000ull) != tag)
+    if ((w0 & kSlotTagMask) != kSlotValid)
       w0 = __hip_atomic_load(slot + n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((w1 & 0xffffffff00000000ull) != tag)
+    if ((w1 & kSlotTagMask) != kSlotValid)
       w1 = __hip_atomic_load(slot + n + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    ok = (w0 & 0xffffffff00000000ull) == tag && (w1 & 0xffffffff00000000ull) == tag;
+    ok = (w0 & kSlotTagMask) == kSlotValid && (w1 & kSlotTagMask) == kSlotValid;
     if (__all(ok) || ++spins >= kSpinLimit) break;
     __builtin_amdgcn_s_sleep(1);
   }
   if (!ok) atomicOr(x.status, kStatusSyncTimeout);
+  __hip_atomic_store(slot + n, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(slot + n + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const float v0 = __uint_as_float((uint32_t)w0), v1 = __uint_as_float((uint32_t)w1);
   const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
   const float sc = amax / 448.0f;
@@ -245,10 +241,7 @@ __device__ __forceinline__ void publish_h(const HExchange& x, float hv, int r, i
   if (amax != 0.0f) q = e4m3_pack4(v0 / sc, v1 / sc, 0.0f, 0.0f);
   const size_t e = (size_t)r * I + n;
   reinterpret_cast<uint16_t*>(x.hq + e)[0] = (uint16_t)q;
-  if (tid == 0) {
-    x.hs[(size_t)r * (I >> 7) + c] = sc;
-    atomicAdd(x.epochs + r * (kHSlotStride / 128) + c, 1u);
-  }
+  if (tid == 0) x.hs[(size_t)r * (I >> 7) + c] = sc;
 }
 
 }  // namespace bef

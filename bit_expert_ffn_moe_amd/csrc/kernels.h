@@ -35,8 +35,7 @@ struct GemvArgs {
   int out_bf16;
   uint8_t* hq_ws;
   float* hs_ws;
-  uint32_t* hq_arrive;  // zeroed counters and tagged slots of the h exchange
-  uint64_t* h_slots;
+  uint64_t* h_slots;    // tagged slots of the h exchange (zero between launches)
   uint32_t* status;
 };
 
@@ -60,9 +59,7 @@ struct FrontArgs {
   const uint16_t* x;
   const uint16_t* wr;
   int T, H, E, k;
-  uint32_t* counter;      // router arrival counter (zero between launches)
-  uint32_t* epoch;        // launch epoch of the tagged partials
-  uint64_t* slots;        // [H/256][T][E] tagged group sums
+  uint64_t* slots;        // [H/256][T][E] tagged group sums (zero between launches)
   int32_t* ids;
   float* w;
   uint8_t* xq;
@@ -76,7 +73,6 @@ struct FrontArgs {
   float* sh_h;
   uint8_t* sh_hq;         // requantised h (rows of the shared expert)
   float* sh_hs;
-  uint32_t* hq_arrive;
   uint64_t* h_slots;
   uint32_t* status;
 };

@@ -186,7 +186,6 @@ GemvArgs gemv_args(const moe_weights* w, int T, int k, const Layout& L, void* ws
   a.h = at<float>(ws, L.h);
   a.hq_ws = at<uint8_t>(ws, L.hq);
   a.hs_ws = at<float>(ws, L.hs);
-  a.hq_arrive = at<WsCtl>(ws, L.ctl)->hq_arrive;
   a.h_slots = at<WsCtl>(ws, L.ctl)->h_slots;
   a.status = &at<WsCtl>(ws, L.ctl)->status;
   return a;
@@ -443,7 +442,6 @@ int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint1
       fa.sh_h = at<float>(ws, L.h);
       fa.sh_hq = at<uint8_t>(ws, L.hq);
       fa.sh_hs = at<float>(ws, L.hs);
-      fa.hq_arrive = ctl->hq_arrive;
       fa.h_slots = ctl->h_slots;
       fa.active = at<int4>(ws, L.active);
       fa.n_active_slots = (T * k < E ? T * k : E);

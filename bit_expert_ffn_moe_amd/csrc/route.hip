@@ -12,8 +12,10 @@
 // in how the (token, expert, chunk) work is spread over the GPU.
 //
 // Selection: order by (logit desc, id asc), keep k in rank order; weights
-// sigmoid(logit) renormalised over the chosen k (fp32, device expf).
+// sigmoid(logit) renormalised over the chosen k (fp32, device expf).  The
+// pages give no order for a NaN logit: it ranks below every number.
 #include <float.h>
+#include <limits.h>
 
 #include "common.h"
 #include "gemv_body.h"
@@ -22,51 +24,61 @@
 namespace bef {
 
 // One wavefront picks the top-k of E <= 256 logits held in LDS and writes
-// ids / weights.  Lane l owns experts l, l+64, l+128, l+192.  Each of the k
-// rounds takes every lane's best remaining expert (its lowest id among its
-// largest), the wave maximum by DPP, and -- when several lanes hold that
-// value -- the lowest of their ids by a DPP minimum; the winner's lane marks
-// it taken.
+// ids / weights.  Lane l owns experts l, l+64, l+128, l+192, as integer keys
+// that order like the logits (-0 made +0; a NaN below every number, an
+// expert beyond E below that), sorted in the lane by (key desc, id asc).
+// Each of the k rounds takes the wave maximum of the lanes' leading keys by
+// DPP -- when several lanes hold it, the lowest of their ids by a DPP
+// minimum -- and the winning lane moves on to its next key.
 __device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, int k,
                                           int32_t* __restrict__ ids_out,
                                           float* __restrict__ w_out) {
-  constexpr int kNone = 0x7fffffff;
+  constexpr int kAbsent = INT_MIN, kNaN = INT_MIN + 1;
   const int lane = threadIdx.x & 63;
-  float v[4];
+  int key[4], sl[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    v[i] = (e < E) ? z[e] : 0.0f;
+    const float v = (e < E) ? z[e] : 0.0f;
+    const int b = __float_as_int(v + 0.0f);
+    key[i] = (e >= E) ? kAbsent : (v != v) ? kNaN : (b >= 0 ? b : b ^ 0x7fffffff);
+    sl[i] = i;
   }
-  uint32_t taken = 0;
-  float my_z = 0.0f;
+  // a 4-input sorting network on (key desc, slot asc)
+  auto ce = [&](int a, int b) {
+    const bool sw = key[b] > key[a] || (key[b] == key[a] && sl[b] < sl[a]);
+    const int ka = key[a], sa = sl[a];
+    key[a] = sw ? key[b] : ka;
+    sl[a] = sw ? sl[b] : sa;
+    key[b] = sw ? ka : key[b];
+    sl[b] = sw ? sa : sl[b];
+  };
+  ce(0, 1);
+  ce(2, 3);
+  ce(0, 2);
+  ce(1, 3);
+  ce(1, 2);
   int my_id = 0;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = kNone;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1u) && (bi == kNone || v[i] > bv)) {
-        bv = v[i];
-        bi = e;
-      }
+    const int m = wave_max_dpp(key[0]);
+    const uint64_t cand = __ballot(key[0] == m);
+    int wl;
+    if (__popcll(cand) == 1) {
+      wl = __ffsll((long long)cand) - 1;
+    } else {
+      const int id = ((cand >> lane) & 1ull) ? lane + 64 * sl[0] : 0x7fffffff;
+      wl = wave_min_dpp(id) & 63;
     }
-    const float m = wave_max_dpp(bv);
-    uint64_t cand = __ballot(bi != kNone && bv == m);
-    if (cand == 0) cand = __ballot(bi != kNone);  // only NaNs left
-    int win;
-    if (__popcll(cand) == 1)
-      win = __builtin_amdgcn_readlane(bi, __ffsll((long long)cand) - 1);
-    else
-      win = wave_min_dpp(((cand >> lane) & 1ull) ? bi : kNone);
-    const float wz = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), win & 63));
-    if (lane == (win & 63)) taken |= 1u << (win >> 6);
-    if (lane == j) {
-      my_z = wz;
-      my_id = win;
+    const int win = __builtin_amdgcn_readlane(lane + 64 * sl[0], wl);
+    if (lane == j) my_id = win;
+    if (lane == wl) {
+      key[0] = key[1], sl[0] = sl[1];
+      key[1] = key[2], sl[1] = sl[2];
+      key[2] = key[3], sl[2] = sl[3];
+      key[3] = kAbsent;
     }
   }
+  const float my_z = (lane < k) ? z[my_id] : 0.0f;
   const float sg = (lane < k) ? 1.0f / (1.0f + expf(-my_z)) : 0.0f;
   const float sum = wave_sum(sg);
   if (lane < k) {
@@ -80,21 +92,20 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, in
 //  * Router blocks (group g, quarter q), g < H/256, q < E/64: wave j computes
 //    the chunk 4g+j partials of experts 64q .. 64q+63 for every token -- lane
 //    l streams 64 rows of column 64q+l, all loads issued before the
-//    multiply-adds -- and the block publishes the group sums, tagged with
-//    the launch's epoch, through 64-bit atomic exchanges (no device-scope
-//    fence).
+//    multiply-adds -- and the block publishes the group sums as
+//    {kSlotValid, value} words through 64-bit atomic exchanges (no
+//    device-scope fence, and nothing read first).
 //  * When sh_h is set (single-token FP4 path), the next I/(4 RUN) blocks per
 //    token run the shared expert's gate+up GEMV rows (it needs no routing):
 //    its 8.9 MB stream overlaps the router's reduction chain; the last block
 //    of each 128-wide block of h requantises it.
 //  * Then, when xq is set, act_quant blocks of x (16 lanes per 128-block).
-//  * The last router block to arrive (arrival counter in the workspace,
-//    returned to zero by that block) reads the group sums with atomic loads
-//    until each carries this launch's tag (a bounded wait), adds them in
-//    group order, runs the top-k (one wave per token), computes the weights
-//    and, when asked, writes the permutation tables (the single-block form
-//    of S4) and the list of active routed groups; last, it advances the
-//    epoch.
+//  * The last router block (in launch order) reads the group sums with
+//    atomic loads until each carries kSlotValid (a bounded wait), returns
+//    the slots to zero for the next launch, adds the sums in group order,
+//    runs the top-k (one wave per token), computes the weights and, when
+//    asked, writes the permutation tables (the single-block form of S4) and
+//    the list of active routed groups.
 // ---------------------------------------------------------------------------
 template <int NB>
 __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
@@ -112,14 +123,13 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
       const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
       const int n0b = (b - t * bpg) * 4 * kGuRun;
       const GUWeights w = {a.sh_gq, a.sh_gs, a.sh_uq, a.sh_us, E, H, a.I};
-      const HExchange hx = {a.hq_arrive, a.h_slots, a.sh_h, a.sh_hq, a.sh_hs, a.status};
-      const uint32_t epoch = h_epoch(hx, T * k + t, n0b);
+      const HExchange hx = {a.h_slots, a.sh_h, a.sh_hq, a.sh_hs, a.status};
       uint4 aq[NB][2];
       float xsc[NB];
       quant_act_codes<NB>(a.x + (size_t)t * H, H, lane, aq, xsc);
       const int n0 = n0b + wv * kGuRun;
       const float hv = gate_up_rows<NB>(w, E, n0, lane, aq, xsc);
-      publish_h(hx, hv, T * k + t, a.I, n0, n0b, tid, lane, epoch);
+      publish_h(hx, hv, T * k + t, a.I, n0, n0b, tid, lane);
       return;
     }
     b -= bpg * T;
@@ -169,11 +179,6 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
   __shared__ float s_w[kRouteSmallT * 16];
   __shared__ int s_sorted[kRouteSmallT * 16];
   __shared__ int s_rank[kRouteSmallT * 16];
-  __shared__ uint32_t s_ticket;
-  // this launch's tag; the epoch word changes only at the very end of a
-  // launch, after every block has read it (each reads it before its ticket)
-  const uint32_t epoch = __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t tag = (uint64_t)(epoch + 1u) << 32;
   for (int i = tid; i < T * 256; i += 256) {
     const int t = i >> 8, h = 256 * g + (i & 255);
     sx[t][i & 255] = (h < H) ? bf16_to_f32(a.x[(size_t)t * H + h]) : 0.0f;
@@ -197,22 +202,21 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
   __syncthreads();
   unsigned long long* slots = reinterpret_cast<unsigned long long*>(a.slots);
   if (tid < T * 64) {
-    // the group sum of this (token, expert), published with this launch's tag
+    // the group sum of this (token, expert)
     const int t = tid >> 6, eg = 64 * q + lane;
     if (eg < E) {
       float G = sp[0][t][lane];
       for (int jc = 1; jc < 4 && 4 * g + jc < nc; ++jc) G = G + sp[jc][t][lane];
-      atomicExch(slots + ((size_t)g * T + t) * E + eg, tag | __float_as_uint(G));
+      atomicExch(slots + ((size_t)g * T + t) * E + eg, kSlotValid | __float_as_uint(G));
     }
   }
-  __syncthreads();
-  if (tid == 0) s_ticket = atomicAdd(a.counter, 1u);
-  __syncthreads();
-  if (s_ticket != (uint32_t)(nr - 1)) return;
+  if ((int)blockIdx.x != nr - 1) return;
 
-  // the last block: logits in the fixed order (group sums added in
+  // the last router block: logits in the fixed order (group sums added in
   // ascending group order), waiting -- bounded -- until every group sum of
-  // this launch is visible; thread ez owns expert ez
+  // this launch is visible, then clearing the slots; thread ez owns expert
+  // ez (each slot is written once per launch, so the clear cannot race a
+  // write of this launch)
   const int ez = tid;
   bool ok = true;
   for (int t = 0; t < T; ++t) {
@@ -225,12 +229,12 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
         for (int i = 0; i < 32; ++i)
           v[i] = (c0 + i < ng) ? __hip_atomic_load(slots + ((size_t)(c0 + i) * T + t) * E + ez,
                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                               : tag;
+                               : kSlotValid;
         for (uint32_t spins = 0;;) {
           bool all = true;
 #pragma unroll
           for (int i = 0; i < 32; ++i)
-            if ((v[i] & 0xffffffff00000000ull) != tag) {
+            if ((v[i] & kSlotTagMask) != kSlotValid) {
               all = false;
               v[i] = __hip_atomic_load(slots + ((size_t)(c0 + i) * T + t) * E + ez,
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -242,6 +246,11 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
           }
           __builtin_amdgcn_s_sleep(1);
         }
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          if (c0 + i < ng)
+            __hip_atomic_store(slots + ((size_t)(c0 + i) * T + t) * E + ez, 0ull, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
         for (int i = 0; i < 32; ++i)
           if (c0 + i < ng) acc = (c0 + i == 0) ? __uint_as_float((uint32_t)v[i])
@@ -312,10 +321,6 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
       for (int i = __popcll(m) + lane; i < a.n_active_slots; i += 64)
         a.active[i] = make_int4(-1, 0, 0, 0);
     }
-  }
-  if (tid == 0) {
-    *a.counter = 0u;
-    atomicAdd(a.epoch, 1u);
   }
 }
 
@@ -428,15 +433,13 @@ hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int H, int
 }
 
 void set_route_sync(FrontArgs& a, WsCtl* ctl) {
-  a.counter = &ctl->route_done;
-  a.epoch = &ctl->route_epoch;
   a.slots = ctl->route_slots;
   a.status = &ctl->status;
 }
 
 hipError_t launch_route_front(const FrontArgs& a, hipStream_t st) {
   if (a.T < 1 || a.T > kRouteSmallT || a.k > 16 || a.E > 256 || a.H % 64 != 0 ||
-      (a.H / 64 + 3) / 4 > kRouteMaxGroups || !a.counter || !a.epoch || !a.slots || !a.status)
+      (a.H / 64 + 3) / 4 > kRouteMaxGroups || !a.slots || !a.status)
     return hipErrorInvalidValue;
   int nq = 0, nsh = 0;
   if (a.xq) nq = (int)(((int64_t)a.T * (a.H / 128) * 16 + 255) / 256);

@@ -68,8 +68,10 @@ enum {
 enum { MOE_DT_BF16 = 1, MOE_DT_F32 = 2 };
 
 /* Device status word bits (see moe_device_status).  MOE_STATUS_SYNC_TIMEOUT:
- * on the one-token path, a block waiting for the h values of other blocks
- * gave up after its bounded wait; the results of that call are invalid. */
+ * on the small-T router or the one-token path, a block waiting for the
+ * values of other blocks gave up after its bounded wait; the results of that
+ * call are invalid, and the workspace must go through moe_workspace_init
+ * again before its next use (a late value could outlive the clean-up). */
 enum { MOE_STATUS_BAD_EXPERT_ID = 1u, MOE_STATUS_SYNC_TIMEOUT = 2u };
 
 /* Stacked expert weights, expert-major; slot E (the last) is the shared
@@ -101,12 +103,12 @@ typedef struct moe_weights {
 size_t moe_workspace_bytes(const moe_weights* w, int32_t max_tokens, int32_t top_k);
 
 /* Enqueue a zero-fill of the workspace's control block (about 1.3 MB: the
- * status word, the counters some kernels keep, and the tagged slots through
- * which blocks of one launch hand each other router partials and h values
- * without device-scope fences; a slot's tag names the launch that wrote it,
- * so the slots must start zeroed).  Call once after allocating a workspace,
- * before its first use; the kernels keep the control block consistent from
- * then on. */
+ * status word and the slots through which blocks of one launch hand each
+ * other router partials and h values without device-scope fences; a slot
+ * holds a valid mark with its value, and the block that consumes it clears
+ * it, so the slots must start zeroed).  Call once after allocating a
+ * workspace, before its first use (and again after MOE_STATUS_SYNC_TIMEOUT);
+ * the kernels keep the control block consistent from then on. */
 int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* S1+S2, the router (dpshk.com article, section "核心实现一"; top-6 of 256:

@@ -180,7 +180,16 @@ void orc_router_logits(const uint16_t* x, const uint16_t* wr, int32_t T, int32_t
 /* id ascending); the first k are kept in that rank order.  Scores are     */
 /* sigmoids (fp64 here), w_j = s_j / sum_{i<k} s_i.  Selection is on the    */
 /* fp32 logit (the sigmoid is increasing, so the order is the same).       */
+/* The pages define no order for a NaN logit (reading: it ranks below every */
+/* number, -inf included, lower id first among NaNs); -0 and +0 are equal.  */
 /* ======================================================================= */
+
+/* Logit a ranks strictly before logit b (ties leave the lower id first). */
+static int ranks_before(float a, float b) {
+  if (isnan(a)) return 0;
+  if (isnan(b)) return 1;
+  return a > b;
+}
 
 void orc_topk(const float* z, int32_t T, int32_t E, int32_t k, int32_t* ids, double* w) {
   char* taken = (char*)malloc((size_t)E);
@@ -191,7 +200,7 @@ void orc_topk(const float* z, int32_t T, int32_t E, int32_t k, int32_t* ids, dou
       int32_t best = -1;
       for (int32_t e = 0; e < E; ++e) {
         if (taken[e]) continue;
-        if (best < 0 || zt[e] > zt[best]) best = e; /* strict '>' keeps the lower id on ties */
+        if (best < 0 || ranks_before(zt[e], zt[best])) best = e; /* ties keep the lower id */
       }
       taken[best] = 1;
       ids[(int64_t)t * k + j] = best;

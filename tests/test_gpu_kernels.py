@@ -160,6 +160,39 @@ def test_route_ties_within_and_across_lanes(T):
     assert np.allclose(to_host(w), wref, rtol=1e-5, atol=0)
 
 
+@pytest.mark.parametrize("T", [1, 4, 9])
+@pytest.mark.parametrize("E,k", [(256, 8), (12, 12)])
+def test_route_nan_and_inf_logits(T, E, k):
+    """0 * inf makes a NaN logit, 1 * (+-inf) an infinite one: +inf ranks
+    first, -inf after every finite logit, NaN after every number (lower ids
+    first among equals), as the oracle orders them."""
+    _print("route nan/inf", T, E, k)
+    H = 256
+    x = synth.normal_bf16(35, 1, (T, H), 1.0) & np.uint16(0x7FFF)
+    x[:, 0] = 0x0000                      # 0.0
+    x[:, 1] = 0x3F80                      # 1.0
+    wr = synth.normal_bf16(35, 2, (H, E), 0.02)
+    for e in (2, 5):
+        wr[0, e] = 0x7F80                 # +inf * 0 -> NaN
+    wr[1, 9] = 0x7F80                     # +inf
+    wr[1, 3] = 0xFF80                     # -inf
+    if E > 130:
+        wr[0, 200] = 0x7F80
+        wr[1, 130] = 0x7F80
+    ws_b = 1 << 22
+    ws = torch.zeros(ws_b, dtype=torch.uint8, device="cuda")
+    moe.moe_workspace_init(ws, ws_b)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_route(to_dev(x), to_dev(wr), T, H, E, k, ids, w, ws, ws_b)
+    ir, wref = orc.route(x, wr, k)
+    assert ir[0, 0] == 9
+    if E == 12:
+        assert ir[0, -3:].tolist() == [3, 2, 5]
+    assert np.array_equal(to_host(ids), ir)
+    assert np.allclose(to_host(w), wref, rtol=1e-5, atol=0, equal_nan=True)
+
+
 # ----------------------------------------------------------------- S4 -----
 
 def _permute_gpu(ids, E):

@@ -79,6 +79,23 @@ def _brute_topk(zt, k):
     return best[1]
 
 
+def test_topk_nan_ranks_after_every_number():
+    # no order is given for NaN logits; the reading ranks them below -inf,
+    # lower id first among themselves, and keeps -0 == +0
+    nan, inf = np.float32(np.nan), np.float32(np.inf)
+    z = np.array([[nan, 1.0, nan, -inf, 0.5, nan],
+                  [nan, nan, nan, nan, nan, nan],
+                  [-0.0, 0.0, nan, -0.0, inf, -inf],
+                  [nan, -inf, -inf, nan, 2.0, 2.0]], dtype=np.float32)
+    expect = {1: [[1], [0], [4], [4]],
+              3: [[1, 4, 3], [0, 1, 2], [4, 0, 1], [4, 5, 1]],
+              6: [[1, 4, 3, 0, 2, 5], [0, 1, 2, 3, 4, 5], [4, 0, 1, 3, 5, 2],
+                  [4, 5, 1, 2, 0, 3]]}
+    for k, rows in expect.items():
+        ids, _ = orc.topk(z, k)
+        assert ids.tolist() == rows
+
+
 def test_topk_matches_brute_force_over_all_subsets():
     rng = np.random.default_rng(11)
     z = rng.standard_normal((50, 8)).astype(np.float32)
