@@ -75,25 +75,52 @@ __global__ __launch_bounds__(256) void gemv_gate_up_fp4_kernel(
 // COMBINE then adds them per output row in LDS -- the shared row first, then
 // the routed slots in rank order, out[m] = y[shared] + sum_j w_j y[row_of[j]]
 // (T = 1); otherwise the totals go to y_rows.
+// A row's group comes from the active list when the front kernel wrote one
+// (a few uniform loads; the last row is the shared expert's), else from the
+// offsets table through LDS.  The combine's row_of / topk_w are loaded at
+// the start, so the kernel's tail has no dependent load.
 // ---------------------------------------------------------------------------
 template <int NB, bool COMBINE>
 __global__ __launch_bounds__(512) void gemv_down_fp4_kernel(
     const uint8_t* __restrict__ dq, const uint8_t* __restrict__ ds,
     const uint8_t* __restrict__ hq, const float* __restrict__ hs,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_of,
-    const float* __restrict__ topk_w, int E, int H, int I, int k, float* __restrict__ y_rows,
-    void* __restrict__ out, int out_bf16) {
+    const int32_t* __restrict__ offsets, const int4* __restrict__ active, int n_slots,
+    int n_rows, const int32_t* __restrict__ row_of, const float* __restrict__ topk_w, int E,
+    int H, int I, int k, float* __restrict__ y_rows, void* __restrict__ out, int out_bf16) {
   constexpr int RMAX = kGemvMaxRows, RUN = 8, DEPTH = 3;
   __shared__ int s_rowexp[RMAX];
   __shared__ float s_y[RMAX][RUN];
   const int tid = threadIdx.x, lane = tid & 63;
   const int r = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int R = min(offsets[E + 1], RMAX);
-  for (int g = tid; g <= E; g += 512) {
-    const int a = offsets[g], b = offsets[g + 1];
-    for (int rr = a; rr < b && rr < RMAX; ++rr) s_rowexp[rr] = g;
+  int ro[RMAX];
+  float twj[RMAX];
+  if (COMBINE) {
+#pragma unroll
+    for (int j = 0; j < RMAX; ++j) {
+      ro[j] = (j <= k) ? row_of[j] : -1;
+      twj[j] = (j < k) ? topk_w[j] : 0.0f;
+    }
   }
-  __syncthreads();
+  int R, g = 0;
+  if (active) {
+    R = min(n_rows, RMAX);
+    g = E;  // the last row: the shared expert
+    if (r < R - 1) {
+      g = 0;
+      for (int q = 0; q < n_slots; ++q) {
+        const int4 v = active[q];
+        if (v.x >= 0 && r >= v.y && r < v.z) g = v.x;
+      }
+    }
+  } else {
+    R = min(offsets[E + 1], RMAX);
+    for (int gg = tid; gg <= E; gg += 512) {
+      const int a = offsets[gg], b = offsets[gg + 1];
+      for (int rr = a; rr < b && rr < RMAX; ++rr) s_rowexp[rr] = gg;
+    }
+    __syncthreads();
+    if (r < R) g = s_rowexp[r];
+  }
   const int m0 = blockIdx.x * RUN;
   if (r < R) {
     const int nch = I >> 5;
@@ -111,7 +138,7 @@ __global__ __launch_bounds__(512) void gemv_down_fp4_kernel(
       aq[c][1] = *reinterpret_cast<const uint4*>(p + 16);
       hs_raw[c] = hs[(size_t)r * (I >> 7) + (ch[c] >> 2)];
     }
-    const size_t row0 = (size_t)s_rowexp[r] * H + m0;
+    const size_t row0 = (size_t)g * H + m0;
     const uint8_t* wb = dq + row0 * rowq;
     const uint8_t* sbb = ds + row0 * rows_;
     uint4 w[DEPTH][NB];
@@ -155,11 +182,11 @@ __global__ __launch_bounds__(512) void gemv_down_fp4_kernel(
   __syncthreads();
   if (COMBINE) {
     if (tid < RUN) {
-      const int rs = row_of[k];
+      const int rs = ro[k & (RMAX - 1)];
       float o = (rs >= 0 && rs < RMAX) ? s_y[rs][tid] : 0.0f;
       for (int j = 0; j < k; ++j) {
-        const int rj = row_of[j];
-        if (rj >= 0 && rj < RMAX) o = fmaf(topk_w[j], s_y[rj][tid], o);
+        const int rj = ro[j & (RMAX - 1)];
+        if (rj >= 0 && rj < RMAX) o = fmaf(twj[j & (RMAX - 1)], s_y[rj][tid], o);
       }
       const int m = m0 + tid;
       if (out_bf16)
@@ -192,9 +219,10 @@ static hipError_t launch_gate_up_nb(const GemvArgs& a, hipStream_t st) {
 template <int NB, bool COMBINE>
 static hipError_t launch_down_nb(const GemvArgs& a, hipStream_t st) {
   if (a.H % 8 != 0) return hipErrorInvalidValue;
+  if (COMBINE && a.k + 1 > kGemvMaxRows) return hipErrorInvalidValue;
   gemv_down_fp4_kernel<NB, COMBINE><<<dim3(a.H / 8), 512, 0, st>>>(
-      a.dq, a.ds, a.hq_ws, a.hs_ws, a.offsets, a.row_of, a.topk_w, a.E, a.H, a.I, a.k, a.y_rows,
-      a.out, a.out_bf16);
+      a.dq, a.ds, a.hq_ws, a.hs_ws, a.offsets, a.active, a.n_slots, a.n_rows, a.row_of,
+      a.topk_w, a.E, a.H, a.I, a.k, a.y_rows, a.out, a.out_bf16);
   return hipGetLastError();
 }
 

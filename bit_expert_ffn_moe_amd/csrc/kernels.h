@@ -37,6 +37,7 @@ struct GemvArgs {
   float* hs_ws;
   uint64_t* h_slots;    // tagged slots of the h exchange (zero between launches)
   uint32_t* status;
+  int n_rows;           // down with an active list: T*k + T rows, the last the shared one
 };
 
 struct GemmArgs {

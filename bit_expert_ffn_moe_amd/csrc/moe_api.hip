@@ -454,8 +454,10 @@ int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint1
       a.n_slots = fa.n_active_slots;
       rc = launch_status(launch_gemv_gate_up(a, st));
       if (rc) return rc;
-      return enqueue_down(w, T, k, offsets, row_of, fa.w, at<float>(ws, L.y), out, out_dtype, L,
-                          ws, st);
+      // down + combine, the rows' groups from the same active list
+      a.row_of = row_of, a.topk_w = fa.w, a.n_rows = T * k + T;
+      a.out = out, a.out_bf16 = out_dtype == MOE_DT_BF16;
+      return launch_status(launch_gemv_down(a, true, st));
     }
     // router + act_quant + permute in one kernel
     fa.xq = xq, fa.xs = xs;

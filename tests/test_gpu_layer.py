@@ -16,8 +16,8 @@ if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import bit_expert_ffn_moe_amd as moe  # noqa: E402
-from gpu_util import (DevLayer, bf16_bits_to_f32, f64_to_bf16_bits, max_rel, rel_l2,  # noqa: E402
-                      to_dev, to_host)
+from gpu_util import (DevLayer, bf16_bits_to_f32, d2h, f64_to_bf16_bits, max_rel,  # noqa: E402
+                      rel_l2, to_dev, to_host)
 
 orc = Oracle()
 REL_L2, MAX_ABS = 2e-3, 1e-2
@@ -129,6 +129,56 @@ def test_decode_t1_repeated_expert_ids():
         _check(to_host(out2), orc.forward(Weights.from_layer(L2), L2.wr, L2.x, 6), "decode I=1024")
     _check(to_host(D.forward()), ref, "decode repeated ids, after I=1024")
     assert moe.moe_device_status(D.ws) == 0
+
+
+@pytest.mark.parametrize("name,over", [("decode_t1", dict(T=1)), ("tiny_t8", dict(T=1)),
+                                       ("decode_t1", dict(T=1, I=1024, seed=2002))])
+def test_decode_layer_matches_stagewise_kernels(name, over):
+    """The router's one-token path (front kernel with the shared expert's
+    gate+up, gate+up kernel, down+combine kernel) against the oracle's h rows
+    and the act_quant of its own h, and bit for bit against the separate
+    gate+up and down+combine calls on the same routing (same arithmetic in
+    the same order); three calls in a row reuse the workspace."""
+    _print("decode vs stagewise", name, over)
+    L = synth.make_layer(name, **over)
+    wl = L.wl
+    k, E, H, I = wl.k, wl.E, wl.H, wl.I
+    R = k + 1
+    D = DevLayer(L)
+    W = Weights.from_layer(L)
+    ids, _ = orc.route(L.x, L.wr, k)
+    xq, xs = orc.act_quant(L.x)
+    offsets, row_token, row_of, _ = orc.permute(ids, E)
+    grp = np.searchsorted(offsets, np.arange(R), side="right") - 1
+    rows_ref = [orc.expert_row(W, int(grp[r]), xq[0], xs[0]) for r in range(R)]
+    ref = orc.forward(W, L.wr, L.x, k)
+    # the separate kernels, on a workspace of their own
+    ws2 = torch.zeros(D.ws_bytes, dtype=torch.uint8, device="cuda")
+    moe.moe_workspace_init(ws2, D.ws_bytes)
+    gids = torch.empty((1, k), dtype=torch.int32, device="cuda")
+    gw = torch.empty((1, k), dtype=torch.float32, device="cuda")
+    moe.moe_route(D.x, D.wr, 1, H, E, k, gids, gw, ws2, D.ws_bytes)
+    assert np.array_equal(to_host(gids), ids)
+    moe.moe_expert_gate_up(D.w, to_dev(xq), to_dev(xs), 1, k, to_dev(offsets), to_dev(row_token),
+                           ws2, D.ws_bytes)
+    out2 = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    moe.moe_expert_down(D.w, 1, k, to_dev(offsets), to_dev(row_of), gw, None, out2,
+                        moe.MOE_DT_F32, ws2, D.ws_bytes)
+    o2 = to_host(out2)
+    for call in range(3):
+        out = to_host(D.forward())
+        _check(out, ref, f"decode {name} {over} call {call}")
+        assert np.array_equal(out, o2), call
+        hp, hqp, hsp = moe.moe_debug_intermediates(D.w, 1, k, D.ws, D.ws_bytes)
+        h = d2h(hp, (R, I), np.float32)
+        hq = d2h(hqp, (R, I), np.uint8)
+        hs = d2h(hsp, (R, I // 128), np.float32)
+        for r in range(R):
+            assert rel_l2(h[r], rows_ref[r][0]) <= 1e-5, (call, r)
+            q2, s2 = orc.act_quant(h[r][None, :])
+            assert np.array_equal(hq[r], q2[0]) and np.array_equal(hs[r], s2[0]), (call, r)
+    assert moe.moe_device_status(D.ws) == 0
+    assert moe.moe_device_status(ws2) == 0
 
 
 def test_verify_t32_full_shapes():
