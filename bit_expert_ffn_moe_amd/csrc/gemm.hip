@@ -61,11 +61,27 @@ constexpr int kGThreads = 512;
 constexpr int waitcnt_vm(int n) { return 0xF70 | (n & 0xF) | ((n >> 4) << 14); }
 constexpr int kWaitLgkm0 = 0xC07F;
 
+// Workgroup barrier that is also a compiler barrier for memory accesses: the
+// s_barrier builtin is modelled as touching no memory, so LDS reads could be
+// moved across it; an asm statement with a memory clobber cannot be.  (It
+// waits for nothing: the callers wait for their own loads explicitly.)
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 __device__ __forceinline__ void dma16(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)l, 16, 0, 0);
 }
 __device__ __forceinline__ void dma4(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)l, 4, 0, 0);
+}
+
+// SwiGLU and requantisation in the grouped GEMM's epilogue use the fast
+// exponential and reciprocals: h there already carries the MFMA's own
+// accumulation error (its 128-term sums are not exactly rounded), next to
+// which a few ulp of the SiLU and of v * (1/s) instead of v / s are
+// negligible.  The one-token GEMV keeps the IEEE forms (its h is exact to
+// fp32 rounding).
+__device__ __forceinline__ float silu_mul_fast(float g, float u) {
+  return g * u * __frcp_rn(1.0f + __expf(-g));
 }
 
 __device__ __forceinline__ uint32_t e4m3_1(float v) {
@@ -217,17 +233,28 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
       __syncthreads();
     }
 
-    auto issue = [&](int ks, uint8_t* sA, uint8_t* sB, uint32_t* sS, float* sX) {
+    // The K steps of a tile run in rotated order, from step ks0 round to
+    // ks0 - 1: weight rows H bytes apart (a power of two) read in lockstep
+    // at one K offset by the neighbouring tiles of an XCD land on few HBM
+    // channels; starting each tile elsewhere spreads them (the order of the
+    // per-step fp32 sums changes, nothing else).
+    const int ks0 = (int)(((uint32_t)wi * 7u) % (uint32_t)KS);
+    auto kr = [&](int ks) {
+      const int k = ks + ks0;
+      return k >= KS ? k - KS : k;
+    };
+    auto issue = [&](int ks_, uint8_t* sA, uint8_t* sB, uint32_t* sS, float* sX) {
+      const uint32_t ks = (uint32_t)kr(ks_);
 #pragma unroll
-      for (int i = 0; i < NAI; ++i) dma16(baseA + (offA[i] + (uint32_t)ks * 128u), sA + (w * NAI + i) * 1024);
+      for (int i = 0; i < NAI; ++i) dma16(baseA + (offA[i] + ks * 128u), sA + (w * NAI + i) * 1024);
 #pragma unroll
       for (int i = 0; i < NBI; ++i) {
         // B rows >= 128 of a gate+up tile are up rows: uniform per instruction
         const uint8_t* bb = (GU && (w * NBI + i) * 64 >= 128 * (FMT == 1 ? 4 : 8)) ? baseU : baseG;
-        dma16(bb + (offB[i] + (uint32_t)ks * (FMT == 1 ? 64u : 128u)), sB + (w * NBI + i) * 1024);
+        dma16(bb + (offB[i] + ks * (FMT == 1 ? 64u : 128u)), sB + (w * NBI + i) * 1024);
       }
-      if (FMT == 1 && lane < 32) dma4(baseS + (offS + (uint32_t)ks * 4u), sS + w * 32);
-      if (lane < 16) dma4(baseX + (offX + (uint32_t)ks), sX + w * 16);
+      if (FMT == 1 && lane < 32) dma4(baseS + (offS + ks * 4u), sS + w * 32);
+      if (lane < 16) dma4(baseX + (offX + ks), sX + w * 16);
     };
 
     v4f_t acc[4][4];
@@ -240,35 +267,21 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
     // real row, never stored)
     const bool live = nrows > wm * 64;
 
-    auto compute = [&](int ks, const uint8_t* sA, const uint8_t* sB, const uint32_t* sS,
-                       const float* sX) {
-      if (!live) return;
-      v8i_t av[4];
-      float4 xv[4], xs_raw[4];
+    // one K step's operands of this wave, read from a stage into registers
+    v8i_t f_av[4], f_bv[4];
+    int f_sb[4];
+    float4 f_xs[4];
+    auto read_frags = [&](const uint8_t* sA, const uint8_t* sB, const uint32_t* sS,
+                          const float* sX) {
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
         const int r = wm * 64 + 16 * mi + (lane & 15);
         const uint4 a0 = *reinterpret_cast<const uint4*>(sA + sw128(r, q));
         const uint4 a1 = *reinterpret_cast<const uint4*>(sA + sw128(r, q + 4));
-        av[mi] = (v8i_t){(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                         (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        xs_raw[mi] = *reinterpret_cast<const float4*>(sX + wm * 64 + 16 * mi + 4 * q);
+        f_av[mi] = (v8i_t){(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                           (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        f_xs[mi] = *reinterpret_cast<const float4*>(sX + wm * 64 + 16 * mi + 4 * q);
       }
-      // activation scales times the FP8 weight block scale (gate half first)
-      float f1 = 1.0f;
-      if (FMT == 2) {
-        const float f0 = s_wsc[GU ? 0 : (wn >> 1)][ks];
-        f1 = GU ? s_wsc[1][ks] : f0;
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-          xv[mi].x = xs_raw[mi].x * f0, xv[mi].y = xs_raw[mi].y * f0;
-          xv[mi].z = xs_raw[mi].z * f0, xv[mi].w = xs_raw[mi].w * f0;
-        }
-      } else {
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) xv[mi] = xs_raw[mi];
-      }
-      const v4f_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         // sub-tile j: gate+up -- j < 2 gate, j >= 2 up, I-columns
@@ -276,55 +289,81 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
         // 64 wn + 16 j + (lane & 15)
         const int n = GU ? ((j < 2 ? 0 : 128) + 32 * wn + 16 * (j & 1) + (lane & 15))
                          : (64 * wn + 16 * j + (lane & 15));
-        v8i_t bv;
-        int sb = 127;
         if (FMT == 1) {
           const uint4 b0 = *reinterpret_cast<const uint4*>(sB + sw64(n, q));
-          bv = (v8i_t){(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
-          sb = (int)((sS[n] >> (8 * q)) & 0xffu);
+          f_bv[j] = (v8i_t){(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
+          f_sb[j] = (int)((sS[n] >> (8 * q)) & 0xffu);
         } else {
           const uint4 b0 = *reinterpret_cast<const uint4*>(sB + sw128(n, q));
           const uint4 b1 = *reinterpret_cast<const uint4*>(sB + sw128(n, q + 4));
-          bv = (v8i_t){(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
-                       (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-        }
-        if (FMT == 2 && GU && j == 2) {
-          // up half: activation scales times the up block scale
-#pragma unroll
-          for (int mi = 0; mi < 4; ++mi) {
-            xv[mi].x = xs_raw[mi].x * f1, xv[mi].y = xs_raw[mi].y * f1;
-            xv[mi].z = xs_raw[mi].z * f1, xv[mi].w = xs_raw[mi].w * f1;
-          }
-        }
-        v4f_t d[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-          d[mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[mi], bv, zero, 0,
-                                                                   FMT == 1 ? 4 : 0, 0, 127, 0, sb);
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-          acc[mi][j][0] = fmaf(xv[mi].x, d[mi][0], acc[mi][j][0]);
-          acc[mi][j][1] = fmaf(xv[mi].y, d[mi][1], acc[mi][j][1]);
-          acc[mi][j][2] = fmaf(xv[mi].z, d[mi][2], acc[mi][j][2]);
-          acc[mi][j][3] = fmaf(xv[mi].w, d[mi][3], acc[mi][j][3]);
+          f_bv[j] = (v8i_t){(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                            (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+          f_sb[j] = 127;
         }
       }
     };
+    auto mma = [&](int ks) {
+      // activation scales times the FP8 weight block scale (gate / up halves)
+      float f0 = 1.0f, f1 = 1.0f;
+      if (FMT == 2) {
+        f0 = s_wsc[GU ? 0 : (wn >> 1)][kr(ks)];
+        f1 = GU ? s_wsc[1][kr(ks)] : f0;
+      }
+      const v4f_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+      // sub-tile j+1's MFMAs are issued before sub-tile j's scale FMAs, so
+      // the FMAs never wait on a result just issued (two result sets live)
+      v4f_t d[2][4];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        d[0][mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            f_av[mi], f_bv[0], zero, 0, FMT == 1 ? 4 : 0, 0, 127, 0, f_sb[0]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j + 1 < 4) {
+#pragma unroll
+          for (int mi = 0; mi < 4; ++mi)
+            d[(j + 1) & 1][mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                f_av[mi], f_bv[j + 1], zero, 0, FMT == 1 ? 4 : 0, 0, 127, 0, f_sb[j + 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const float fj = (GU && j >= 2) ? f1 : f0;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+          const v4f_t& dd = d[j & 1][mi];
+          acc[mi][j][0] = fmaf(FMT == 2 ? f_xs[mi].x * fj : f_xs[mi].x, dd[0], acc[mi][j][0]);
+          acc[mi][j][1] = fmaf(FMT == 2 ? f_xs[mi].y * fj : f_xs[mi].y, dd[1], acc[mi][j][1]);
+          acc[mi][j][2] = fmaf(FMT == 2 ? f_xs[mi].z * fj : f_xs[mi].z, dd[2], acc[mi][j][2]);
+          acc[mi][j][3] = fmaf(FMT == 2 ? f_xs[mi].w * fj : f_xs[mi].w, dd[3], acc[mi][j][3]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
 
-    // ---- K loop: three stages in separate LDS objects.  Step ks waits for
-    // its stage (the loads of step ks+1 may stay in flight), passes one
-    // barrier -- after which every wave is done with step ks-1's stage --,
-    // issues step ks+2 into that stage, then multiplies. ----
+    // ---- K loop, two wave groups in ping-pong: waves 0-3 (one per SIMD)
+    // and waves 4-7 run half a step apart, so that one group reads its
+    // operands from LDS while the other multiplies from registers.  Per step
+    // ks a wave passes barrier 1, issues the DMA of step ks+2 into the stage
+    // every wave has finished reading, reads stage ks, waits for its own DMA
+    // of step ks+1, passes barrier 2 and multiplies.  Group 1 starts one
+    // barrier late; at every barrier both groups have waited for the DMA of
+    // the stage read next, and the stage refilled next was read by both
+    // before the previous barrier. ----
+    const bool grp1 = w >= 4;
     issue(0, sA0, sB0, sS0, sX0);
     if (KS > 1) issue(1, sA1, sB1, sS1, sX1);
+    if (KS > 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    if (grp1) block_barrier();
 #define BEF_GEMM_STEP(KS_, SA, SB, SS, SX, NA, NB_, NS, NX)                   \
     {                                                                        \
-      if ((KS_) + 1 < KS) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads));    \
-      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                        \
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);                                \
-      __builtin_amdgcn_s_barrier();                                          \
+      block_barrier();                                                       \
       if ((KS_) + 2 < KS) issue((KS_) + 2, NA, NB_, NS, NX);                 \
-      compute((KS_), SA, SB, SS, SX);                                        \
+      if (live) read_frags(SA, SB, SS, SX);                                  \
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);                                \
+      if ((KS_) + 2 < KS) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads));    \
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                        \
+      block_barrier();                                                       \
+      if (live) mma((KS_));                                                  \
     }
     for (int ks = 0; ks < KS; ks += 3) {
       BEF_GEMM_STEP(ks, sA0, sB0, sS0, sX0, sA2, sB2, sS2, sX2)
@@ -334,8 +373,9 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
       BEF_GEMM_STEP(ks + 2, sA2, sB2, sS2, sX2, sA1, sB1, sS1, sX1)
     }
 #undef BEF_GEMM_STEP
+    if (!grp1) block_barrier();
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
+    block_barrier();
 
     if (GU) {
       // ---- epilogue: h = silu(g) * u, per-row amax over the tile's 128
@@ -347,7 +387,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            hv[mi][jj][v] = silu_mul_accurate(acc[mi][jj][v], acc[mi][jj + 2][v]);
+            hv[mi][jj][v] = silu_mul_fast(acc[mi][jj][v], acc[mi][jj + 2][v]);
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -367,10 +407,11 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
           const int R = wm * 64 + 16 * mi + 4 * q + v;
           const float am = fmaxf(fmaxf(s_amax[0][R], s_amax[1][R]), fmaxf(s_amax[2][R], s_amax[3][R]));
           const float sc = am / 448.0f;
+          const float rsc = __frcp_rn(sc);
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
             const int col = 32 * wn + 16 * jj + (lane & 15);
-            s_out[R * 128 + col] = (uint8_t)((am != 0.0f) ? e4m3_1(hv[mi][jj][v] / sc) : 0u);
+            s_out[R * 128 + col] = (uint8_t)((am != 0.0f) ? e4m3_1(hv[mi][jj][v] * rsc) : 0u);
           }
           if (wn == 0 && (lane & 15) == 0 && R < nrows)
             a.hs[(size_t)(row0 + R) * I128 + nb] = sc;
