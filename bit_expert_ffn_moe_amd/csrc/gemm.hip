@@ -53,8 +53,6 @@ namespace bef {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* glb_ptr_t;
 
-constexpr int kTM = 128;      // tokens per tile
-constexpr int kTN = 256;      // output columns per tile
 constexpr int kGThreads = 512;
 
 // s_waitcnt immediates (gfx9: vmcnt [3:0] + [15:14], expcnt [6:4], lgkmcnt [11:8])
@@ -94,50 +92,64 @@ __device__ __forceinline__ uint32_t e4m3_1(float v) {
 __device__ __forceinline__ int sw128(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 __device__ __forceinline__ int sw64(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 
-template <int FMT>
-struct StageBytes {
-  static constexpr int kB = FMT == 1 ? kTN * 64 : kTN * 128;
-};
+// ---------------------------------------------------------------------------
+// The kernel.  Tile: 256 weight rows (gate+up: rows nb*128 .. +127 of W_gate
+// then the same rows of W_up; down: rows nb*256 .. +255 of W_down) x 256
+// tokens of one group.  The product is taken transposed, D[n][t] =
+// sum_k W[n][k] X[t][k]: the weights are the MFMA's A operand (FP4 with its
+// UE8M0 scale as the hardware A scale, or FP8), the activations its B
+// operand, so a lane holds 4 consecutive weight rows of one token and the
+// token's activation scale is one value per lane.  8 waves as 2 (weight
+// rows) x 4 (tokens), 128 x 64 outputs each: weight fragments i = 0..7 are,
+// for gate+up, gate rows 64 wn + 16 i (i < 4) and the same up rows (i >= 4),
+// so SwiGLU pairs stay in one lane; for down, rows 128 wn + 16 i.
+// ---------------------------------------------------------------------------
+constexpr int kTN2 = 256;   // weight rows per tile
 
-// GU = gate+up (+SwiGLU, requant of h), else down.
-template <int FMT, bool GU>
+// TM = tokens per tile (256, or 128 when groups are small): wave tile 128
+// weight rows x TM/4 tokens.
+template <int FMT, bool GU, int TM>
 __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
-  constexpr int KB = StageBytes<FMT>::kB;
-  constexpr int NAI = 2;                 // A DMA instructions per wave per K step
-  constexpr int NBI = FMT == 1 ? 2 : 4;  // B DMA instructions per wave per K step
-  constexpr int kLoads = NAI + NBI + (FMT == 1 ? 2 : 1);  // DMA instructions per wave per stage
-  __shared__ __align__(16) uint8_t sA0[kTM * 128];
-  __shared__ __align__(16) uint8_t sA1[kTM * 128];
-  __shared__ __align__(16) uint8_t sA2[kTM * 128];
-  __shared__ __align__(16) uint8_t sB0[KB];
-  __shared__ __align__(16) uint8_t sB1[KB];
-  __shared__ __align__(16) uint8_t sB2[KB];
-  __shared__ __align__(16) uint32_t sS0[FMT == 1 ? kTN : 1];  // FP4: 4 UE8M0 bytes per B row
-  __shared__ __align__(16) uint32_t sS1[FMT == 1 ? kTN : 1];
-  __shared__ __align__(16) uint32_t sS2[FMT == 1 ? kTN : 1];
-  __shared__ __align__(16) float sX0[kTM];  // activation scales of the K step
-  __shared__ __align__(16) float sX1[kTM];
-  __shared__ __align__(16) float sX2[kTM];
-  __shared__ float s_amax[4][kTM];
+  constexpr int NT = TM / 64;                              // token fragments per wave
+  constexpr int KB_A = TM * 128;                           // E4M3 activations per K step
+  constexpr int KB_B = FMT == 1 ? kTN2 * 64 : kTN2 * 128;  // weight codes per K step
+  constexpr int NST = (FMT == 2 && TM == 256) ? 2 : 3;     // stages (LDS: 160 KB per CU)
+  constexpr int XL = TM / 8;                               // act-scale DMA lanes per wave
+  constexpr int NAI = KB_A / 8192;                         // A DMA instructions per wave
+  constexpr int NBI = KB_B / 8192;                         // B DMA instructions per wave
+  constexpr int kLoads = NAI + NBI + (FMT == 1 ? 1 : 0) + 1;  // + FP4 scales + act scales
+  __shared__ __align__(16) uint8_t sA0[KB_A];
+  __shared__ __align__(16) uint8_t sA1[KB_A];
+  __shared__ __align__(16) uint8_t sA2[NST > 2 ? KB_A : 16];
+  __shared__ __align__(16) uint8_t sB0[KB_B];
+  __shared__ __align__(16) uint8_t sB1[KB_B];
+  __shared__ __align__(16) uint8_t sB2[NST > 2 ? KB_B : 16];
+  __shared__ __align__(16) uint32_t sS0[FMT == 1 ? kTN2 : 4];  // FP4: 4 UE8M0 bytes per weight row
+  __shared__ __align__(16) uint32_t sS1[FMT == 1 ? kTN2 : 4];
+  __shared__ __align__(16) uint32_t sS2[FMT == 1 && NST > 2 ? kTN2 : 4];
+  __shared__ __align__(16) float sX0[TM];  // activation scales of the K step
+  __shared__ __align__(16) float sX1[TM];
+  __shared__ __align__(16) float sX2[NST > 2 ? TM : 4];
+  __shared__ float s_amax[2][TM];
   __shared__ float s_wsc[2][64];  // FP8 weight block scales of the tile, per K step
-  __shared__ int s_mtp[258];  // m-tile prefix per group
-  __shared__ int s_tok[kTM];
+  __shared__ int s_mtp[258];      // m-tile prefix per group
+  __shared__ int s_tok[TM];
   __shared__ int stmp[kGThreads / 64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w & 1, wn = w >> 1, q = lane >> 4;  // 2 (M) x 4 (N) waves of 64 x 64
+  const int wn = w & 1, wt = w >> 1, q = lane >> 4;
   const int E = a.E, H = a.H, I = a.I;
   const int K = GU ? H : I;  // contraction length
   const int KS = K >> 7;
-  const int NB = GU ? (I >> 7) : (H / kTN);  // N-blocks per M-tile
+  const int NB = GU ? (I >> 7) : (H / kTN2);  // N-blocks per M-tile
 
   // m-tiles per group and their exclusive prefix (groups 0..E, E = shared)
   {
     int my_mt = 0;
     if (tid <= E) {
       const int c = a.offsets[tid + 1] - a.offsets[tid];
-      my_mt = (c + kTM - 1) / kTM;
+      my_mt = (c + TM - 1) / TM;
     }
     int inc = my_mt;
 #pragma unroll
@@ -170,17 +182,16 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
       const int mid = (lo + hi) >> 1;
       if (s_mtp[mid] <= mtg) lo = mid + 1; else hi = mid;
     }
-    // block-uniform values in scalar registers (scalar loads of the scales)
     const int g = __builtin_amdgcn_readfirstlane(lo - 1);
-    const int row0 = __builtin_amdgcn_readfirstlane(a.offsets[g] + (mtg - s_mtp[g]) * kTM);
-    const int nrows = __builtin_amdgcn_readfirstlane(min(kTM, a.offsets[g + 1] - row0));
+    const int row0 = __builtin_amdgcn_readfirstlane(a.offsets[g] + (mtg - s_mtp[g]) * TM);
+    const int nrows = __builtin_amdgcn_readfirstlane(min(TM, a.offsets[g + 1] - row0));
     if (GU) {
-      for (int i = tid; i < kTM; i += kGThreads) s_tok[i] = a.row_token[row0 + min(i, nrows - 1)];
+      for (int i = tid; i < TM; i += kGThreads) s_tok[i] = a.row_token[row0 + min(i, nrows - 1)];
       __syncthreads();
     }
 
-    // ---- DMA sources of this tile (K offset 0): a wave-uniform 64-bit base
-    // (scalar registers) and a 32-bit per-lane offset ----
+    // ---- DMA sources of this tile (K offset 0): a wave-uniform base and a
+    // 32-bit per-lane offset ----
     const uint8_t* baseA = GU ? a.xq : a.hq + (size_t)row0 * I;
     uint32_t offA[NAI];
 #pragma unroll
@@ -190,12 +201,10 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
       offA[i] = (GU ? (uint32_t)s_tok[rr] * (uint32_t)H : (uint32_t)rr * (uint32_t)I) + 16u * c;
     }
     const uint32_t brow_bytes = FMT == 1 ? (uint32_t)(K >> 1) : (uint32_t)K;
-    // B row r of the tile: gate rows 0..127 and up rows 128..255 of I-block
-    // nb (gate+up), or rows nb*256 + r of W_down (down)
     const size_t rows_per_expert = GU ? (size_t)I : (size_t)H;
     const uint8_t* baseG = (GU ? a.gq : a.dq) + (size_t)g * rows_per_expert * brow_bytes;
     const uint8_t* baseU = (GU ? a.uq : a.dq) + (size_t)g * rows_per_expert * brow_bytes;
-    const uint32_t row_base = GU ? (uint32_t)nb * 128u : (uint32_t)nb * kTN;
+    const uint32_t row_base = GU ? (uint32_t)nb * 128u : (uint32_t)nb * kTN2;
     uint32_t offB[NBI];
 #pragma unroll
     for (int i = 0; i < NBI; ++i) {
@@ -204,7 +213,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
       const int c = FMT == 1 ? ((p & 3) ^ ((r >> 2) & 3)) : ((p & 7) ^ ((r >> 1) & 7));
       offB[i] = (row_base + (uint32_t)(GU ? (r & 127) : r)) * brow_bytes + 16u * c;
     }
-    // FP4 scales: B row w*32 + lane (lanes < 32; uniform matrix per wave)
+    // FP4 scales: weight row w*32 + lane (lanes < 32; gate rows are waves 0-3)
     const uint32_t sbytes = (uint32_t)(K >> 5);
     const uint8_t* baseS = nullptr;
     uint32_t offS = 0;
@@ -214,15 +223,15 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
       const int r = w * 32 + (lane & 31);
       offS = (row_base + (uint32_t)(GU ? (r & 127) : r)) * sbytes;
     }
-    // activation scales: A row w*16 + lane (lanes < 16)
+    // activation scales: token w*XL + lane (lanes < XL)
     const float* baseX = GU ? a.xs : a.hs + (size_t)row0 * KS;
     uint32_t offX;
     {
-      const int rr = min(w * 16 + (lane & 15), nrows - 1);
+      const int rr = min(w * XL + (lane & (XL - 1)), nrows - 1);
       offX = (GU ? (uint32_t)s_tok[rr] : (uint32_t)rr) * (uint32_t)KS;
     }
     // FP8 weight block scales of the tile into LDS, once: [0] gate (GU) or
-    // columns 0..127 (down), [1] up (GU) or columns 128..255 (down)
+    // rows 0..127 (down), [1] up (GU) or rows 128..255 (down)
     if (FMT == 2) {
       for (int t = tid; t < 2 * KS; t += kGThreads) {
         const int hsel = t >= KS, ks = t - hsel * KS;
@@ -249,175 +258,173 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
       for (int i = 0; i < NAI; ++i) dma16(baseA + (offA[i] + ks * 128u), sA + (w * NAI + i) * 1024);
 #pragma unroll
       for (int i = 0; i < NBI; ++i) {
-        // B rows >= 128 of a gate+up tile are up rows: uniform per instruction
+        // weight rows >= 128 of a gate+up tile are up rows: uniform per instruction
         const uint8_t* bb = (GU && (w * NBI + i) * 64 >= 128 * (FMT == 1 ? 4 : 8)) ? baseU : baseG;
         dma16(bb + (offB[i] + ks * (FMT == 1 ? 64u : 128u)), sB + (w * NBI + i) * 1024);
       }
       if (FMT == 1 && lane < 32) dma4(baseS + (offS + ks * 4u), sS + w * 32);
-      if (lane < 16) dma4(baseX + (offX + ks), sX + w * 16);
+      if (lane < XL) dma4(baseX + (offX + ks), sX + w * XL);
     };
 
-    v4f_t acc[4][4];
+    v4f_t acc[8][NT];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[mi][j] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
-    // a wave whose 64 rows hold no token skips the multiplies (the rows of a
-    // partly filled 64-row band are multiplied anyway: clamped copies of a
-    // real row, never stored)
-    const bool live = nrows > wm * 64;
+      for (int ti = 0; ti < NT; ++ti) acc[i][ti] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
+    // a wave whose 64 tokens are all past the group's rows skips the
+    // multiplies (the tokens of a partly filled band are multiplied anyway:
+    // clamped copies of a real row, never stored)
+    const bool live = nrows > wt * (TM / 4);
+    auto wrow = [&](int i) {
+      return GU ? ((i < 4 ? 0 : 128) + 64 * wn + 16 * (i & 3) + (lane & 15))
+                : (128 * wn + 16 * i + (lane & 15));
+    };
 
-    // one K step's operands of this wave, read from a stage into registers
-    v8i_t f_av[4], f_bv[4];
-    int f_sb[4];
-    float4 f_xs[4];
-    auto read_frags = [&](const uint8_t* sA, const uint8_t* sB, const uint32_t* sS,
-                          const float* sX) {
+    auto compute = [&](int ks, const uint8_t* sA, const uint8_t* sB, const uint32_t* sS,
+                       const float* sX) {
+      if (!live) return;
+      // the wave's 4 token fragments and their activation scales (times the
+      // FP8 weight block scale: gate / up halves)
+      v8i_t tv[NT];
+      float cx[NT], cy[NT];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int r = wm * 64 + 16 * mi + (lane & 15);
+      for (int ti = 0; ti < NT; ++ti) {
+        const int r = wt * (TM / 4) + 16 * ti + (lane & 15);
         const uint4 a0 = *reinterpret_cast<const uint4*>(sA + sw128(r, q));
         const uint4 a1 = *reinterpret_cast<const uint4*>(sA + sw128(r, q + 4));
-        f_av[mi] = (v8i_t){(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                           (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        f_xs[mi] = *reinterpret_cast<const float4*>(sX + wm * 64 + 16 * mi + 4 * q);
+        tv[ti] = (v8i_t){(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                         (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        const float x = sX[r];
+        cx[ti] = x;
+        cy[ti] = x;
       }
+      if (FMT == 2) {
+        const float f0 = s_wsc[GU ? 0 : wn][kr(ks)];
+        const float f1 = GU ? s_wsc[1][kr(ks)] : f0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // sub-tile j: gate+up -- j < 2 gate, j >= 2 up, I-columns
-        // 32 wn + 16 (j & 1) + (lane & 15) of the block; down -- H-columns
-        // 64 wn + 16 j + (lane & 15)
-        const int n = GU ? ((j < 2 ? 0 : 128) + 32 * wn + 16 * (j & 1) + (lane & 15))
-                         : (64 * wn + 16 * j + (lane & 15));
+        for (int ti = 0; ti < NT; ++ti) {
+          cy[ti] = cx[ti] * f1;
+          cx[ti] = cx[ti] * f0;
+        }
+      }
+      auto read_w = [&](int i, v8i_t& wv, int& sw) {
+        const int n = wrow(i);
         if (FMT == 1) {
           const uint4 b0 = *reinterpret_cast<const uint4*>(sB + sw64(n, q));
-          f_bv[j] = (v8i_t){(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
-          f_sb[j] = (int)((sS[n] >> (8 * q)) & 0xffu);
+          wv = (v8i_t){(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
+          sw = (int)((sS[n] >> (8 * q)) & 0xffu);
         } else {
           const uint4 b0 = *reinterpret_cast<const uint4*>(sB + sw128(n, q));
           const uint4 b1 = *reinterpret_cast<const uint4*>(sB + sw128(n, q + 4));
-          f_bv[j] = (v8i_t){(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
-                            (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-          f_sb[j] = 127;
+          wv = (v8i_t){(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                       (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+          sw = 127;
         }
-      }
-    };
-    auto mma = [&](int ks) {
-      // activation scales times the FP8 weight block scale (gate / up halves)
-      float f0 = 1.0f, f1 = 1.0f;
-      if (FMT == 2) {
-        f0 = s_wsc[GU ? 0 : (wn >> 1)][kr(ks)];
-        f1 = GU ? s_wsc[1][kr(ks)] : f0;
-      }
+      };
       const v4f_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-      // sub-tile j+1's MFMAs are issued before sub-tile j's scale FMAs, so
-      // the FMAs never wait on a result just issued (two result sets live)
-      v4f_t d[2][4];
+      v8i_t wv[2];
+      int sw[2];
+      read_w(0, wv[0], sw[0]);
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        d[0][mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            f_av[mi], f_bv[0], zero, 0, FMT == 1 ? 4 : 0, 0, 127, 0, f_sb[0]);
+      for (int i = 0; i < 8; ++i) {
+        // fragment i+1 is read while fragment i multiplies
+        if (i + 1 < 8) read_w(i + 1, wv[(i + 1) & 1], sw[(i + 1) & 1]);
+        v4f_t d[NT];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (j + 1 < 4) {
+        for (int ti = 0; ti < NT; ++ti)
+          d[ti] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              wv[i & 1], tv[ti], zero, FMT == 1 ? 4 : 0, 0, 0, sw[i & 1], 0, 127);
 #pragma unroll
-          for (int mi = 0; mi < 4; ++mi)
-            d[(j + 1) & 1][mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                f_av[mi], f_bv[j + 1], zero, 0, FMT == 1 ? 4 : 0, 0, 127, 0, f_sb[j + 1]);
+        for (int ti = 0; ti < NT; ++ti) {
+          const float c = (GU && i >= 4) ? cy[ti] : cx[ti];
+          acc[i][ti][0] = fmaf(c, d[ti][0], acc[i][ti][0]);
+          acc[i][ti][1] = fmaf(c, d[ti][1], acc[i][ti][1]);
+          acc[i][ti][2] = fmaf(c, d[ti][2], acc[i][ti][2]);
+          acc[i][ti][3] = fmaf(c, d[ti][3], acc[i][ti][3]);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        const float fj = (GU && j >= 2) ? f1 : f0;
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-          const v4f_t& dd = d[j & 1][mi];
-          acc[mi][j][0] = fmaf(FMT == 2 ? f_xs[mi].x * fj : f_xs[mi].x, dd[0], acc[mi][j][0]);
-          acc[mi][j][1] = fmaf(FMT == 2 ? f_xs[mi].y * fj : f_xs[mi].y, dd[1], acc[mi][j][1]);
-          acc[mi][j][2] = fmaf(FMT == 2 ? f_xs[mi].z * fj : f_xs[mi].z, dd[2], acc[mi][j][2]);
-          acc[mi][j][3] = fmaf(FMT == 2 ? f_xs[mi].w * fj : f_xs[mi].w, dd[3], acc[mi][j][3]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
       }
     };
 
-    // ---- K loop, two wave groups in ping-pong: waves 0-3 (one per SIMD)
-    // and waves 4-7 run half a step apart, so that one group reads its
-    // operands from LDS while the other multiplies from registers.  Per step
-    // ks a wave passes barrier 1, issues the DMA of step ks+2 into the stage
-    // every wave has finished reading, reads stage ks, waits for its own DMA
-    // of step ks+1, passes barrier 2 and multiplies.  Group 1 starts one
-    // barrier late; at every barrier both groups have waited for the DMA of
-    // the stage read next, and the stage refilled next was read by both
-    // before the previous barrier. ----
-    const bool grp1 = w >= 4;
+    // ---- K loop: NST stages in separate LDS objects.  Step ks waits for
+    // its own DMA of stage ks, passes a barrier -- after which the stage is
+    // complete and every wave is done with step ks-1 --, issues step
+    // ks+NST-1 into step ks-1's stage, then multiplies. ----
     issue(0, sA0, sB0, sS0, sX0);
-    if (KS > 1) issue(1, sA1, sB1, sS1, sX1);
-    if (KS > 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    if (grp1) block_barrier();
-#define BEF_GEMM_STEP(KS_, SA, SB, SS, SX, NA, NB_, NS, NX)                   \
-    {                                                                        \
-      block_barrier();                                                       \
-      if ((KS_) + 2 < KS) issue((KS_) + 2, NA, NB_, NS, NX);                 \
-      if (live) read_frags(SA, SB, SS, SX);                                  \
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);                                \
-      if ((KS_) + 2 < KS) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads));    \
-      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                        \
-      block_barrier();                                                       \
-      if (live) mma((KS_));                                                  \
+    if (NST > 2 && KS > 1) issue(1, sA1, sB1, sS1, sX1);
+#define BEF_GEMM_STEP(KS_, SA, SB, SS, SX, NA, NB_, NS, NX)                     \
+    {                                                                          \
+      if ((KS_) + NST - 2 < KS && NST > 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads)); \
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                          \
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);                                  \
+      block_barrier();                                                         \
+      if ((KS_) + NST - 1 < KS) issue((KS_) + NST - 1, NA, NB_, NS, NX);       \
+      compute((KS_), SA, SB, SS, SX);                                          \
     }
-    for (int ks = 0; ks < KS; ks += 3) {
-      BEF_GEMM_STEP(ks, sA0, sB0, sS0, sX0, sA2, sB2, sS2, sX2)
-      if (ks + 1 >= KS) break;
-      BEF_GEMM_STEP(ks + 1, sA1, sB1, sS1, sX1, sA0, sB0, sS0, sX0)
-      if (ks + 2 >= KS) break;
-      BEF_GEMM_STEP(ks + 2, sA2, sB2, sS2, sX2, sA1, sB1, sS1, sX1)
+    if (NST > 2) {
+      for (int ks = 0; ks < KS; ks += 3) {
+        BEF_GEMM_STEP(ks, sA0, sB0, sS0, sX0, sA2, sB2, sS2, sX2)
+        if (ks + 1 >= KS) break;
+        BEF_GEMM_STEP(ks + 1, sA1, sB1, sS1, sX1, sA0, sB0, sS0, sX0)
+        if (ks + 2 >= KS) break;
+        BEF_GEMM_STEP(ks + 2, sA2, sB2, sS2, sX2, sA1, sB1, sS1, sX1)
+      }
+    } else {
+      for (int ks = 0; ks < KS; ks += 2) {
+        BEF_GEMM_STEP(ks, sA0, sB0, sS0, sX0, sA1, sB1, sS1, sX1)
+        if (ks + 1 >= KS) break;
+        BEF_GEMM_STEP(ks + 1, sA1, sB1, sS1, sX1, sA0, sB0, sS0, sX0)
+      }
     }
 #undef BEF_GEMM_STEP
-    if (!grp1) block_barrier();
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     block_barrier();
 
     if (GU) {
-      // ---- epilogue: h = silu(g) * u, per-row amax over the tile's 128
-      // columns of I, E4M3 codes and scale (the act_quant rule) ----
-      float hv[4][2][4];
+      // ---- epilogue: h = silu(g) * u for the lane's token (16 ti + lane%16)
+      // and h columns 64 wn + 16 i + 4 q + v; per-token amax over the tile's
+      // 128 columns (4 lanes of a column group, then the 2 column waves),
+      // E4M3 codes and scale (the act_quant rule) ----
+      // h overwrites the gate accumulators: acc[i][ti][v], i < 4
+      float m[NT];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int ti = 0; ti < NT; ++ti) m[ti] = 0.0f;
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            hv[mi][jj][v] = silu_mul_fast(acc[mi][jj][v], acc[mi][jj + 2][v]);
+        for (int ti = 0; ti < NT; ++ti)
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+          for (int v = 0; v < 4; ++v) {
+            acc[i][ti][v] = silu_mul_fast(acc[i][ti][v], acc[i + 4][ti][v]);
+            m[ti] = fmaxf(m[ti], fabsf(acc[i][ti][v]));
+          }
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float m = fmaxf(fabsf(hv[mi][0][v]), fabsf(hv[mi][1][v]));
-          m = group_max<16>(m);
-          const int R = wm * 64 + 16 * mi + 4 * q + v;
-          if ((lane & 15) == 0) s_amax[wn][R] = m;
-        }
+      for (int ti = 0; ti < NT; ++ti) {
+        m[ti] = fmaxf(m[ti], __shfl_xor(m[ti], 16, kWave));
+        m[ti] = fmaxf(m[ti], __shfl_xor(m[ti], 32, kWave));
+        if (q == 0) s_amax[wn][wt * (TM / 4) + 16 * ti + lane] = m[ti];
+      }
       __syncthreads();
-      uint8_t* s_out = sA0;
+      uint8_t* s_out = sA0;  // [token][128 codes]
       const int I128 = I >> 7;
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int ti = 0; ti < NT; ++ti) {
+        const int t = wt * (TM / 4) + 16 * ti + (lane & 15);
+        const float am = fmaxf(s_amax[0][t], s_amax[1][t]);
+        const float sc = am / 448.0f;
+        const float rsc = __frcp_rn(sc);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int R = wm * 64 + 16 * mi + 4 * q + v;
-          const float am = fmaxf(fmaxf(s_amax[0][R], s_amax[1][R]), fmaxf(s_amax[2][R], s_amax[3][R]));
-          const float sc = am / 448.0f;
-          const float rsc = __frcp_rn(sc);
+        for (int i = 0; i < 4; ++i) {
+          uint32_t cw = 0;
+          if (am != 0.0f) {
 #pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int col = 32 * wn + 16 * jj + (lane & 15);
-            s_out[R * 128 + col] = (uint8_t)((am != 0.0f) ? e4m3_1(hv[mi][jj][v] * rsc) : 0u);
+            for (int v = 0; v < 4; ++v) cw |= e4m3_1(acc[i][ti][v] * rsc) << (8 * v);
           }
-          if (wn == 0 && (lane & 15) == 0 && R < nrows)
-            a.hs[(size_t)(row0 + R) * I128 + nb] = sc;
+          *reinterpret_cast<uint32_t*>(&s_out[t * 128 + 64 * wn + 16 * i + 4 * q]) = cw;
         }
+        if (wn == 0 && q == 0 && t < nrows) a.hs[(size_t)(row0 + t) * I128 + nb] = sc;
+      }
       __syncthreads();
-      for (int t = tid; t < kTM * 8; t += kGThreads) {
+      for (int t = tid; t < TM * 8; t += kGThreads) {
         const int R = t >> 3, c16 = t & 7;
         if (R < nrows)
           *reinterpret_cast<uint4*>(a.hq + (size_t)(row0 + R) * I + nb * 128 + 16 * c16) =
@@ -426,16 +433,16 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
       __syncthreads();
     } else {
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int ti = 0; ti < NT; ++ti) {
+        const int t = wt * (TM / 4) + 16 * ti + (lane & 15);
+        if (live && t < nrows) {
+          float* yp = a.y_rows + (size_t)(row0 + t) * H + nb * kTN2 + 128 * wn + 4 * q;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int R = wm * 64 + 16 * mi + 4 * q + v;
-          if (R < nrows) {
-            float* yp = a.y_rows + (size_t)(row0 + R) * H + nb * kTN + 64 * wn + (lane & 15);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) yp[16 * j] = acc[mi][j][v];
-          }
+          for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<float4*>(yp + 16 * i) =
+                make_float4(acc[i][ti][0], acc[i][ti][1], acc[i][ti][2], acc[i][ti][3]);
         }
+      }
     }
   }
 }
@@ -460,26 +467,29 @@ static int grid_blocks() {
   return g_cu_count[dev];
 }
 
-template <int FMT, bool GU>
+template <int FMT, bool GU, int TM>
 static hipError_t launch_g(const GemmArgs& a, hipStream_t st) {
-  if (a.E + 1 > 257 || (GU ? (a.I % 128) : (a.H % kTN)) != 0) return hipErrorInvalidValue;
+  if (a.E + 1 > 257 || (GU ? (a.I % 128) : (a.H % kTN2)) != 0) return hipErrorInvalidValue;
   const KernelTimer& tm = g_kernel_timer[MOE_KERNEL_GEMM_GATE_UP];
   if (GU && tm.start)
-    hipExtLaunchKernelGGL(gemm_kernel<FMT, GU>, dim3(grid_blocks()), dim3(kGThreads), 0, st,
+    hipExtLaunchKernelGGL(gemm_kernel<FMT, GU, TM>, dim3(grid_blocks()), dim3(kGThreads), 0, st,
                           tm.start, tm.stop, 0, a);
   else
-    gemm_kernel<FMT, GU><<<dim3(grid_blocks()), dim3(kGThreads), 0, st>>>(a);
+    gemm_kernel<FMT, GU, TM><<<dim3(grid_blocks()), dim3(kGThreads), 0, st>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_gate_up(const GemmArgs& a, hipStream_t st) {
-  if (a.fmt == 1) return launch_g<1, true>(a, st);
-  return launch_g<2, true>(a, st);
+// 256-token tiles when the routed groups average at least 128 rows (each
+// expert's weights then stream once for all of its tokens), else 128.
+template <bool GU>
+static hipError_t launch_gg(const GemmArgs& a, hipStream_t st) {
+  const bool big = (int64_t)a.T * a.k >= (int64_t)128 * a.E;
+  if (a.fmt == 1) return big ? launch_g<1, GU, 256>(a, st) : launch_g<1, GU, 128>(a, st);
+  return big ? launch_g<2, GU, 256>(a, st) : launch_g<2, GU, 128>(a, st);
 }
 
-hipError_t launch_gemm_down(const GemmArgs& a, hipStream_t st) {
-  if (a.fmt == 1) return launch_g<1, false>(a, st);
-  return launch_g<2, false>(a, st);
-}
+hipError_t launch_gemm_gate_up(const GemmArgs& a, hipStream_t st) { return launch_gg<true>(a, st); }
+
+hipError_t launch_gemm_down(const GemmArgs& a, hipStream_t st) { return launch_gg<false>(a, st); }
 
 }  // namespace bef
