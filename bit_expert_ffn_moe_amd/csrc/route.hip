@@ -325,19 +325,22 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Large T: a block owns 32 tokens x all E (<= 256) experts.  Per 64-wide
-// chunk it stages x (as fp32) and the router rows (bf16) in LDS; thread
-// (ty, tx) accumulates tokens 4ty..4ty+3 x experts tx + 32j (j < 8), each in
-// the fixed order.  The block's logits then go through LDS to 4 waves that
-// run the top-k, 8 tokens each.
+// Large T: a block owns 32 tokens x all E (<= 256) experts, 4 waves.  Per
+// 64-row chunk the router rows go to LDS converted to fp32 (each element
+// once per block) and x as fp32; thread (ty, tx) accumulates tokens
+// 4ty..4ty+3 x experts 8tx..8tx+7, each in the fixed order, reading its 8
+// experts with two 16-byte LDS reads and x four rows at a time.  The next
+// chunk's rows are loaded into registers while the current one multiplies.
+// The block's logits then go through LDS to 4 waves that run the top-k, 8
+// tokens each.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void route_tile_kernel(const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ wr, int T,
                                                          int H, int E, int k,
                                                          int32_t* __restrict__ ids,
                                                          float* __restrict__ w) {
-  __shared__ float sx[32][65];
-  __shared__ uint16_t sw[64][256];
+  __shared__ __align__(16) float sx[32][68];    // [token][h of the chunk], padded rows
+  __shared__ __align__(16) float sw[64][256];   // [h of the chunk][expert]
   __shared__ float sz[32][257];
   const int t0 = blockIdx.x * 32;
   const int tid = threadIdx.x;
@@ -348,52 +351,76 @@ __global__ __launch_bounds__(256) void route_tile_kernel(const uint16_t* __restr
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = grp[i][j] = 0.0f;
   const int nc = H / 64;
-  for (int c = 0; c < nc; ++c) {
-    {
-      const int row = tid >> 3, col8 = (tid & 7) * 8;
-      const int t = t0 + row;
-      uint4 r = make_uint4(0, 0, 0, 0);
-      if (t < T) r = *reinterpret_cast<const uint4*>(x + (size_t)t * H + 64 * c + col8);
-      sx[row][col8 + 0] = bf16_to_f32(r.x & 0xffffu);
-      sx[row][col8 + 1] = bf16_to_f32(r.x >> 16);
-      sx[row][col8 + 2] = bf16_to_f32(r.y & 0xffffu);
-      sx[row][col8 + 3] = bf16_to_f32(r.y >> 16);
-      sx[row][col8 + 4] = bf16_to_f32(r.z & 0xffffu);
-      sx[row][col8 + 5] = bf16_to_f32(r.z >> 16);
-      sx[row][col8 + 6] = bf16_to_f32(r.w & 0xffffu);
-      sx[row][col8 + 7] = bf16_to_f32(r.w >> 16);
-    }
-    if (E == 256) {
+  // this thread's share of a chunk: x row tid/8, 8 bf16 at (tid%8)*8; router
+  // 16-byte pieces q = tid + 256 i: row q/32, experts (q%32)*8 .. +7
+  const int xr = tid >> 3, xc = (tid & 7) * 8;
+  const bool xin = t0 + xr < T;
+  uint4 px;
+  uint4 pw[8];
+  auto load_chunk = [&](int c) {
+    px = xin ? *reinterpret_cast<const uint4*>(x + (size_t)(t0 + xr) * H + 64 * c + xc)
+             : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = tid + 256 * i;  // 16-byte chunk: row q/32, 8 experts (q%32)*8..
-        const int h = q >> 5, e8 = (q & 31) * 8;
-        *reinterpret_cast<uint4*>(&sw[h][e8]) =
-            *reinterpret_cast<const uint4*>(wr + (size_t)(64 * c + h) * 256 + e8);
-      }
-    } else {
-      for (int q = tid; q < 64 * 256; q += 256) {
-        const int h = q >> 8, e = q & 255;
-        sw[h][e] = (e < E) ? wr[(size_t)(64 * c + h) * E + e] : (uint16_t)0;
+    for (int i = 0; i < 8; ++i) {
+      const int q = tid + 256 * i, h = q >> 5, e8 = (q & 31) * 8;
+      const uint16_t* src = wr + (size_t)(64 * c + h) * E + e8;
+      if (E == 256) {
+        pw[i] = *reinterpret_cast<const uint4*>(src);
+      } else {
+        uint16_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = (e8 + u < E) ? src[u] : (uint16_t)0;
+        pw[i] = make_uint4(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
+                           v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16));
       }
     }
+  };
+  auto store_chunk = [&]() {
+    float4 f0 = make_float4(bf16_to_f32(px.x & 0xffffu), bf16_to_f32(px.x >> 16),
+                            bf16_to_f32(px.y & 0xffffu), bf16_to_f32(px.y >> 16));
+    float4 f1 = make_float4(bf16_to_f32(px.z & 0xffffu), bf16_to_f32(px.z >> 16),
+                            bf16_to_f32(px.w & 0xffffu), bf16_to_f32(px.w >> 16));
+    *reinterpret_cast<float4*>(&sx[xr][xc]) = f0;
+    *reinterpret_cast<float4*>(&sx[xr][xc + 4]) = f1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = tid + 256 * i, h = q >> 5, e8 = (q & 31) * 8;
+      const uint4 r = pw[i];
+      *reinterpret_cast<float4*>(&sw[h][e8]) =
+          make_float4(bf16_to_f32(r.x & 0xffffu), bf16_to_f32(r.x >> 16),
+                      bf16_to_f32(r.y & 0xffffu), bf16_to_f32(r.y >> 16));
+      *reinterpret_cast<float4*>(&sw[h][e8 + 4]) =
+          make_float4(bf16_to_f32(r.z & 0xffffu), bf16_to_f32(r.z >> 16),
+                      bf16_to_f32(r.w & 0xffffu), bf16_to_f32(r.w >> 16));
+    }
+  };
+  load_chunk(0);
+  for (int c = 0; c < nc; ++c) {
+    store_chunk();
     __syncthreads();
+    if (c + 1 < nc) load_chunk(c + 1);  // in flight while this chunk multiplies
     float p[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) p[i][j] = 0.0f;
-#pragma unroll 4
-    for (int h = 0; h < 64; ++h) {
-      float xv[4], wv[8];
+#pragma unroll 2
+    for (int h4 = 0; h4 < 64; h4 += 4) {
+      float4 xv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xv[i] = sx[4 * ty + i][h];
+      for (int i = 0; i < 4; ++i) xv[i] = *reinterpret_cast<const float4*>(&sx[4 * ty + i][h4]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) wv[j] = bf16_to_f32(sw[h][tx + 32 * j]);
+      for (int hh = 0; hh < 4; ++hh) {
+        const float4 w0 = *reinterpret_cast<const float4*>(&sw[h4 + hh][8 * tx]);
+        const float4 w1 = *reinterpret_cast<const float4*>(&sw[h4 + hh][8 * tx + 4]);
+        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+          const float xs = hh == 0 ? xv[i].x : hh == 1 ? xv[i].y : hh == 2 ? xv[i].z : xv[i].w;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) p[i][j] = fmaf(xv[i], wv[j], p[i][j]);
+          for (int j = 0; j < 8; ++j) p[i][j] = fmaf(xs, wv[j], p[i][j]);
+        }
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -410,7 +437,7 @@ __global__ __launch_bounds__(256) void route_tile_kernel(const uint16_t* __restr
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sz[4 * ty + i][tx + 32 * j] = acc[i][j];
+    for (int j = 0; j < 8; ++j) sz[4 * ty + i][8 * tx + j] = acc[i][j];
   __syncthreads();
   const int wv = tid >> 6;
   for (int tt = wv; tt < 32; tt += 4) {
