@@ -39,7 +39,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // layer call: control | permute scratch (T, E) | router partials (T, H, E) |
 // everything else (needs the weights' shapes).
 struct Layout {
-  size_t ctl, cnt, base, ids, w, xq, xs, offsets, row_token, row_of, active, h, hq, hs, y,
+  size_t ctl, cnt, base, gsum, ids, w, xq, xs, offsets, row_token, row_of, active, h, hq, hs, y,
       total;
   size_t end_permute, end_route, end_ffn;
 };
@@ -61,6 +61,9 @@ Layout layout_for(int E, int H, int I, int T, int k, bool with_h) {
   L.base = o;
   o += up(nblk * E * 4);
   L.end_permute = o;
+  // router group sums for T > kRouteSmallT: [ceil(H/256)][T][E] f32
+  L.gsum = o;
+  if (T > kRouteSmallT) o += up((size_t)((H / 64 + 3) / 4) * T * E * 4);
   L.end_route = o;
   L.ids = o;
   o += up((size_t)T * k * 4);
@@ -279,7 +282,8 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H,
   if (rc) return rc;
   WsCtl* ctl = at<WsCtl>(ws, L.ctl);
   return launch_status(
-      launch_route(x, w_router, T, H, E, k, topk_ids, topk_w, ctl, (hipStream_t)stream));
+      launch_route(x, w_router, T, H, E, k, topk_ids, topk_w, ctl, at<float>(ws, L.gsum),
+                   (hipStream_t)stream));
 }
 
 int act_quant_fp8(const void* x, int32_t x_dtype, int64_t rows, int32_t cols, uint8_t* q,
@@ -471,7 +475,7 @@ int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint1
   if (!ids) {
     int32_t* ids_ws = at<int32_t>(ws, L.ids);
     float* w_ws = at<float>(ws, L.w);
-    rc = launch_status(launch_route(x, w_router, T, H, E, k, ids_ws, w_ws, ctl, st));
+    rc = launch_status(launch_route(x, w_router, T, H, E, k, ids_ws, w_ws, ctl, at<float>(ws, L.gsum), st));
     if (rc) return rc;
     ids = ids_ws;
     tw = w_ws;

@@ -325,32 +325,31 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Large T: a block owns 32 tokens x all E (<= 256) experts, 4 waves.  Per
-// 64-row chunk the router rows go to LDS converted to fp32 (each element
-// once per block) and x as fp32; thread (ty, tx) accumulates tokens
-// 4ty..4ty+3 x experts 8tx..8tx+7, each in the fixed order, reading its 8
-// experts with two 16-byte LDS reads and x four rows at a time.  The next
-// chunk's rows are loaded into registers while the current one multiplies.
-// The block's logits then go through LDS to 4 waves that run the top-k, 8
-// tokens each.
+// T > 4, in two kernels.  route_group_kernel: block (g, tile) owns tokens
+// 32 tile .. +31, all E (<= 256) experts and rows 256 g .. 256 g + 255 (chunks
+// 4g .. 4g+3), 4 waves.  Per 64-row chunk the router rows go to LDS
+// converted to fp32 (each element once per block) and x as fp32; thread
+// (ty, tx) accumulates tokens 4ty..4ty+3 x experts 8tx..8tx+7 in the fixed
+// order (chunk chains from +0 in ascending h, the group's chunks in
+// ascending order), reading its 8 experts with two 16-byte LDS reads and x
+// four rows at a time, while the next chunk's rows load into registers.  It
+// writes the group sums G[g][t][e].  route_reduce_kernel: a block per 4
+// tokens adds the group sums in ascending group order (thread e owns expert
+// e) and one wave per token runs the top-k.  Splitting over H keeps the
+// GPU busy at moderate T (32 tokens: 16 blocks instead of one).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void route_tile_kernel(const uint16_t* __restrict__ x,
-                                                         const uint16_t* __restrict__ wr, int T,
-                                                         int H, int E, int k,
-                                                         int32_t* __restrict__ ids,
-                                                         float* __restrict__ w) {
+__global__ __launch_bounds__(256) void route_group_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ wr, int T,
+                                                          int H, int E,
+                                                          float* __restrict__ gsum) {
   __shared__ __align__(16) float sx[32][68];    // [token][h of the chunk], padded rows
   __shared__ __align__(16) float sw[64][256];   // [h of the chunk][expert]
-  __shared__ float sz[32][257];
-  const int t0 = blockIdx.x * 32;
+  const int g = blockIdx.x, t0 = blockIdx.y * 32;
   const int tid = threadIdx.x;
   const int ty = tid >> 5, tx = tid & 31;
-  float acc[4][8], grp[4][8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = grp[i][j] = 0.0f;
   const int nc = H / 64;
+  const int c0 = 4 * g, c1 = min(4 * g + 4, nc);
+  float grp[4][8];
   // this thread's share of a chunk: x row tid/8, 8 bf16 at (tid%8)*8; router
   // 16-byte pieces q = tid + 256 i: row q/32, experts (q%32)*8 .. +7
   const int xr = tid >> 3, xc = (tid & 7) * 8;
@@ -376,12 +375,12 @@ __global__ __launch_bounds__(256) void route_tile_kernel(const uint16_t* __restr
     }
   };
   auto store_chunk = [&]() {
-    float4 f0 = make_float4(bf16_to_f32(px.x & 0xffffu), bf16_to_f32(px.x >> 16),
-                            bf16_to_f32(px.y & 0xffffu), bf16_to_f32(px.y >> 16));
-    float4 f1 = make_float4(bf16_to_f32(px.z & 0xffffu), bf16_to_f32(px.z >> 16),
-                            bf16_to_f32(px.w & 0xffffu), bf16_to_f32(px.w >> 16));
-    *reinterpret_cast<float4*>(&sx[xr][xc]) = f0;
-    *reinterpret_cast<float4*>(&sx[xr][xc + 4]) = f1;
+    *reinterpret_cast<float4*>(&sx[xr][xc]) =
+        make_float4(bf16_to_f32(px.x & 0xffffu), bf16_to_f32(px.x >> 16),
+                    bf16_to_f32(px.y & 0xffffu), bf16_to_f32(px.y >> 16));
+    *reinterpret_cast<float4*>(&sx[xr][xc + 4]) =
+        make_float4(bf16_to_f32(px.z & 0xffffu), bf16_to_f32(px.z >> 16),
+                    bf16_to_f32(px.w & 0xffffu), bf16_to_f32(px.w >> 16));
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int q = tid + 256 * i, h = q >> 5, e8 = (q & 31) * 8;
@@ -394,11 +393,11 @@ __global__ __launch_bounds__(256) void route_tile_kernel(const uint16_t* __restr
                       bf16_to_f32(r.w & 0xffffu), bf16_to_f32(r.w >> 16));
     }
   };
-  load_chunk(0);
-  for (int c = 0; c < nc; ++c) {
+  load_chunk(c0);
+  for (int c = c0; c < c1; ++c) {
     store_chunk();
     __syncthreads();
-    if (c + 1 < nc) load_chunk(c + 1);  // in flight while this chunk multiplies
+    if (c + 1 < c1) load_chunk(c + 1);  // in flight while this chunk multiplies
     float p[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -425,29 +424,52 @@ __global__ __launch_bounds__(256) void route_tile_kernel(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) grp[i][j] = (c % 4 == 0) ? p[i][j] : grp[i][j] + p[i][j];
-    if (c % 4 == 3 || c == nc - 1) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = (c < 4) ? grp[i][j] : acc[i][j] + grp[i][j];
-    }
+      for (int j = 0; j < 8; ++j) grp[i][j] = (c == c0) ? p[i][j] : grp[i][j] + p[i][j];
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 4 * ty + i;
+    if (t >= T) continue;
+    float* dst = gsum + ((size_t)g * T + t) * E;
+    if (E == 256) {
+      *reinterpret_cast<float4*>(dst + 8 * tx) =
+          make_float4(grp[i][0], grp[i][1], grp[i][2], grp[i][3]);
+      *reinterpret_cast<float4*>(dst + 8 * tx + 4) =
+          make_float4(grp[i][4], grp[i][5], grp[i][6], grp[i][7]);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sz[4 * ty + i][8 * tx + j] = acc[i][j];
-  __syncthreads();
-  const int wv = tid >> 6;
-  for (int tt = wv; tt < 32; tt += 4) {
-    const int t = t0 + tt;
-    if (t < T) topk_wave(sz[tt], E, k, ids + (size_t)t * k, w + (size_t)t * k);
+      for (int j = 0; j < 8; ++j)
+        if (8 * tx + j < E) dst[8 * tx + j] = grp[i][j];
+    }
   }
 }
 
+__global__ __launch_bounds__(256) void route_reduce_kernel(const float* __restrict__ gsum, int T,
+                                                           int H, int E, int k,
+                                                           int32_t* __restrict__ ids,
+                                                           float* __restrict__ w) {
+  __shared__ float sz[4][256];
+  const int t0 = blockIdx.x * 4, tid = threadIdx.x;
+  const int ng = (H / 64 + 3) / 4;
+  const int e = tid;
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int t = t0 + tt;
+    float acc = 0.0f;
+    if (t < T && e < E) {
+      acc = gsum[(size_t)t * E + e];
+      for (int g = 1; g < ng; ++g) acc = acc + gsum[((size_t)g * T + t) * E + e];
+    }
+    sz[tt][e] = acc;
+  }
+  __syncthreads();
+  const int wv = tid >> 6, t = t0 + wv;
+  if (t < T) topk_wave(sz[wv], E, k, ids + (size_t)t * k, w + (size_t)t * k);
+}
+
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int H, int E, int k,
-                        int32_t* ids, float* w, WsCtl* ctl, hipStream_t st) {
+                        int32_t* ids, float* w, WsCtl* ctl, float* gsum, hipStream_t st) {
   if (T <= kRouteSmallT) {
     FrontArgs a = {};
     a.x = x, a.wr = wr, a.T = T, a.H = H, a.E = E, a.k = k;
@@ -455,7 +477,10 @@ hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int H, int
     set_route_sync(a, ctl);
     return launch_route_front(a, st);
   }
-  route_tile_kernel<<<dim3((T + 31) / 32), dim3(256), 0, st>>>(x, wr, T, H, E, k, ids, w);
+  if (!gsum || E > 256 || H % 64 != 0) return hipErrorInvalidValue;
+  const int ng = (H / 64 + 3) / 4;
+  route_group_kernel<<<dim3(ng, (T + 31) / 32), dim3(256), 0, st>>>(x, wr, T, H, E, gsum);
+  route_reduce_kernel<<<dim3((T + 3) / 4), dim3(256), 0, st>>>(gsum, T, H, E, k, ids, w);
   return hipGetLastError();
 }
 

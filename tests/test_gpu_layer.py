@@ -103,7 +103,11 @@ def test_decode_t1_full_shapes_many_tokens():
     assert moe.moe_device_status(D.ws) == 0
     ids = torch.empty((L.wl.T, 6), dtype=torch.int32, device="cuda")
     w = torch.empty((L.wl.T, 6), dtype=torch.float32, device="cuda")
-    moe.moe_route(D.x, D.wr, L.wl.T, 4096, 256, 6, ids, w, D.ws, D.ws_bytes)
+    # the router for all 24 tokens at once: a workspace sized for T = 24
+    rb = moe.moe_workspace_bytes(D.w, L.wl.T, 6)
+    rws = torch.zeros(rb, dtype=torch.uint8, device="cuda")
+    moe.moe_workspace_init(rws, rb)
+    moe.moe_route(D.x, D.wr, L.wl.T, 4096, 256, 6, ids, w, rws, rb)
     ir, _ = orc.route(L.x, L.wr, 6)
     assert np.array_equal(to_host(ids), ir)
 
