@@ -113,23 +113,24 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
   constexpr int NT = TM / 64;                              // token fragments per wave
   constexpr int KB_A = TM * 128;                           // E4M3 activations per K step
   constexpr int KB_B = FMT == 1 ? kTN2 * 64 : kTN2 * 128;  // weight codes per K step
-  constexpr int NST = (FMT == 2 && TM == 256) ? 2 : 3;     // stages (LDS: 160 KB per CU)
+  // stages: as many as fit in ~156 KB of LDS, at most 6
+  constexpr int kStage = KB_A + KB_B + (FMT == 1 ? kTN2 * 4 : 0) + TM * 4;
+  constexpr int NST = (159744 / kStage) > 6 ? 6 : (159744 / kStage);
+  static_assert(NST >= 2, "LDS stages");
   constexpr int XL = TM / 8;                               // act-scale DMA lanes per wave
   constexpr int NAI = KB_A / 8192;                         // A DMA instructions per wave
   constexpr int NBI = KB_B / 8192;                         // B DMA instructions per wave
   constexpr int kLoads = NAI + NBI + (FMT == 1 ? 1 : 0) + 1;  // + FP4 scales + act scales
-  __shared__ __align__(16) uint8_t sA0[KB_A];
-  __shared__ __align__(16) uint8_t sA1[KB_A];
-  __shared__ __align__(16) uint8_t sA2[NST > 2 ? KB_A : 16];
-  __shared__ __align__(16) uint8_t sB0[KB_B];
-  __shared__ __align__(16) uint8_t sB1[KB_B];
-  __shared__ __align__(16) uint8_t sB2[NST > 2 ? KB_B : 16];
-  __shared__ __align__(16) uint32_t sS0[FMT == 1 ? kTN2 : 4];  // FP4: 4 UE8M0 bytes per weight row
-  __shared__ __align__(16) uint32_t sS1[FMT == 1 ? kTN2 : 4];
-  __shared__ __align__(16) uint32_t sS2[FMT == 1 && NST > 2 ? kTN2 : 4];
-  __shared__ __align__(16) float sX0[TM];  // activation scales of the K step
-  __shared__ __align__(16) float sX1[TM];
-  __shared__ __align__(16) float sX2[NST > 2 ? TM : 4];
+  // stage buffers, separate LDS objects (the compiler tracks LDS DMA per
+  // object): activation codes, weight codes, FP4 weight scales (4 UE8M0
+  // bytes per weight row), activation scales of the K step
+#define BEF_STAGE(i)                                                        \
+  __shared__ __align__(16) uint8_t sA##i[NST > i ? KB_A : 16];              \
+  __shared__ __align__(16) uint8_t sB##i[NST > i ? KB_B : 16];              \
+  __shared__ __align__(16) uint32_t sS##i[FMT == 1 && NST > i ? kTN2 : 4];  \
+  __shared__ __align__(16) float sX##i[NST > i ? TM : 4];
+  BEF_STAGE(0) BEF_STAGE(1) BEF_STAGE(2) BEF_STAGE(3) BEF_STAGE(4) BEF_STAGE(5)
+#undef BEF_STAGE
   __shared__ float s_amax[2][TM];
   __shared__ float s_wsc[2][64];  // FP8 weight block scales of the tile, per K step
   __shared__ int s_mtp[258];      // m-tile prefix per group
@@ -345,37 +346,61 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
       }
     };
 
-    // ---- K loop: NST stages in separate LDS objects.  Step ks waits for
-    // its own DMA of stage ks, passes a barrier -- after which the stage is
-    // complete and every wave is done with step ks-1 --, issues step
-    // ks+NST-1 into step ks-1's stage, then multiplies. ----
-    issue(0, sA0, sB0, sS0, sX0);
-    if (NST > 2 && KS > 1) issue(1, sA1, sB1, sS1, sX1);
-#define BEF_GEMM_STEP(KS_, SA, SB, SS, SX, NA, NB_, NS, NX)                     \
-    {                                                                          \
-      if ((KS_) + NST - 2 < KS && NST > 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads)); \
-      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                          \
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);                                  \
-      block_barrier();                                                         \
-      if ((KS_) + NST - 1 < KS) issue((KS_) + NST - 1, NA, NB_, NS, NX);       \
-      compute((KS_), SA, SB, SS, SX);                                          \
-    }
-    if (NST > 2) {
-      for (int ks = 0; ks < KS; ks += 3) {
-        BEF_GEMM_STEP(ks, sA0, sB0, sS0, sX0, sA2, sB2, sS2, sX2)
-        if (ks + 1 >= KS) break;
-        BEF_GEMM_STEP(ks + 1, sA1, sB1, sS1, sX1, sA0, sB0, sS0, sX0)
-        if (ks + 2 >= KS) break;
-        BEF_GEMM_STEP(ks + 2, sA2, sB2, sS2, sX2, sA1, sB1, sS1, sX1)
+    // ---- K loop: NST stages.  Step ks waits for its own DMA of stage ks
+    // (the younger stages' loads may stay in flight), passes a barrier --
+    // after which the stage is complete and every wave is done with step
+    // ks-1 --, issues step ks+NST-1 into step ks-1's stage, then
+    // multiplies. ----
+    struct Stage {
+      uint8_t* a;
+      uint8_t* b;
+      uint32_t* s;
+      float* x;
+    };
+    auto stage = [&](int i) -> Stage {
+      switch (i) {
+        case 0: return {sA0, sB0, sS0, sX0};
+        case 1: return {sA1, sB1, sS1, sX1};
+        case 2: return {sA2, sB2, sS2, sX2};
+        case 3: return {sA3, sB3, sS3, sX3};
+        case 4: return {sA4, sB4, sS4, sX4};
+        default: return {sA5, sB5, sS5, sX5};
       }
-    } else {
-      for (int ks = 0; ks < KS; ks += 2) {
-        BEF_GEMM_STEP(ks, sA0, sB0, sS0, sX0, sA1, sB1, sS1, sX1)
-        if (ks + 1 >= KS) break;
-        BEF_GEMM_STEP(ks + 1, sA1, sB1, sS1, sX1, sA0, sB0, sS0, sX0)
+    };
+    // wait until at most `newer` stages of this wave's loads are in flight
+    auto wait_stages = [&](int newer) {
+      switch (newer) {
+        case 0: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
+        case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kLoads)); break;
+        case 3: __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * kLoads)); break;
+        default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * kLoads)); break;
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < NST - 1; ++i) {
+      if (i < KS) {
+        const Stage st = stage(i);
+        issue(i, st.a, st.b, st.s, st.x);
       }
     }
-#undef BEF_GEMM_STEP
+    for (int kb = 0; kb < KS; kb += NST) {
+#pragma unroll
+      for (int j = 0; j < NST; ++j) {
+        const int ks = kb + j;
+        if (ks < KS) {
+          wait_stages(min(NST - 2, KS - 1 - ks));
+          __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+          block_barrier();
+          if (ks + NST - 1 < KS) {
+            const Stage nx = stage((j + NST - 1) % NST);
+            issue(ks + NST - 1, nx.a, nx.b, nx.s, nx.x);
+          }
+          const Stage cu = stage(j);
+          compute(ks, cu.a, cu.b, cu.s, cu.x);
+        }
+      }
+    }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     block_barrier();
 
@@ -479,13 +504,21 @@ static hipError_t launch_g(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// 256-token tiles when the routed groups average at least 128 rows (each
-// expert's weights then stream once for all of its tokens), else 128.
+// Token tile by the routed groups' average size: 256 from 128 rows (each
+// expert's weights then stream once for all of its tokens), 128 from 32,
+// else 64 (small stages: more K steps in flight while little multiplies).
 template <bool GU>
 static hipError_t launch_gg(const GemmArgs& a, hipStream_t st) {
-  const bool big = (int64_t)a.T * a.k >= (int64_t)128 * a.E;
-  if (a.fmt == 1) return big ? launch_g<1, GU, 256>(a, st) : launch_g<1, GU, 128>(a, st);
-  return big ? launch_g<2, GU, 256>(a, st) : launch_g<2, GU, 128>(a, st);
+  const int64_t rows = (int64_t)a.T * a.k;
+  const int tm = rows >= (int64_t)128 * a.E ? 256 : rows >= (int64_t)32 * a.E ? 128 : 64;
+  if (a.fmt == 1) {
+    if (tm == 256) return launch_g<1, GU, 256>(a, st);
+    if (tm == 128) return launch_g<1, GU, 128>(a, st);
+    return launch_g<1, GU, 64>(a, st);
+  }
+  if (tm == 256) return launch_g<2, GU, 256>(a, st);
+  if (tm == 128) return launch_g<2, GU, 128>(a, st);
+  return launch_g<2, GU, 64>(a, st);
 }
 
 hipError_t launch_gemm_gate_up(const GemmArgs& a, hipStream_t st) { return launch_gg<true>(a, st); }
