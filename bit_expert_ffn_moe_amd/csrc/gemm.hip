@@ -50,13 +50,9 @@
 
 namespace bef {
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* glb_ptr_t;
-
 constexpr int kGThreads = 512;
 
-// s_waitcnt immediates (gfx9: vmcnt [3:0] + [15:14], expcnt [6:4], lgkmcnt [11:8])
-constexpr int waitcnt_vm(int n) { return 0xF70 | (n & 0xF) | ((n >> 4) << 14); }
+// s_waitcnt immediate of lgkmcnt(0) (vmcnt and expcnt left at their maxima)
 constexpr int kWaitLgkm0 = 0xC07F;
 
 // Workgroup barrier that is also a compiler barrier for memory accesses: the
@@ -65,9 +61,6 @@ constexpr int kWaitLgkm0 = 0xC07F;
 // waits for nothing: the callers wait for their own loads explicitly.)
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-__device__ __forceinline__ void dma16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)l, 16, 0, 0);
-}
 __device__ __forceinline__ void dma4(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)l, 4, 0, 0);
 }

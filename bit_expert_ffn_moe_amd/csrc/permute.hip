@@ -14,48 +14,88 @@
 
 namespace bef {
 
-// One block for small T*k (<= kPermuteSmallPairs): ids staged in LDS, thread e
-// counts expert e, block scan gives the offsets, thread e then walks the
-// pairs again and assigns its rows.
+// Stable ranks of one chunk of 256 consecutive pairs, pair c0 + tid held by
+// thread tid with expert e (valid: e in [0, E), E <= 256).  Returns the
+// number of earlier pairs of the same expert in this chunk plus s_run[e],
+// the count from the chunks before; then adds this chunk's counts to s_run.
+// The lanes of a wave holding the same expert come from 8 ballots (one per
+// bit of e); the counts of the earlier waves of the chunk go through
+// s_hist, which must be zero on entry and is zero again on return.  All 256
+// threads must call it (it holds barriers).
+__device__ __forceinline__ int chunk_rank(int e, bool valid, int* s_run, int (*s_hist)[256]) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  uint64_t m = __ballot(valid);
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    const bool on = (e >> bit) & 1;
+    const uint64_t bb = __ballot(valid && on);
+    m &= on ? bb : ~bb;
+  }
+  const int before = __popcll(m & ((1ull << lane) - 1ull));
+  if (valid && before == 0) s_hist[w][e] = __popcll(m);
+  __syncthreads();
+  int r = 0;
+  if (valid) {
+    r = s_run[e] + before;
+    for (int w2 = 0; w2 < w; ++w2) r += s_hist[w2][e];
+  }
+  __syncthreads();
+  s_run[tid] += s_hist[0][tid] + s_hist[1][tid] + s_hist[2][tid] + s_hist[3][tid];
+  s_hist[0][tid] = 0, s_hist[1][tid] = 0, s_hist[2][tid] = 0, s_hist[3][tid] = 0;
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ void clear_rank_state(int* s_run, int (*s_hist)[256]) {
+  const int tid = threadIdx.x;
+  s_run[tid] = 0;
+  s_hist[0][tid] = 0, s_hist[1][tid] = 0, s_hist[2][tid] = 0, s_hist[3][tid] = 0;
+}
+
+// One block for small T*k (<= kPermuteSmallPairs): counts by LDS atomics,
+// block scan for the offsets, then the rows chunk by chunk.
 __global__ __launch_bounds__(256) void permute_small_kernel(
     const int32_t* __restrict__ ids, int T, int k, int E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ row_token, int32_t* __restrict__ row_of, uint32_t* __restrict__ status) {
-  __shared__ int32_t sid[kPermuteSmallPairs];
+  __shared__ int s_cnt[256], s_run[256], s_hist[4][256];
   __shared__ int stmp[8];
   __shared__ int s_bad;
   const int P = T * k;
   const int tid = threadIdx.x;
   if (tid == 0) s_bad = 0;
-  for (int p = tid; p < P; p += 256) sid[p] = ids[p];
+  s_cnt[tid] = 0;
+  clear_rank_state(s_run, s_hist);
   __syncthreads();
-  int bad = 0;
   for (int p = tid; p < P; p += 256) {
-    const int e = sid[p];
+    const int e = ids[p];
     if (e < 0 || e >= E) {
       row_of[(size_t)(p / k) * (k + 1) + (p % k)] = -1;
-      bad = 1;
+      s_bad = 1;
+    } else {
+      atomicAdd(&s_cnt[e], 1);
     }
   }
-  if (bad) s_bad = 1;
-  int cnt = 0;
-  if (tid < E)
-    for (int p = 0; p < P; ++p) cnt += (sid[p] == tid);
+  __syncthreads();
+  const int cnt = tid < E ? s_cnt[tid] : 0;
   int total;
-  const int pre = block256_exclusive_scan(tid < E ? cnt : 0, stmp, &total);
+  const int pre = block256_exclusive_scan(cnt, stmp, &total);
+  s_cnt[tid] = pre;  // each thread rewrites only the entry it read
   if (tid < E) offsets[tid] = pre;
   if (tid == 0) {
     offsets[E] = total;
     offsets[E + 1] = total + T;
     if (s_bad) set_status(status, MOE_STATUS_BAD_EXPERT_ID_DEV);
   }
-  if (tid < E && cnt > 0) {
-    int r = pre;
-    for (int p = 0; p < P; ++p) {
-      if (sid[p] == tid) {
-        row_token[r] = p / k;
-        row_of[(size_t)(p / k) * (k + 1) + (p % k)] = r;
-        ++r;
-      }
+  __syncthreads();
+  for (int c0 = 0; c0 < P; c0 += 256) {
+    const int p = c0 + tid;
+    const int e = p < P ? ids[p] : -1;
+    const bool valid = e >= 0 && e < E;
+    const int r = chunk_rank(e, valid, s_run, s_hist);
+    if (valid) {
+      const int row = s_cnt[e] + r, t = p / k;
+      row_token[row] = t;
+      row_of[(size_t)t * (k + 1) + (p % k)] = row;
     }
   }
   for (int t = tid; t < T; t += 256) {
@@ -65,34 +105,33 @@ __global__ __launch_bounds__(256) void permute_small_kernel(
 }
 
 // Large T: three passes over token blocks of kPermuteTokBlock tokens.
-// Pass 1: per-block counts cnt[b][e] (thread e walks the block's pairs).
+// Pass 1: per-block counts cnt[b][e] (LDS atomics).
 __global__ __launch_bounds__(256) void permute_count_kernel(const int32_t* __restrict__ ids,
                                                             int T, int k, int E,
                                                             int32_t* __restrict__ cnt,
                                                             int32_t* __restrict__ row_of,
                                                             uint32_t* __restrict__ status) {
-  __shared__ int32_t sid[kPermuteTokBlock * 16];
+  __shared__ int s_cnt[256];
   const int b = blockIdx.x;
   const int t0 = b * kPermuteTokBlock;
   const int nt = min(kPermuteTokBlock, T - t0);
   const int P = nt * k;
   const int tid = threadIdx.x;
+  s_cnt[tid] = 0;
+  __syncthreads();
   int bad = 0;
   for (int p = tid; p < P; p += 256) {
     const int e = ids[(size_t)t0 * k + p];
-    sid[p] = e;
     if (e < 0 || e >= E) {
       row_of[(size_t)(t0 + p / k) * (k + 1) + (p % k)] = -1;
       bad = 1;
+    } else {
+      atomicAdd(&s_cnt[e], 1);
     }
   }
   if (bad) set_status(status, MOE_STATUS_BAD_EXPERT_ID_DEV);
   __syncthreads();
-  if (tid < E) {
-    int c = 0;
-    for (int p = 0; p < P; ++p) c += (sid[p] == tid);
-    cnt[(size_t)b * E + tid] = c;
-  }
+  if (tid < E) cnt[(size_t)b * E + tid] = s_cnt[tid];
 }
 
 // Pass 2 (one block): running sums over blocks per expert, scan over experts.
@@ -122,28 +161,29 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(int nblk, int T, int 
   }
 }
 
-// Pass 3: thread e walks its block's pairs in order and assigns its rows.
+// Pass 3: the block's pairs get their rows chunk by chunk.
 __global__ __launch_bounds__(256) void permute_scatter_kernel(
     const int32_t* __restrict__ ids, int T, int k, int E, const int32_t* __restrict__ base,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
     int32_t* __restrict__ row_of) {
-  __shared__ int32_t sid[kPermuteTokBlock * 16];
+  __shared__ int s_base[256], s_run[256], s_hist[4][256];
   const int b = blockIdx.x;
   const int t0 = b * kPermuteTokBlock;
   const int nt = min(kPermuteTokBlock, T - t0);
   const int P = nt * k;
   const int tid = threadIdx.x;
-  for (int p = tid; p < P; p += 256) sid[p] = ids[(size_t)t0 * k + p];
+  s_base[tid] = tid < E ? base[(size_t)b * E + tid] : 0;
+  clear_rank_state(s_run, s_hist);
   __syncthreads();
-  if (tid < E) {
-    int r = base[(size_t)b * E + tid];
-    for (int p = 0; p < P; ++p) {
-      if (sid[p] == tid) {
-        const int t = t0 + p / k;
-        row_token[r] = t;
-        row_of[(size_t)t * (k + 1) + (p % k)] = r;
-        ++r;
-      }
+  for (int c0 = 0; c0 < P; c0 += 256) {
+    const int p = c0 + tid;
+    const int e = p < P ? ids[(size_t)t0 * k + p] : -1;
+    const bool valid = e >= 0 && e < E;
+    const int r = chunk_rank(e, valid, s_run, s_hist);
+    if (valid) {
+      const int row = s_base[e] + r, t = t0 + p / k;
+      row_token[row] = t;
+      row_of[(size_t)t * (k + 1) + (p % k)] = row;
     }
   }
   const int shared0 = offsets[E];
@@ -157,6 +197,7 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
                           int32_t* row_token, int32_t* row_of, int32_t* cnt, int32_t* base,
                           uint32_t* status, hipStream_t st) {
+  if (E < 1 || E > 256 || k < 1) return hipErrorInvalidValue;  // one thread per expert
   if ((int64_t)T * k <= kPermuteSmallPairs) {
     permute_small_kernel<<<1, 256, 0, st>>>(ids, T, k, E, offsets, row_token, row_of, status);
     return hipGetLastError();
