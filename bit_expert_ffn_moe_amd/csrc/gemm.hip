@@ -81,9 +81,12 @@ __device__ __forceinline__ uint32_t e4m3_1(float v) {
 }
 
 // LDS byte offset of 16-byte chunk c of row r: rows of 128 bytes (E4M3, one
-// K step) swizzle by bits 3..1 of r, rows of 64 bytes (E2M1) by bits 3..2.
+// K step) swizzle by bits 3..1 of r, rows of 64 bytes (E2M1) by bits 2..1.
+// Measured with the fragment read (rows r = lane mod 16, chunk lane / 16,
+// ds_read_b128): both run at ~142 B/clk per CU, while 64-byte rows unswizzled
+// or swizzled by bits 3..2 reach only ~116 (bank conflicts).
 __device__ __forceinline__ int sw128(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
-__device__ __forceinline__ int sw64(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+__device__ __forceinline__ int sw64(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 3)) << 4); }
 
 // ---------------------------------------------------------------------------
 // The kernel.  Tile: 256 weight rows (gate+up: rows nb*128 .. +127 of W_gate
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
     for (int i = 0; i < NBI; ++i) {
       const int p = (w * NBI + i) * 64 + lane;
       const int r = FMT == 1 ? (p >> 2) : (p >> 3);
-      const int c = FMT == 1 ? ((p & 3) ^ ((r >> 2) & 3)) : ((p & 7) ^ ((r >> 1) & 7));
+      const int c = FMT == 1 ? ((p & 3) ^ ((r >> 1) & 3)) : ((p & 7) ^ ((r >> 1) & 7));
       offB[i] = (row_base + (uint32_t)(GU ? (r & 127) : r)) * brow_bytes + 16u * c;
     }
     // FP4 scales: weight row w*32 + lane (lanes < 32; gate rows are waves 0-3)
