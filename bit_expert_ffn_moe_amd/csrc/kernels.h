@@ -9,6 +9,7 @@ namespace bef {
 
 constexpr int kRouteSmallT = 4;           // router: per-chunk blocks + last-block top-k
 constexpr int kRouteMaxGroups = 32;       // router: 256-row groups, H <= 8192
+constexpr int kRouteSplitT = 256;         // router: experts also split in quarters below this T
 constexpr int kPermuteSmallPairs = 2048;  // permute: single block up to this many pairs
 constexpr int kPermuteTokBlock = 256;     // permute: tokens per block above that
 constexpr int kGemvMaxRows = 8;           // VALU GEMV path: rows (k + 1) per token

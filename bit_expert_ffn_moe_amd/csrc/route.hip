@@ -445,6 +445,99 @@ __global__ __launch_bounds__(256) void route_group_kernel(const uint16_t* __rest
   }
 }
 
+// Fewer tokens (T < kRouteSplitT): the same group sums with the experts split
+// in quarters as well, block (g, quarter, 32-token tile), so that a 32-token
+// batch still spreads over 64 blocks; thread (ty, tx) accumulates token ty x
+// experts 64 quarter + 8tx .. +7 in the same fixed order.
+__global__ __launch_bounds__(256) void route_group_quarter_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int H, int E,
+    float* __restrict__ gsum) {
+  __shared__ __align__(16) float sx[32][68];   // [token][h of the chunk], padded rows
+  __shared__ __align__(16) float sw[64][64];   // [h of the chunk][expert of the quarter]
+  const int g = blockIdx.x, e00 = 64 * blockIdx.y, t0 = blockIdx.z * 32;
+  const int tid = threadIdx.x;
+  const int ty = tid >> 3, tx = tid & 7;
+  const int nc = H / 64;
+  const int c0 = 4 * g, c1 = min(4 * g + 4, nc);
+  // this thread's share of a chunk: x row tid/8, 8 bf16 at (tid%8)*8; router
+  // 16-byte pieces q = tid + 256 i (i < 2): row q/8, experts e00 + (q%8)*8 .. +7
+  const int xr = tid >> 3, xc = (tid & 7) * 8;
+  const bool xin = t0 + xr < T;
+  uint4 px, pw[2];
+  auto load_chunk = [&](int c) {
+    px = xin ? *reinterpret_cast<const uint4*>(x + (size_t)(t0 + xr) * H + 64 * c + xc)
+             : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + 256 * i, h = q >> 3, e8 = e00 + (q & 7) * 8;
+      const uint16_t* src = wr + (size_t)(64 * c + h) * E + e8;
+      if (e8 + 8 <= E && (E & 7) == 0) {
+        pw[i] = *reinterpret_cast<const uint4*>(src);
+      } else {
+        uint16_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = (e8 + u < E) ? src[u] : (uint16_t)0;
+        pw[i] = make_uint4(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
+                           v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16));
+      }
+    }
+  };
+  auto store_chunk = [&]() {
+    *reinterpret_cast<float4*>(&sx[xr][xc]) =
+        make_float4(bf16_to_f32(px.x & 0xffffu), bf16_to_f32(px.x >> 16),
+                    bf16_to_f32(px.y & 0xffffu), bf16_to_f32(px.y >> 16));
+    *reinterpret_cast<float4*>(&sx[xr][xc + 4]) =
+        make_float4(bf16_to_f32(px.z & 0xffffu), bf16_to_f32(px.z >> 16),
+                    bf16_to_f32(px.w & 0xffffu), bf16_to_f32(px.w >> 16));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + 256 * i, h = q >> 3, e8 = (q & 7) * 8;
+      const uint4 r = pw[i];
+      *reinterpret_cast<float4*>(&sw[h][e8]) =
+          make_float4(bf16_to_f32(r.x & 0xffffu), bf16_to_f32(r.x >> 16),
+                      bf16_to_f32(r.y & 0xffffu), bf16_to_f32(r.y >> 16));
+      *reinterpret_cast<float4*>(&sw[h][e8 + 4]) =
+          make_float4(bf16_to_f32(r.z & 0xffffu), bf16_to_f32(r.z >> 16),
+                      bf16_to_f32(r.w & 0xffffu), bf16_to_f32(r.w >> 16));
+    }
+  };
+  float grp[8];
+  load_chunk(c0);
+  for (int c = c0; c < c1; ++c) {
+    store_chunk();
+    __syncthreads();
+    if (c + 1 < c1) load_chunk(c + 1);  // in flight while this chunk multiplies
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = 0.0f;
+#pragma unroll 4
+    for (int h4 = 0; h4 < 64; h4 += 4) {
+      const float4 xv = *reinterpret_cast<const float4*>(&sx[ty][h4]);
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        const float4 w0 = *reinterpret_cast<const float4*>(&sw[h4 + hh][8 * tx]);
+        const float4 w1 = *reinterpret_cast<const float4*>(&sw[h4 + hh][8 * tx + 4]);
+        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        const float xs = hh == 0 ? xv.x : hh == 1 ? xv.y : hh == 2 ? xv.z : xv.w;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[j] = fmaf(xs, wv[j], p[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) grp[j] = (c == c0) ? p[j] : grp[j] + p[j];
+    __syncthreads();
+  }
+  const int t = t0 + ty, e0 = e00 + 8 * tx;
+  if (t >= T) return;
+  float* dst = gsum + ((size_t)g * T + t) * E;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (e0 + j < E) dst[e0 + j] = grp[j];
+}
+
+// The logits of 4 tokens per block: group sums added in ascending group order
+// (thread e owns expert e; all group loads issued before the adds), then
+// one wave per token runs the top-k.
 __global__ __launch_bounds__(256) void route_reduce_kernel(const float* __restrict__ gsum, int T,
                                                            int H, int E, int k,
                                                            int32_t* __restrict__ ids,
@@ -452,16 +545,19 @@ __global__ __launch_bounds__(256) void route_reduce_kernel(const float* __restri
   __shared__ float sz[4][256];
   const int t0 = blockIdx.x * 4, tid = threadIdx.x;
   const int ng = (H / 64 + 3) / 4;
-  const int e = tid;
+  const int e = min(tid, E - 1);
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
-    const int t = t0 + tt;
-    float acc = 0.0f;
-    if (t < T && e < E) {
-      acc = gsum[(size_t)t * E + e];
-      for (int g = 1; g < ng; ++g) acc = acc + gsum[((size_t)g * T + t) * E + e];
-    }
-    sz[tt][e] = acc;
+    const int t = min(t0 + tt, T - 1);
+    float v[kRouteMaxGroups];
+#pragma unroll
+    for (int g = 0; g < kRouteMaxGroups; ++g)
+      v[g] = gsum[((size_t)min(g, ng - 1) * T + t) * E + e];
+    float acc = v[0];
+#pragma unroll
+    for (int g = 1; g < kRouteMaxGroups; ++g)
+      if (g < ng) acc = acc + v[g];
+    sz[tt][tid] = (t0 + tt < T && tid < E) ? acc : 0.0f;
   }
   __syncthreads();
   const int wv = tid >> 6, t = t0 + wv;
@@ -477,9 +573,14 @@ hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int H, int
     set_route_sync(a, ctl);
     return launch_route_front(a, st);
   }
-  if (!gsum || E > 256 || H % 64 != 0) return hipErrorInvalidValue;
+  if (!gsum || E > 256 || H % 64 != 0 || (H / 64 + 3) / 4 > kRouteMaxGroups)
+    return hipErrorInvalidValue;
   const int ng = (H / 64 + 3) / 4;
-  route_group_kernel<<<dim3(ng, (T + 31) / 32), dim3(256), 0, st>>>(x, wr, T, H, E, gsum);
+  if (T < kRouteSplitT)
+    route_group_quarter_kernel<<<dim3(ng, (E + 63) / 64, (T + 31) / 32), dim3(256), 0, st>>>(
+        x, wr, T, H, E, gsum);
+  else
+    route_group_kernel<<<dim3(ng, (T + 31) / 32), dim3(256), 0, st>>>(x, wr, T, H, E, gsum);
   route_reduce_kernel<<<dim3((T + 3) / 4), dim3(256), 0, st>>>(gsum, T, H, E, k, ids, w);
   return hipGetLastError();
 }

@@ -100,7 +100,8 @@ def test_act_quant_encoder_exhaustive_sweep():
                                      (64, 256, 8, 2), (1, 4096, 256, 6), (4, 4096, 256, 6),
                                      (5, 4096, 256, 6), (37, 4096, 256, 6),
                                      (300, 4096, 256, 6), (40, 1024, 100, 16),
-                                     (4, 8192, 256, 16), (2, 8192, 200, 11)])
+                                     (4, 8192, 256, 16), (2, 8192, 200, 11),
+                                     (33, 8192, 200, 11), (257, 4096, 256, 6)])
 def test_route_ids_bitexact(T, H, E, k):
     _print("route", T, H, E, k)
     x = synth.normal_bf16(900 + T, 1, (T, H), 1.0)
