@@ -138,38 +138,34 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// The same DPP pattern for max / min: lanes whose source is out of range or
-// whose row is masked keep their own value (DPP "old" operand = the value).
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ int dpp_keep(int v) {
-  return __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xF, false);
+// Maximum / minimum over the 64 lanes, in every lane: inside each row of 16
+// by DPP (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror; every source lane exists, so each step fuses into one
+// v_max/min_i32_dpp), then across rows by the gfx950 row swaps
+// (v_permlane16_swap: rows 0<->1 and 2<->3; v_permlane32_swap: halves).
+template <int CTRL>
+__device__ __forceinline__ int dpp_row(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
-__device__ __forceinline__ float wave_max_dpp(float v) {
-  v = fmaxf(v, __int_as_float(dpp_keep<0xB1>(__float_as_int(v))));
-  v = fmaxf(v, __int_as_float(dpp_keep<0x4E>(__float_as_int(v))));
-  v = fmaxf(v, __int_as_float(dpp_keep<0x141>(__float_as_int(v))));
-  v = fmaxf(v, __int_as_float(dpp_keep<0x140>(__float_as_int(v))));
-  v = fmaxf(v, __int_as_float(dpp_keep<0x142, 0xA>(__float_as_int(v))));
-  v = fmaxf(v, __int_as_float(dpp_keep<0x143, 0xC>(__float_as_int(v))));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+__device__ __forceinline__ int wave_max_all(int v) {
+  v = max(v, dpp_row<0xB1>(v));
+  v = max(v, dpp_row<0x4E>(v));
+  v = max(v, dpp_row<0x141>(v));
+  v = max(v, dpp_row<0x140>(v));
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max((int)a[0], (int)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((int)b[0], (int)b[1]);
 }
-__device__ __forceinline__ int wave_max_dpp(int v) {
-  v = max(v, dpp_keep<0xB1>(v));
-  v = max(v, dpp_keep<0x4E>(v));
-  v = max(v, dpp_keep<0x141>(v));
-  v = max(v, dpp_keep<0x140>(v));
-  v = max(v, dpp_keep<0x142, 0xA>(v));
-  v = max(v, dpp_keep<0x143, 0xC>(v));
-  return __builtin_amdgcn_readlane(v, 63);
-}
-__device__ __forceinline__ int wave_min_dpp(int v) {
-  v = min(v, dpp_keep<0xB1>(v));
-  v = min(v, dpp_keep<0x4E>(v));
-  v = min(v, dpp_keep<0x141>(v));
-  v = min(v, dpp_keep<0x140>(v));
-  v = min(v, dpp_keep<0x142, 0xA>(v));
-  v = min(v, dpp_keep<0x143, 0xC>(v));
-  return __builtin_amdgcn_readlane(v, 63);
+__device__ __forceinline__ int wave_min_all(int v) {
+  v = min(v, dpp_row<0xB1>(v));
+  v = min(v, dpp_row<0x4E>(v));
+  v = min(v, dpp_row<0x141>(v));
+  v = min(v, dpp_row<0x140>(v));
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = min((int)a[0], (int)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return min((int)b[0], (int)b[1]);
 }
 
 // Butterfly reduce-scatter over the 64 lanes.  Each lane starts with N

@@ -27,9 +27,10 @@ namespace bef {
 // ids / weights.  Lane l owns experts l, l+64, l+128, l+192, as integer keys
 // that order like the logits (-0 made +0; a NaN below every number, an
 // expert beyond E below that), sorted in the lane by (key desc, id asc).
-// Each of the k rounds takes the wave maximum of the lanes' leading keys by
-// DPP -- when several lanes hold it, the lowest of their ids by a DPP
-// minimum -- and the winning lane moves on to its next key.
+// Each of the k rounds takes the wave maximum of the lanes' leading keys
+// (wave_max_all: fused DPP steps and row swaps) -- when several lanes hold
+// it, the lowest of their ids by the same minimum -- and the winning lane
+// moves on to its next key.
 __device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, int k,
                                           int32_t* __restrict__ ids_out,
                                           float* __restrict__ w_out) {
@@ -38,10 +39,11 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, in
   int key[4], sl[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    const float v = (e < E) ? z[e] : 0.0f;
+    const int e = lane + 64 * i;  // < 256: z holds 256 entries, those from E on unused
+    const float v = z[e];
     const int b = __float_as_int(v + 0.0f);
-    key[i] = (e >= E) ? kAbsent : (v != v) ? kNaN : (b >= 0 ? b : b ^ 0x7fffffff);
+    const int kv = (v != v) ? kNaN : (b >= 0 ? b : b ^ 0x7fffffff);
+    key[i] = (e >= E) ? kAbsent : kv;
     sl[i] = i;
   }
   // a 4-input sorting network on (key desc, slot asc)
@@ -59,24 +61,27 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, in
   ce(1, 3);
   ce(1, 2);
   int my_id = 0;
-  for (int j = 0; j < k; ++j) {
-    const int m = wave_max_dpp(key[0]);
+  // k <= 16 (checked by the launchers): unrolled, so the lane's list shifts
+  // are register renamings rather than copies carried around a loop
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j >= k) continue;  // uniform; no early exit, so the loop unrolls fully
+    const int m = wave_max_all(key[0]);
     const uint64_t cand = __ballot(key[0] == m);
     int wl;
     if (__popcll(cand) == 1) {
       wl = __ffsll((long long)cand) - 1;
     } else {
       const int id = ((cand >> lane) & 1ull) ? lane + 64 * sl[0] : 0x7fffffff;
-      wl = wave_min_dpp(id) & 63;
+      wl = __builtin_amdgcn_readfirstlane(wave_min_all(id)) & 63;
     }
     const int win = __builtin_amdgcn_readlane(lane + 64 * sl[0], wl);
     if (lane == j) my_id = win;
-    if (lane == wl) {
-      key[0] = key[1], sl[0] = sl[1];
-      key[1] = key[2], sl[1] = sl[2];
-      key[2] = key[3], sl[2] = sl[3];
-      key[3] = kAbsent;
-    }
+    const bool pop = lane == wl;
+    key[0] = pop ? key[1] : key[0], sl[0] = pop ? sl[1] : sl[0];
+    key[1] = pop ? key[2] : key[1], sl[1] = pop ? sl[2] : sl[1];
+    key[2] = pop ? key[3] : key[2], sl[2] = pop ? sl[3] : sl[2];
+    key[3] = pop ? kAbsent : key[3];
   }
   const float my_z = (lane < k) ? z[my_id] : 0.0f;
   const float sg = (lane < k) ? 1.0f / (1.0f + expf(-my_z)) : 0.0f;
