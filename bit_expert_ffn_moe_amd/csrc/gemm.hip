@@ -66,13 +66,15 @@ __device__ __forceinline__ void dma4(const void* g, void* l) {
 }
 
 // SwiGLU and requantisation in the grouped GEMM's epilogue use the fast
-// exponential and reciprocals: h there already carries the MFMA's own
-// accumulation error (its 128-term sums are not exactly rounded), next to
-// which a few ulp of the SiLU and of v * (1/s) instead of v / s are
-// negligible.  The one-token GEMV keeps the IEEE forms (its h is exact to
-// fp32 rounding).
+// exponential and the hardware reciprocal (v_rcp_f32, ~1 ulp; the
+// correctly rounded __frcp_rn is a ~10-instruction division sequence): h
+// there already carries the MFMA's own accumulation error (its 128-term sums
+// are not exactly rounded), next to which a few ulp of the SiLU and of
+// v * (1/s) instead of v / s are negligible.  The scale s = amax / 448 itself
+// stays an IEEE division.  The one-token GEMV keeps the IEEE forms (its h is
+// exact to fp32 rounding).
 __device__ __forceinline__ float silu_mul_fast(float g, float u) {
-  return g * u * __frcp_rn(1.0f + __expf(-g));
+  return g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
 __device__ __forceinline__ uint32_t e4m3_1(float v) {
@@ -432,7 +434,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
         const int t = wt * (TM / 4) + 16 * ti + (lane & 15);
         const float am = fmaxf(s_amax[0][t], s_amax[1][t]);
         const float sc = am / 448.0f;
-        const float rsc = __frcp_rn(sc);
+        const float rsc = __builtin_amdgcn_rcpf(sc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           uint32_t cw = 0;
