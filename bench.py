@@ -49,7 +49,8 @@ def is_dominant(kernel_name, path):
     """Does a profiler kernel name belong to the path's dominant kernel?"""
     if path == "gemv":
         return "gemv_gate_up_fp4_kernel" in kernel_name
-    return "gemm_kernel<" in kernel_name and "true>" in kernel_name
+    # gemm_kernel<FMT, GU, TM>: the gate+up instances
+    return "gemm_kernel<" in kernel_name and ", true," in kernel_name
 
 
 # --------------------------------------------------------------------------
