@@ -222,45 +222,47 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
   // this launch is visible, then clearing the slots; thread ez owns expert
   // ez (each slot is written once per launch, so the clear cannot race a
   // write of this launch)
+  // (the loads go out together, unconditionally: H <= 2048 NB, so ng <=
+  // 8 NB = GMAX and a clamped index repeats the last group only when H is
+  // not a multiple of 2048; a branch per load would issue them one by one)
+  constexpr int GMAX = 8 * NB;
   const int ez = tid;
   bool ok = true;
   for (int t = 0; t < T; ++t) {
     float acc = -INFINITY;  // experts beyond E never rank
     if (ez < E) {
-      acc = 0.0f;
-      for (int c0 = 0; c0 < ng; c0 += 32) {
-        unsigned long long v[32];
+      unsigned long long* st = slots + (size_t)t * E + ez;
+      const size_t gstride = (size_t)T * E;
+      unsigned long long v[GMAX];
 #pragma unroll
-        for (int i = 0; i < 32; ++i)
-          v[i] = (c0 + i < ng) ? __hip_atomic_load(slots + ((size_t)(c0 + i) * T + t) * E + ez,
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                               : kSlotValid;
-        for (uint32_t spins = 0;;) {
-          bool all = true;
+      for (int i = 0; i < GMAX; ++i)
+        v[i] = __hip_atomic_load(st + (size_t)min(i, ng - 1) * gstride, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      for (uint32_t spins = 0;;) {
+        bool all = true;
 #pragma unroll
-          for (int i = 0; i < 32; ++i)
-            if ((v[i] & kSlotTagMask) != kSlotValid) {
-              all = false;
-              v[i] = __hip_atomic_load(slots + ((size_t)(c0 + i) * T + t) * E + ez,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-          if (all) break;
-          if (++spins >= kSpinLimit) {
-            ok = false;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
+        for (int i = 0; i < GMAX; ++i) all &= (v[i] & kSlotTagMask) == kSlotValid;
+        if (all) break;
+        if (++spins >= kSpinLimit) {
+          ok = false;
+          break;
         }
+        __builtin_amdgcn_s_sleep(1);
 #pragma unroll
-        for (int i = 0; i < 32; ++i)
-          if (c0 + i < ng)
-            __hip_atomic_store(slots + ((size_t)(c0 + i) * T + t) * E + ez, 0ull, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-          if (c0 + i < ng) acc = (c0 + i == 0) ? __uint_as_float((uint32_t)v[i])
-                                               : acc + __uint_as_float((uint32_t)v[i]);
+        for (int i = 0; i < GMAX; ++i)
+          if ((v[i] & kSlotTagMask) != kSlotValid)
+            v[i] = __hip_atomic_load(st + (size_t)min(i, ng - 1) * gstride, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
       }
+#pragma unroll
+      for (int i = 0; i < GMAX; ++i)
+        if (i < ng)
+          __hip_atomic_store(st + (size_t)i * gstride, 0ull, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      acc = __uint_as_float((uint32_t)v[0]);
+#pragma unroll
+      for (int i = 1; i < GMAX; ++i)
+        if (i < ng) acc = acc + __uint_as_float((uint32_t)v[i]);
     }
     sz[t][ez] = acc;
   }
