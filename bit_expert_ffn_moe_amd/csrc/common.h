@@ -243,19 +243,35 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
+// Max over aligned groups of G lanes (G = 2, 4, 8, 16, 32 or 64), in every
+// lane of the group: DPP inside rows of 16 (quad_perm [1,0,3,2], quad_perm
+// [2,3,0,1], row_half_mirror, row_mirror -- each pairs the halves of the
+// next larger group), the gfx950 row swaps above.  A maximum does not depend
+// on the order of its operands, so this is the same value as any other tree.
+template <int CTRL>
+__device__ __forceinline__ float dpp_rowf(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
-
-// Max over aligned groups of G lanes (G a power of two <= 64).
 template <int G>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int m = G / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  static_assert(G == 2 || G == 4 || G == 8 || G == 16 || G == 32 || G == 64, "group size");
+  v = fmaxf(v, dpp_rowf<0xB1>(v));
+  if constexpr (G >= 4) v = fmaxf(v, dpp_rowf<0x4E>(v));
+  if constexpr (G >= 8) v = fmaxf(v, dpp_rowf<0x141>(v));
+  if constexpr (G >= 16) v = fmaxf(v, dpp_rowf<0x140>(v));
+  if constexpr (G >= 32) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  }
+  if constexpr (G >= 64) {
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    v = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  }
   return v;
 }
+__device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
