@@ -176,8 +176,20 @@ __device__ __forceinline__ int wave_min_all(int v) {
 // (i <-> 15-i) flips bit 3, row_half_mirror (i <-> 7-i) flips bit 2, and the
 // quad permutations flip bits 1 and 0 -- each pairing also flips lower bits,
 // which is harmless because those have not been used yet.
-__device__ __forceinline__ float xchg32(float a) { return __shfl_xor(a, 32, kWave); }
-__device__ __forceinline__ float xchg16(float a) { return __shfl_xor(a, 16, kWave); }
+// The value of lane l ^ 32 / l ^ 16 by the gfx950 row swaps (no LDS round
+// trip): with both operands a, v_permlane32_swap returns {lanes 0-31 of a
+// in both halves, lanes 32-63 of a in both halves} and v_permlane16_swap
+// {the even rows of a in both rows of each pair, the odd rows likewise}.
+__device__ __forceinline__ float xchg32(float a) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false,
+                                                  false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xchg16(float a) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false,
+                                                  false);
+  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
 __device__ __forceinline__ float xchg_b3(float a) { return dpp_f<0x140>(a); }
 __device__ __forceinline__ float xchg_b2(float a) { return dpp_f<0x141>(a); }
 __device__ __forceinline__ float xchg_b1(float a) { return dpp_f<0x4E>(a); }
