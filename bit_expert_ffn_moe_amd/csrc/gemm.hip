@@ -7,13 +7,14 @@
 // are fp4_gemm (FP8-quantised activation x FP4 packed weight) and fp8_gemm
 // (tcti.cn post, section "补齐软件栈缺失"), dequantised inside the MFMA
 // (dpshk.com article, section "核心实现四"):
-//   v_mfma_scale_f32_16x16x128_f8f6f4, A = E4M3 activations (scale 2^0),
-//   B = E2M1 weights with their UE8M0 scale per 32 K as the hardware B scale
-//   (FP4), or B = E4M3 weights (FP8, fp32 block scale applied below).
+//   v_mfma_scale_f32_16x16x128_f8f6f4, taken transposed: A = weight rows
+//   (E2M1 with their UE8M0 scale per 32 K as the hardware A scale, or E4M3
+//   with an fp32 128x128 block scale applied below), B = E4M3 token rows.
 // The fp32 activation scale (amax/448 per 128 of K) cannot ride in the MFMA
 // scale operand, so each 128-deep K step is issued into a fresh result and
 // folded into the running sum with one FMA per output: acc += s_x * d (times
-// the weight block scale for FP8).
+// the weight block scale for FP8).  In the transposed form a lane holds 4
+// weight rows of one token, so s_x is one value per lane.
 //
 // Operand layout of the 16x16x128 f8f6f4 MFMA (measured on gfx950 with a
 // one-hot probe): lane l supplies row/column l%16; lane group q = l/16 holds
@@ -25,24 +26,23 @@
 // Shapes: an expert sees ~200 tokens in a uniformly routed 8192-token
 // prefill, so its weights carry ~2x200 flops per byte -- below the chip's
 // ~600 flop/byte balance point: the weights must stream from HBM once.  A
-// tile is 128 tokens x 256 output columns (gate+up: 128 columns of I for both
-// matrices, so SwiGLU and the per-128 requant of h finish in the tile); 4
-// waves, one per SIMD, as 2 (M) x 2 (N), 64 x 128 outputs each (128 fp32
-// accumulators per lane, up to 512 registers per wave).  Per 128-deep K step
-// the block stages its A rows (gathered token rows) and B rows (weight rows)
-// in LDS with direct global->LDS loads (global_load_lds_dwordx4), three
-// stages deep in separate LDS objects so that the compiler's wait tracking
-// lets the next stages' loads fly while one is multiplied; the 16-byte chunk
-// positions are XOR-swizzled by row so the MFMA operand reads are
-// conflict-free.
+// tile is 256 weight rows (gate+up: 128 rows of each matrix for the same 128
+// columns of I, so SwiGLU and the per-128 requant of h finish in the tile) x
+// TM tokens (256, 128 or 64 by the groups' average size); 8 waves as 2
+// (rows) x 4 (tokens).  Per 128-deep K step the block stages its weight rows
+// and gathered token rows in LDS with direct global->LDS loads
+// (global_load_lds_dwordx4), as many stages as fit (at most 6) in separate
+// LDS objects so that the compiler's wait tracking lets the younger stages'
+// loads fly while one is multiplied; the 16-byte chunk positions are
+// XOR-swizzled by row so the MFMA operand reads are conflict-free.
 //
-// The grid is persistent (one block per CU) and XCD-aware: the work items
-// (expert M-tile, N-block), N-blocks of one M-tile adjacent, are split into 8
-// contiguous ranges, one per XCD (block b runs on XCD b mod 8).  The 32
-// blocks of an XCD thus work on neighbouring items together: the N-blocks of
-// an M-tile share its activation rows in the XCD's L2, and the M-tiles of
-// one expert (16 items apart for I = 2048) read the same weight rows at the
-// same time, so those stream from HBM about once.
+// The grid is persistent (one block per CU, two for the small FP4 tiles) and
+// XCD-aware: the work items (expert M-tile, N-block), N-blocks of one M-tile
+// adjacent, are split into 8 contiguous ranges, one per XCD (block b runs on
+// XCD b mod 8).  The blocks of an XCD thus work on neighbouring items
+// together: the N-blocks of an M-tile share its token rows in the XCD's L2,
+// and the M-tiles of one expert read the same weight rows at about the same
+// time, so those stream from HBM about once.
 #include <hip/hip_ext.h>
 
 #include "common.h"
