@@ -20,12 +20,6 @@ typedef __attribute__((address_space(1))) void* glb_ptr_t;
 // s_waitcnt immediates (gfx9: vmcnt [3:0] + [15:14], expcnt [6:4], lgkmcnt [11:8])
 constexpr int waitcnt_vm(int n) { return 0xF70 | (n & 0xF) | ((n >> 4) << 14); }
 
-// Direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4): the
-// LDS address is the wave-uniform base l plus 16 x lane.
-__device__ __forceinline__ void dma16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)l, 16, 0, 0);
-}
-
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v4f_t __attribute__((ext_vector_type(4)));

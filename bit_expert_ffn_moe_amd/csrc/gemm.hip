@@ -31,10 +31,10 @@
 // TM tokens (256, 128 or 64 by the groups' average size); 8 waves as 2
 // (rows) x 4 (tokens).  Per 128-deep K step the block stages its weight rows
 // and gathered token rows in LDS with direct global->LDS loads
-// (global_load_lds_dwordx4), as many stages as fit (at most 6) in separate
-// LDS objects so that the compiler's wait tracking lets the younger stages'
-// loads fly while one is multiplied; the 16-byte chunk positions are
-// XOR-swizzled by row so the MFMA operand reads are conflict-free.
+// (global_load_lds_dwordx4), as many stages as fit (at most 6), each waited
+// for explicitly so that the younger stages' loads fly while one is
+// multiplied; the 16-byte chunk positions are XOR-swizzled by row so the
+// MFMA operand reads are conflict-free.
 //
 // The grid is persistent (one block per CU, two for the small FP4 tiles) and
 // XCD-aware: the work items (expert M-tile, N-block), N-blocks of one M-tile
@@ -61,8 +61,24 @@ constexpr int kWaitLgkm0 = 0xC07F;
 // waits for nothing: the callers wait for their own loads explicitly.)
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-__device__ __forceinline__ void dma4(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)l, 4, 0, 0);
+// Direct global->LDS loads of 16 or 4 bytes per lane: global address base +
+// voff (base wave-uniform), LDS address M0 + size x lane, with M0 the
+// wave-uniform LDS base l.  Written as asm statements (no register output,
+// LDS written, hence the memory clobber): the compiler's tracking of the
+// builtin form marks the LDS counter out of order, so every later LDS read
+// then waits for all outstanding ones (lgkmcnt(0)) and the first MFMA of a
+// K step waits for all of the step's operand reads.  Unseen by the compiler,
+// these loads are waited for explicitly (vmcnt before each step's barrier).
+__device__ __forceinline__ uint32_t lds_addr(void* l) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)l);
+}
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, void* l) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr(l))
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const uint8_t* base, uint32_t voff, void* l) {
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr(l))
+               : "memory");
 }
 
 // SwiGLU and requantisation in the grouped GEMM's epilogue use the fast
@@ -263,15 +279,15 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
     auto issue = [&](int ks_, uint8_t* sA, uint8_t* sB, uint32_t* sS, float* sX) {
       const uint32_t ks = (uint32_t)kr(ks_);
 #pragma unroll
-      for (int i = 0; i < NAI; ++i) dma16(baseA + (offA[i] + ks * 128u), sA + (w * NAI + i) * 1024);
+      for (int i = 0; i < NAI; ++i) dma16(baseA, offA[i] + ks * 128u, sA + (w * NAI + i) * 1024);
 #pragma unroll
       for (int i = 0; i < NBI; ++i) {
         // weight rows >= 128 of a gate+up tile are up rows: uniform per instruction
         const uint8_t* bb = (GU && (w * NBI + i) * 64 >= 128 * (FMT == 1 ? 4 : 8)) ? baseU : baseG;
-        dma16(bb + (offB[i] + ks * (FMT == 1 ? 64u : 128u)), sB + (w * NBI + i) * 1024);
+        dma16(bb, offB[i] + ks * (FMT == 1 ? 64u : 128u), sB + (w * NBI + i) * 1024);
       }
-      if (FMT == 1 && lane < 32) dma4(baseS + (offS + ks * 4u), sS + w * 32);
-      if (lane < XL) dma4(baseX + (offX + ks), sX + w * XL);
+      if (FMT == 1 && lane < 32) dma4(baseS, offS + ks * 4u, sS + w * 32);
+      if (lane < XL) dma4((const uint8_t*)baseX, (offX + ks) * 4u, sX + w * XL);
     };
 
     v4f_t acc[8][NT];
@@ -291,30 +307,6 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
     auto compute = [&](int ks, const uint8_t* sA, const uint8_t* sB, const uint32_t* sS,
                        const float* sX) {
       if (!live) return;
-      // the wave's 4 token fragments and their activation scales (times the
-      // FP8 weight block scale: gate / up halves)
-      v8i_t tv[NT];
-      float cx[NT], cy[NT];
-#pragma unroll
-      for (int ti = 0; ti < NT; ++ti) {
-        const int r = wt * (TM / 4) + 16 * ti + (lane & 15);
-        const uint4 a0 = *reinterpret_cast<const uint4*>(sA + sw128(r, q));
-        const uint4 a1 = *reinterpret_cast<const uint4*>(sA + sw128(r, q + 4));
-        tv[ti] = (v8i_t){(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                         (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        const float x = sX[r];
-        cx[ti] = x;
-        cy[ti] = x;
-      }
-      if (FMT == 2) {
-        const float f0 = s_wsc[GU ? 0 : wn][kr(ks)];
-        const float f1 = GU ? s_wsc[1][kr(ks)] : f0;
-#pragma unroll
-        for (int ti = 0; ti < NT; ++ti) {
-          cy[ti] = cx[ti] * f1;
-          cx[ti] = cx[ti] * f0;
-        }
-      }
       auto read_w = [&](int i, v8i_t& wv, int& sw) {
         const int n = wrow(i);
         if (FMT == 1) {
@@ -329,10 +321,43 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
           sw = 127;
         }
       };
-      const v4f_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+      // LDS reads in the order of first use (the hardware returns them in
+      // order): the scales (a few bytes; the first fold needs them), weight
+      // fragment 0, then the wave's 4 token fragments, so that the first
+      // MFMA waits only for its own two fragments
+      float cx[NT], cy[NT];
+#pragma unroll
+      for (int ti = 0; ti < NT; ++ti) {
+        const float x = sX[wt * (TM / 4) + 16 * ti + (lane & 15)];
+        cx[ti] = x;
+        cy[ti] = x;
+      }
+      float f0 = 1.0f, f1 = 1.0f;
+      if (FMT == 2) {
+        // the FP8 weight block scales: gate / up halves (down: this wave's rows)
+        f0 = s_wsc[GU ? 0 : wn][kr(ks)];
+        f1 = GU ? s_wsc[1][kr(ks)] : f0;
+      }
       v8i_t wv[2];
       int sw[2];
       read_w(0, wv[0], sw[0]);
+      v8i_t tv[NT];
+#pragma unroll
+      for (int ti = 0; ti < NT; ++ti) {
+        const int r = wt * (TM / 4) + 16 * ti + (lane & 15);
+        const uint4 a0 = *reinterpret_cast<const uint4*>(sA + sw128(r, q));
+        const uint4 a1 = *reinterpret_cast<const uint4*>(sA + sw128(r, q + 4));
+        tv[ti] = (v8i_t){(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                         (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      }
+      if (FMT == 2) {
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) {
+          cy[ti] = cx[ti] * f1;
+          cx[ti] = cx[ti] * f0;
+        }
+      }
+      const v4f_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         // fragment i+1 is read while fragment i multiplies
