@@ -131,8 +131,10 @@ int launch_status(hipError_t e) {
   return MOE_OK;
 }
 
+// T = 0 is an empty batch: valid, and the entry points return MOE_OK after
+// checking their other arguments, reading, writing and launching nothing.
 int check_tk(int T, int k, int E) {
-  if (T < 1 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
+  if (T < 0 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
   if (E > 256 || k > 16) return MOE_ENOTSUP;
   return MOE_OK;
 }
@@ -250,7 +252,7 @@ using namespace bef;
 extern "C" {
 
 size_t moe_workspace_bytes(const moe_weights* w, int32_t max_tokens, int32_t top_k) {
-  if (check_weights(w) != MOE_OK) return 0;
+  if (check_weights(w) != MOE_OK || max_tokens < 1) return 0;
   if (check_tk(max_tokens, top_k, w->n_experts) != MOE_OK) return 0;
   size_t a = layout_w(w, max_tokens, top_k).total;
   size_t b = layout_w(w, 1, top_k).total;
@@ -275,6 +277,7 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H,
   if (rc) return rc;
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(topk_ids) || !aligned16(topk_w))
     return MOE_EALIGN;
+  if (T == 0) return MOE_OK;
   const Layout L = layout_for(E, H, 128, T, k, false);
   rc = check_ws(ws, ws_bytes, L.end_route);
   if (rc) return rc;
@@ -290,9 +293,10 @@ int act_quant_fp8(const void* x, int32_t x_dtype, int64_t rows, int32_t cols, ui
                   float* scales, void* stream) {
   if (!x || !q || !scales) return MOE_EINVAL;
   if (x_dtype != MOE_DT_BF16 && x_dtype != MOE_DT_F32) return MOE_EINVAL;
-  if (rows < 1 || cols < 128 || cols % 128 != 0) return MOE_EINVAL;
+  if (rows < 0 || cols < 128 || cols % 128 != 0) return MOE_EINVAL;
   if (rows * (int64_t)(cols / 128) * 16 > (int64_t)0x7fffffff * 256) return MOE_ENOTSUP;
   if (!aligned16(x) || !aligned16(q) || !aligned16(scales)) return MOE_EALIGN;
+  if (rows == 0) return MOE_OK;
   int rc = check_device();
   if (rc) return rc;
   return launch_status(
@@ -306,6 +310,7 @@ int moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_
   if (rc) return rc;
   if (!aligned16(topk_ids) || !aligned16(offsets) || !aligned16(row_token) || !aligned16(row_of))
     return MOE_EALIGN;
+  if (T == 0) return MOE_OK;
   const Layout L = layout_for(E, 128, 128, T, k, false);
   rc = check_ws(ws, ws_bytes, L.end_permute);
   if (rc) return rc;
@@ -328,6 +333,7 @@ int moe_expert_ffn(const moe_weights* w, const uint8_t* xq, const float* xs, int
   if (!aligned16(xq) || !aligned16(xs) || !aligned16(offsets) || !aligned16(row_token) ||
       !aligned16(y_rows))
     return MOE_EALIGN;
+  if (T == 0) return MOE_OK;
   const Layout L = layout_w(w, T, k);
   rc = check_ws(ws, ws_bytes, L.end_ffn);
   if (rc) return rc;
@@ -349,6 +355,7 @@ int moe_expert_gate_up(const moe_weights* w, const uint8_t* xq, const float* xs,
   if (rc) return rc;
   if (!aligned16(xq) || !aligned16(xs) || !aligned16(offsets) || !aligned16(row_token))
     return MOE_EALIGN;
+  if (T == 0) return MOE_OK;
   const Layout L = layout_w(w, T, k);
   rc = check_ws(ws, ws_bytes, L.end_ffn);
   if (rc) return rc;
@@ -373,6 +380,7 @@ int moe_expert_down(const moe_weights* w, int32_t T, int32_t k, const int32_t* o
   }
   if (!y_rows && !(gv && out)) return MOE_EINVAL;
   if (!aligned16(offsets) || (y_rows && !aligned16(y_rows))) return MOE_EALIGN;
+  if (T == 0) return MOE_OK;
   const Layout L = layout_w(w, T, k);
   rc = check_ws(ws, ws_bytes, L.end_ffn);
   if (rc) return rc;
@@ -385,13 +393,14 @@ int moe_expert_down(const moe_weights* w, int32_t T, int32_t k, const int32_t* o
 int moe_combine(const float* y_rows, const int32_t* row_of, const float* topk_w, int32_t T,
                 int32_t k, int32_t H, void* out, int32_t out_dtype, void* stream) {
   if (!y_rows || !row_of || !topk_w || !out) return MOE_EINVAL;
-  if (T < 1 || k < 1) return MOE_EINVAL;
+  if (T < 0 || k < 1) return MOE_EINVAL;
   if (k > 16) return MOE_ENOTSUP;
   int rc = check_hidden(H);
   if (rc) return rc;
   if (out_dtype != MOE_DT_BF16 && out_dtype != MOE_DT_F32) return MOE_EINVAL;
   if (!aligned16(y_rows) || !aligned16(row_of) || !aligned16(topk_w) || !aligned16(out))
     return MOE_EALIGN;
+  if (T == 0) return MOE_OK;
   rc = check_device();
   if (rc) return rc;
   return launch_status(
@@ -413,6 +422,7 @@ int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint1
   if (!aligned16(x) || !aligned16(out) || (w_router && !aligned16(w_router)) ||
       (routing_ids && (!aligned16(routing_ids) || !aligned16(routing_w))))
     return MOE_EALIGN;
+  if (T == 0) return MOE_OK;
   const Layout L = layout_w(w, T, k);
   rc = check_ws(ws, ws_bytes, L.total);
   if (rc) return rc;
@@ -540,6 +550,7 @@ int moe_debug_intermediates(const moe_weights* w, int32_t T, int32_t k, void* ws
   if (rc) return rc;
   rc = check_tk(T, k, w->n_experts);
   if (rc) return rc;
+  if (T == 0) return MOE_EINVAL;  // an empty batch leaves no intermediates
   const Layout L = layout_w(w, T, k);
   rc = check_ws(ws, ws_bytes, L.end_ffn);
   if (rc) return rc;

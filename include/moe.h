@@ -34,9 +34,12 @@
  *  - Calls are reentrant for distinct workspaces; two calls in flight on the
  *    same workspace race.
  *  - Limits: 1 <= E <= 256, 1 <= k <= min(E, 16), H and I multiples of 128,
- *    128 <= H <= 8192, 128 <= I <= 8192, T >= 1 (MOE_ENOTSUP beyond the
+ *    128 <= H <= 8192, 128 <= I <= 8192, T >= 0 (MOE_ENOTSUP beyond the
  *    size limits, MOE_EINVAL for malformed values).  The device must be a
  *    gfx950 (MOE_ENOTSUP otherwise).
+ *  - T = 0 (rows = 0 for act_quant_fp8) is an empty batch: the other
+ *    arguments are checked as usual, then MOE_OK is returned with nothing
+ *    read, written or enqueued (no device is needed for that answer).
  */
 #ifndef BEF_MOE_H
 #define BEF_MOE_H
@@ -97,7 +100,8 @@ typedef struct moe_weights {
 
 /* Bytes of workspace needed by any call below for up to `max_tokens` tokens
  * at top-k `top_k` (router partials, quantised activations, routing tables,
- * intermediate h, y rows, status word).  0 if the arguments are invalid.
+ * intermediate h, y rows, status word).  0 if the arguments are invalid or
+ * max_tokens < 1.
  * Allocate once, call moe_workspace_init once, then reuse for every call
  * (dpshk.com article, section "核心实现四": workspaces preallocated). */
 size_t moe_workspace_bytes(const moe_weights* w, int32_t max_tokens, int32_t top_k);
@@ -132,7 +136,7 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H,
  *   x      [rows][cols] bf16 (x_dtype MOE_DT_BF16) or f32 (MOE_DT_F32)
  *   q      [rows][cols] u8 E4M3 codes out
  *   scales [rows][cols/128] f32 out
- * cols must be a multiple of 128; rows >= 1. */
+ * cols must be a multiple of 128; rows >= 0. */
 int act_quant_fp8(const void* x, int32_t x_dtype, int64_t rows, int32_t cols, uint8_t* q,
                   float* scales, void* stream);
 
@@ -206,7 +210,8 @@ int moe_device_status(void* ws, void* stream, uint32_t* status, int clear);
 /* DEBUG/TESTS ONLY -- device pointers to the intermediate activations that
  * the last moe_expert_ffn / dsv4_moe_forward call with the same (w, T, k)
  * left in `ws`: h [T*k+T][I] f32 (VALU path only, else NULL), and
- * hq [T*k+T][I] u8 with hs [T*k+T][I/128] f32 (both paths). */
+ * hq [T*k+T][I] u8 with hs [T*k+T][I/128] f32 (both paths).  T >= 1 (an
+ * empty batch leaves none: MOE_EINVAL). */
 int moe_debug_intermediates(const moe_weights* w, int32_t T, int32_t k, void* ws,
                             size_t ws_bytes, float** h, uint8_t** hq, float** hs);
 

@@ -130,7 +130,7 @@ def test_act_quant_rejects_bad_arguments_on_host():
     f = moe._lib.act_quant_fp8
     assert f(p, 1, 4, 100, p, p, None) == moe.MOE_EINVAL       # cols % 128
     assert f(p, 5, 4, 128, p, p, None) == moe.MOE_EINVAL       # dtype
-    assert f(p, 1, 0, 128, p, p, None) == moe.MOE_EINVAL       # rows
+    assert f(p, 1, -1, 128, p, p, None) == moe.MOE_EINVAL      # rows
     assert f(p + 2, 1, 4, 128, p, p, None) == moe.MOE_EALIGN
     assert f(None, 1, 4, 128, p, p, None) == moe.MOE_EINVAL
 
@@ -147,3 +147,38 @@ def test_python_binding_raises_on_error_status():
     with pytest.raises(moe.MoeError) as ei:
         moe.act_quant_fp8(0x100000, 1, 4, 100, 0x100000, 0x100000, stream=0)
     assert ei.value.status == moe.MOE_EINVAL
+
+
+def test_empty_batch_is_accepted_without_a_device():
+    """T = 0 (rows = 0): the other arguments are still checked, then MOE_OK
+    with nothing enqueued -- so the answer needs no GPU; T < 0 is invalid."""
+    p, ws, big = 0x100000, 0x200000, 1 << 30
+    w = _w(ptr=p)
+    L = moe._lib
+    wb = ctypes.byref(w)
+    assert L.moe_route(p, p, 0, 4096, 256, 6, p, p, ws, big, None) == moe.MOE_OK
+    assert L.act_quant_fp8(p, moe.MOE_DT_BF16, 0, 4096, p, p, None) == moe.MOE_OK
+    assert L.moe_permute(p, 0, 6, 256, p, p, p, ws, big, None) == moe.MOE_OK
+    assert L.moe_expert_ffn(wb, p, p, 0, 6, p, p, p, ws, big, None) == moe.MOE_OK
+    assert L.moe_expert_gate_up(wb, p, p, 0, 6, p, p, ws, big, None) == moe.MOE_OK
+    assert L.moe_expert_down(wb, 0, 6, p, p, p, p, p, moe.MOE_DT_F32, ws, big,
+                             None) == moe.MOE_OK
+    assert L.moe_combine(p, p, p, 0, 6, 4096, p, moe.MOE_DT_F32, None) == moe.MOE_OK
+    assert L.dsv4_moe_forward(wb, p, p, 0, 6, None, None, p, moe.MOE_DT_F32, ws, big,
+                              None) == moe.MOE_OK
+    # the other arguments are still validated for an empty batch
+    assert L.moe_route(None, p, 0, 4096, 256, 6, p, p, ws, big, None) == moe.MOE_EINVAL
+    assert L.moe_route(p, p, 0, 4096, 256, 6, p + 4, p, ws, big, None) == moe.MOE_EALIGN
+    assert L.act_quant_fp8(p, moe.MOE_DT_BF16, 0, 100, p, p, None) == moe.MOE_EINVAL
+    assert L.dsv4_moe_forward(wb, p, p, 0, 17, None, None, p, moe.MOE_DT_F32, ws, big,
+                              None) == moe.MOE_ENOTSUP
+    # negative sizes are not
+    assert L.moe_route(p, p, -1, 4096, 256, 6, p, p, ws, big, None) == moe.MOE_EINVAL
+    assert L.act_quant_fp8(p, moe.MOE_DT_BF16, -1, 4096, p, p, None) == moe.MOE_EINVAL
+    assert L.moe_combine(p, p, p, -1, 6, 4096, p, moe.MOE_DT_F32, None) == moe.MOE_EINVAL
+    assert L.dsv4_moe_forward(wb, p, p, -1, 6, None, None, p, moe.MOE_DT_F32, ws, big,
+                              None) == moe.MOE_EINVAL
+    # no intermediates for an empty batch
+    h = ctypes.c_void_p()
+    assert L.moe_debug_intermediates(wb, 0, 6, ws, big, ctypes.byref(h), None,
+                                     None) == moe.MOE_EINVAL

@@ -223,3 +223,23 @@ def test_bad_expert_id_is_skipped_and_flagged():
     ids[3, 1] = 0          # weight 0: same as skipping the slot
     ref = orc.forward(Weights.from_layer(L), L.wr, L.x, 2, ids=ids, w=w)
     _check(out, ref, "bad id")
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
+def test_empty_batch_then_a_real_one(fmt):
+    """T = 0 enqueues nothing: the output buffer keeps its contents and the
+    workspace stays clean; the next call with tokens is unaffected."""
+    L = synth.make_layer("tiny_t8", fmt=fmt)
+    D = DevLayer(L)
+    sentinel = torch.full((1, L.wl.H), 7.0, dtype=torch.float32, device="cuda:0")
+    moe.dsv4_moe_forward(D.w, D.wr, D.x, 0, L.wl.k, None, None, sentinel, moe.MOE_DT_F32, D.ws,
+                         D.ws_bytes)
+    xq = torch.full((1, L.wl.H), 5, dtype=torch.uint8, device="cuda:0")
+    xs = torch.full((1, L.wl.H // 128), 3.0, dtype=torch.float32, device="cuda:0")
+    moe.act_quant_fp8(D.x, moe.MOE_DT_BF16, 0, L.wl.H, xq, xs)
+    assert (to_host(sentinel) == 7.0).all()
+    assert (to_host(xq) == 5).all() and (to_host(xs) == 3.0).all()
+    assert moe.moe_device_status(D.ws) == 0
+    out = to_host(D.forward(injected=False))
+    ref = orc.forward(Weights.from_layer(L), L.wr, L.x, L.wl.k)
+    _check(out, ref, f"after an empty batch ({fmt})")
