@@ -243,3 +243,14 @@ def test_empty_batch_then_a_real_one(fmt):
     out = to_host(D.forward(injected=False))
     ref = orc.forward(Weights.from_layer(L), L.wr, L.x, L.wl.k)
     _check(out, ref, f"after an empty batch ({fmt})")
+
+
+@pytest.mark.parametrize("over", [
+    dict(fmt="fp4", T=1, H=8192, I=4096),   # the one-token VALU path at its largest shape
+    dict(fmt="fp4", T=3, H=8192, I=8192),   # the MFMA path at the ABI's limits
+    dict(fmt="fp8", T=3, H=8192, I=8192),
+])
+def test_maximum_hidden_and_intermediate(over):
+    """H and I at the largest values the ABI accepts (two routed experts keep
+    the weights and the oracle small); the router runs on x."""
+    _run("tiny_t8", E=2, k=2, threads=16, **over)
