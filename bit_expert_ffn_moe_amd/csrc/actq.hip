@@ -5,7 +5,9 @@
 //
 // HBM-bound elementwise work: one 128-block per 16 lanes, 8 consecutive
 // elements per lane (16 B of bf16 or 32 B of f32 in, 8 B of codes out), the
-// block max reduced across the 16 lanes with lane shuffles.  No LDS.
+// block max reduced across the 16 lanes by cross-lane steps (actq.h).  No
+// LDS.
+#include "actq.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -15,46 +17,7 @@ template <bool BF16>
 __global__ __launch_bounds__(256) void act_quant_kernel(const void* __restrict__ x,
                                                         int64_t nblocks, uint8_t* __restrict__ q,
                                                         float* __restrict__ s) {
-  const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t blk = gt >> 4;
-  const int sub = threadIdx.x & 15;
-  const bool valid = blk < nblocks;
-  float v[8];
-  if (valid) {
-    if (BF16) {
-      const uint4 r = reinterpret_cast<const uint4*>(x)[gt];
-      v[0] = bf16_to_f32(r.x & 0xffffu);
-      v[1] = bf16_to_f32(r.x >> 16);
-      v[2] = bf16_to_f32(r.y & 0xffffu);
-      v[3] = bf16_to_f32(r.y >> 16);
-      v[4] = bf16_to_f32(r.z & 0xffffu);
-      v[5] = bf16_to_f32(r.z >> 16);
-      v[6] = bf16_to_f32(r.w & 0xffffu);
-      v[7] = bf16_to_f32(r.w >> 16);
-    } else {
-      const float4 a = reinterpret_cast<const float4*>(x)[2 * gt];
-      const float4 b = reinterpret_cast<const float4*>(x)[2 * gt + 1];
-      v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w;
-      v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  amax = group_max<16>(amax);
-  const float sc = amax / 448.0f;
-  uint32_t lo = 0, hi = 0;
-  if (amax != 0.0f) {
-    lo = e4m3_pack4(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
-    hi = e4m3_pack4(v[4] / sc, v[5] / sc, v[6] / sc, v[7] / sc);
-  }
-  if (valid) {
-    reinterpret_cast<uint2*>(q)[gt] = make_uint2(lo, hi);
-    if (sub == 0) s[blk] = sc;
-  }
+  act_quant_lanes<BF16>(x, nblocks, q, s, (int64_t)blockIdx.x * 256 + threadIdx.x);
 }
 
 hipError_t launch_act_quant(const void* x, bool bf16, int64_t rows, int32_t cols, uint8_t* q,

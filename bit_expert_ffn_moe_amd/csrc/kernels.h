@@ -84,8 +84,11 @@ hipError_t launch_route_front(const FrontArgs& a, hipStream_t st);
 hipError_t launch_act_quant(const void* x, bool bf16, int64_t rows, int32_t cols, uint8_t* q,
                             float* s, hipStream_t st);
 // T > kRouteSmallT needs gsum: (H/256) * T * E floats of workspace (group sums).
+// xq/xs set: the act_quant of x runs in the same launch (T > kRouteSmallT) or
+// in the front kernel (T <= kRouteSmallT).
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int H, int E, int k,
-                        int32_t* ids, float* w, WsCtl* ctl, float* gsum, hipStream_t st);
+                        int32_t* ids, float* w, WsCtl* ctl, float* gsum, hipStream_t st,
+                        uint8_t* xq = nullptr, float* xs = nullptr);
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
                           int32_t* row_token, int32_t* row_of, int32_t* cnt, int32_t* base,
                           uint32_t* status, hipStream_t st);

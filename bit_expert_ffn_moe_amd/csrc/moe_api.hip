@@ -483,15 +483,18 @@ int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint1
                         ws, st);
   }
   if (!ids) {
+    // router, with the act_quant of x in the same launch
     int32_t* ids_ws = at<int32_t>(ws, L.ids);
     float* w_ws = at<float>(ws, L.w);
-    rc = launch_status(launch_route(x, w_router, T, H, E, k, ids_ws, w_ws, ctl, at<float>(ws, L.gsum), st));
+    rc = launch_status(launch_route(x, w_router, T, H, E, k, ids_ws, w_ws, ctl,
+                                    at<float>(ws, L.gsum), st, xq, xs));
     if (rc) return rc;
     ids = ids_ws;
     tw = w_ws;
+  } else {
+    rc = launch_status(launch_act_quant(x, true, T, H, xq, xs, st));
+    if (rc) return rc;
   }
-  rc = launch_status(launch_act_quant(x, true, T, H, xq, xs, st));
-  if (rc) return rc;
   rc = launch_status(launch_permute(ids, T, k, E, offsets, row_token, row_of,
                                     at<int32_t>(ws, L.cnt), at<int32_t>(ws, L.base),
                                     &ctl->status, st));

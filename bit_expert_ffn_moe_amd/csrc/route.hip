@@ -17,6 +17,7 @@
 #include <float.h>
 #include <limits.h>
 
+#include "actq.h"
 #include "common.h"
 #include "gemv_body.h"
 #include "kernels.h"
@@ -141,35 +142,7 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
   }
   if (b >= 0) {
     // act_quant of x: 16 lanes per 128-block, 8 elements per lane
-    const int64_t gt = (int64_t)b * 256 + tid;
-    const int64_t blk = gt >> 4;
-    const int64_t nblocks = (int64_t)T * (H / 128);
-    const bool valid = blk < nblocks;
-    float v[8];
-    if (valid) {
-      const uint4 r = reinterpret_cast<const uint4*>(a.x)[gt];
-      v[0] = bf16_to_f32(r.x & 0xffffu), v[1] = bf16_to_f32(r.x >> 16);
-      v[2] = bf16_to_f32(r.y & 0xffffu), v[3] = bf16_to_f32(r.y >> 16);
-      v[4] = bf16_to_f32(r.z & 0xffffu), v[5] = bf16_to_f32(r.z >> 16);
-      v[6] = bf16_to_f32(r.w & 0xffffu), v[7] = bf16_to_f32(r.w >> 16);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = group_max<16>(amax);
-    const float sc = amax / 448.0f;
-    uint32_t lo = 0, hi = 0;
-    if (amax != 0.0f) {
-      lo = e4m3_pack4(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
-      hi = e4m3_pack4(v[4] / sc, v[5] / sc, v[6] / sc, v[7] / sc);
-    }
-    if (valid) {
-      reinterpret_cast<uint2*>(a.xq)[gt] = make_uint2(lo, hi);
-      if ((tid & 15) == 0) a.xs[blk] = sc;
-    }
+    act_quant_lanes<true>(a.x, (int64_t)T * (H / 128), a.xq, a.xs, (int64_t)b * 256 + tid);
     return;
   }
   // router block (group g, quarter q): rows 256g .. 256g+255 (chunks 4g ..
@@ -331,6 +304,21 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
   }
 }
 
+// The act_quant of x riding along the router launch of 4 < T < kRouteSplitT
+// tokens: blocks past the router's groups in x run thread-blocks b < nb of
+// the act_quant kernel's range (b counts over the extra blocks in launch
+// order); q == nullptr: none.
+struct ActQuantArgs {
+  const uint16_t* x;
+  uint8_t* q;
+  float* s;
+  int64_t nblocks;  // 128-element blocks of x
+  int64_t nb;       // act_quant thread-blocks of 256 threads
+  __device__ __forceinline__ void run(int64_t b, int tid) const {
+    if (q && b < nb) act_quant_lanes<true>(x, nblocks, q, s, b * 256 + tid);
+  }
+};
+
 // ---------------------------------------------------------------------------
 // T > 4, in two kernels.  route_group_kernel: block (g, tile) owns tokens
 // 32 tile .. +31, all E (<= 256) experts and rows 256 g .. 256 g + 255 (chunks
@@ -458,11 +446,16 @@ __global__ __launch_bounds__(256) void route_group_kernel(const uint16_t* __rest
 // experts 64 quarter + 8tx .. +7 in the same fixed order.
 __global__ __launch_bounds__(256) void route_group_quarter_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int H, int E,
-    float* __restrict__ gsum) {
+    float* __restrict__ gsum, ActQuantArgs aq) {
   __shared__ __align__(16) float sx[32][68];   // [token][h of the chunk], padded rows
   __shared__ __align__(16) float sw[64][64];   // [h of the chunk][expert of the quarter]
   const int g = blockIdx.x, e00 = 64 * blockIdx.y, t0 = blockIdx.z * 32;
   const int tid = threadIdx.x;
+  const int ng = (H / 64 + 3) / 4;
+  if (g >= ng) {
+    aq.run(((int64_t)(g - ng) * gridDim.z + blockIdx.z) * gridDim.y + blockIdx.y, tid);
+    return;
+  }
   const int ty = tid >> 3, tx = tid & 7;
   const int nc = H / 64;
   const int c0 = 4 * g, c1 = min(4 * g + 4, nc);
@@ -572,23 +565,36 @@ __global__ __launch_bounds__(256) void route_reduce_kernel(const float* __restri
 }
 
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int H, int E, int k,
-                        int32_t* ids, float* w, WsCtl* ctl, float* gsum, hipStream_t st) {
+                        int32_t* ids, float* w, WsCtl* ctl, float* gsum, hipStream_t st,
+                        uint8_t* xq, float* xs) {
   if (T <= kRouteSmallT) {
     FrontArgs a = {};
     a.x = x, a.wr = wr, a.T = T, a.H = H, a.E = E, a.k = k;
     a.ids = ids, a.w = w;
+    a.xq = xq, a.xs = xs;
     set_route_sync(a, ctl);
     return launch_route_front(a, st);
   }
   if (!gsum || E > 256 || H % 64 != 0 || (H / 64 + 3) / 4 > kRouteMaxGroups)
     return hipErrorInvalidValue;
   const int ng = (H / 64 + 3) / 4;
-  if (T < kRouteSplitT)
-    route_group_quarter_kernel<<<dim3(ng, (E + 63) / 64, (T + 31) / 32), dim3(256), 0, st>>>(
-        x, wr, T, H, E, gsum);
-  else
+  if (T < kRouteSplitT) {
+    // act_quant of x (when xq is set) in extra x-slices of the router's grid:
+    // one launch fewer.  (Not at more tokens: extra blocks of
+    // route_group_kernel would each hold its 73 KB of LDS and crowd out the
+    // router blocks -- measured at 8192 tokens, +42 us; a launch of its own
+    // follows instead.)
+    ActQuantArgs aq = {x, xq, xs, (int64_t)T * (H / 128), 0};
+    if (xq) aq.nb = (aq.nblocks * 16 + 255) / 256;
+    const int ny = (E + 63) / 64, nz = (T + 31) / 32;
+    const int nqx = (int)((aq.nb + ny * nz - 1) / (ny * nz));
+    route_group_quarter_kernel<<<dim3(ng + nqx, ny, nz), dim3(256), 0, st>>>(x, wr, T, H, E,
+                                                                            gsum, aq);
+  } else {
     route_group_kernel<<<dim3(ng, (T + 31) / 32), dim3(256), 0, st>>>(x, wr, T, H, E, gsum);
+  }
   route_reduce_kernel<<<dim3((T + 3) / 4), dim3(256), 0, st>>>(gsum, T, H, E, k, ids, w);
+  if (xq && T >= kRouteSplitT) return launch_act_quant(x, true, T, H, xq, xs, st);
   return hipGetLastError();
 }
 
