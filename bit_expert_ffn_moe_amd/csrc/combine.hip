@@ -16,8 +16,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ topk_w, int T,
                                                       int k, int H, void* __restrict__ out) {
-  const int t = blockIdx.y;
-  const int m4 = blockIdx.x * 256 + threadIdx.x;
+  const int t = blockIdx.x;  // tokens in x: more than 65535 of them are valid
+  const int m4 = blockIdx.y * 256 + threadIdx.x;
   if (4 * m4 >= H) return;
   const int32_t* ro = row_of + (size_t)t * (k + 1);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 hipError_t launch_combine(const float* y, const int32_t* row_of, const float* topk_w, int T, int k,
                           int H, void* out, bool bf16, hipStream_t st) {
-  const dim3 grid((H / 4 + 255) / 256, T);
+  const dim3 grid(T, (H / 4 + 255) / 256);
   if (bf16)
     combine_kernel<true><<<grid, 256, 0, st>>>(y, row_of, topk_w, T, k, H, out);
   else

@@ -133,9 +133,13 @@ int launch_status(hipError_t e) {
 
 // T = 0 is an empty batch: valid, and the entry points return MOE_OK after
 // checking their other arguments, reading, writing and launching nothing.
+// At most 2^18 tokens per call: the kernels address a token's row of x or xq
+// (T x H bytes, H <= 8192) with 32-bit offsets.
+constexpr int kMaxTokens = 1 << 18;
+
 int check_tk(int T, int k, int E) {
   if (T < 0 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
-  if (E > 256 || k > 16) return MOE_ENOTSUP;
+  if (E > 256 || k > 16 || T > kMaxTokens) return MOE_ENOTSUP;
   return MOE_OK;
 }
 

@@ -34,8 +34,8 @@
  *  - Calls are reentrant for distinct workspaces; two calls in flight on the
  *    same workspace race.
  *  - Limits: 1 <= E <= 256, 1 <= k <= min(E, 16), H and I multiples of 128,
- *    128 <= H <= 8192, 128 <= I <= 8192, T >= 0 (MOE_ENOTSUP beyond the
- *    size limits, MOE_EINVAL for malformed values).  The device must be a
+ *    128 <= H <= 8192, 128 <= I <= 8192, 0 <= T <= 262144 (MOE_ENOTSUP
+ *    beyond the size limits, MOE_EINVAL for malformed values).  The device must be a
  *    gfx950 (MOE_ENOTSUP otherwise).
  *  - T = 0 (rows = 0 for act_quant_fp8) is an empty batch: the other
  *    arguments are checked as usual, then MOE_OK is returned with nothing

@@ -182,3 +182,18 @@ def test_empty_batch_is_accepted_without_a_device():
     h = ctypes.c_void_p()
     assert L.moe_debug_intermediates(wb, 0, 6, ws, big, ctypes.byref(h), None,
                                      None) == moe.MOE_EINVAL
+
+
+def test_token_count_limit():
+    """At most 2^18 tokens per call (32-bit row offsets of x in the kernels):
+    one more is refused on the host with MOE_ENOTSUP."""
+    p, ws, big = 0x100000, 0x200000, 1 << 45
+    w = _w(ptr=p)
+    wb = ctypes.byref(w)
+    L = moe._lib
+    assert moe.moe_workspace_bytes(w, 1 << 18, 6) > 0
+    assert moe.moe_workspace_bytes(w, (1 << 18) + 1, 6) == 0
+    assert L.dsv4_moe_forward(wb, p, p, (1 << 18) + 1, 6, None, None, p, moe.MOE_DT_F32, ws,
+                              big, None) == moe.MOE_ENOTSUP
+    assert L.moe_route(p, p, (1 << 18) + 1, 4096, 256, 6, p, p, ws, big, None) == moe.MOE_ENOTSUP
+    assert L.moe_permute(p, (1 << 18) + 1, 6, 256, p, p, p, ws, big, None) == moe.MOE_ENOTSUP

@@ -254,3 +254,10 @@ def test_maximum_hidden_and_intermediate(over):
     """H and I at the largest values the ABI accepts (two routed experts keep
     the weights and the oracle small); the router runs on x."""
     _run("tiny_t8", E=2, k=2, threads=16, **over)
+
+
+def test_more_tokens_than_a_grid_row():
+    """70,000 tokens (past 65,535, the largest grid y extent): the router,
+    permute, grouped GEMM and combine launches index tokens where the grid
+    allows that many; checked on a sample that includes the last token."""
+    _run("tiny_t8", T=70000, sample=16, threads=16)
