@@ -144,9 +144,8 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
   constexpr int NAI = KB_A / 8192;                         // A DMA instructions per wave
   constexpr int NBI = KB_B / 8192;                         // B DMA instructions per wave
   constexpr int kLoads = NAI + NBI + (FMT == 1 ? 1 : 0) + 1;  // + FP4 scales + act scales
-  // stage buffers, separate LDS objects (the compiler tracks LDS DMA per
-  // object): activation codes, weight codes, FP4 weight scales (4 UE8M0
-  // bytes per weight row), activation scales of the K step
+  // stage buffers: activation codes, weight codes, FP4 weight scales (4
+  // UE8M0 bytes per weight row), activation scales of the K step
 #define BEF_STAGE(i)                                                        \
   __shared__ __align__(16) uint8_t sA##i[NST > i ? KB_A : 16];              \
   __shared__ __align__(16) uint8_t sB##i[NST > i ? KB_B : 16];              \
