@@ -286,8 +286,10 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
     // N-block), so the M-tiles that stream the same weight rows -- running
     // side by side on one XCD -- read them in step and share them in its L2
     // (4096-token FP4 prefill, whose hot experts and shared expert have many
-    // M-tiles: gate+up -2.3%).
-    const int rot = s_mtp[g + 1] - s_mtp[g] > 1 ? g * NB + nb : wi;
+    // M-tiles: gate+up -2.3%).  Pairs of neighbouring items share a start, so
+    // that two N-blocks read a token tile's K steps together (verify_t32 and
+    // both prefills: -0.3 to -0.6%).
+    const int rot = (s_mtp[g + 1] - s_mtp[g] > 1 ? g * NB + nb : wi) >> 1;
     const int ks0 = (int)(((uint32_t)rot * 7u) % (uint32_t)KS);
     auto kr = [&](int ks) {
       const int k = ks + ks0;
