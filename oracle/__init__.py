@@ -64,6 +64,7 @@ def _bind(lib):
     lib.orc_act_quant_bf16.argtypes = [vp, i64, i32, vp, vp]
     lib.orc_router_logits.argtypes = [vp, vp, i32, i32, i32, vp]
     lib.orc_topk.argtypes = [vp, i32, i32, i32, vp, vp]
+    lib.orc_topk_weights.argtypes = [vp, i32, i32, i32, vp, vp]
     lib.orc_permute.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     lib.orc_permute.restype = ctypes.c_int
     lib.orc_weight.argtypes = [ctypes.POINTER(_W), ctypes.c_int, i32, i32, i32]
@@ -156,6 +157,17 @@ class Oracle:
         w = np.empty((T, k), np.float64)
         self.lib.orc_topk(_p(z), T, E, k, _p(ids), _p(w))
         return ids, w
+
+    def topk_weights(self, z, ids):
+        """Renormalised sigmoid weights of a given selection ids [T][k]."""
+        z = np.ascontiguousarray(z, np.float32)
+        ids = np.ascontiguousarray(ids, np.int32)
+        T, E = z.shape
+        k = ids.shape[1]
+        assert ids.min() >= 0 and ids.max() < E
+        w = np.empty((T, k), np.float64)
+        self.lib.orc_topk_weights(_p(z), T, E, k, _p(ids), _p(w))
+        return w
 
     def route(self, x, wr, k):
         return self.topk(self.router_logits(x, wr), k)

@@ -80,6 +80,8 @@ void orc_act_quant_bf16(const uint16_t* x, int64_t rows, int32_t cols, uint8_t* 
 void orc_router_logits(const uint16_t* x, const uint16_t* wr, int32_t T, int32_t H, int32_t E,
                        float* z);
 void orc_topk(const float* z, int32_t T, int32_t E, int32_t k, int32_t* ids, double* w);
+void orc_topk_weights(const float* z, int32_t T, int32_t E, int32_t k, const int32_t* ids,
+                      double* w);
 
 /* ---- S4: permutation ---------------------------------------------------- */
 int orc_permute(const int32_t* ids, int32_t T, int32_t k, int32_t E, int32_t* offsets,

@@ -29,25 +29,46 @@ def test_router_logits_within_fp32_bound_of_exact_sum():
     assert np.all(np.abs(z - exact) <= bound)
 
 
-def test_router_sum_order_groups_four_chunks():
+def test_router_sum_order_is_one_ascending_chain():
     """Worked case of the fixed order: x = 1, H = 512 (8 chunks of 64).
-    Expert 0: chunk 0 sums to 2^24 and chunks 4..7 to 1 each.  The group of
-    chunks 4..7 reaches 4 before it meets 2^24, so z = 2^24 + 4 exactly (one
-    running sum over the chunks would drop every +1 and give 2^24).  Expert
-    1 holds the same values in the reverse order: 1 + 1 + 1 + 1 = 4 in group
-    0, then 4 + 2^24."""
-    H, E = 512, 2
-    x = np.full((1, H), 0x3F80, np.uint16)           # bf16 1.0
+    Expert 0: chunk 0 sums to 2^24 and chunks 4..7 to 1 each.  One running
+    sum over the chunk partials in ascending order meets 2^24 first, and
+    2^24 + 1 rounds back to 2^24 (a tie, to the even significand), so every
+    +1 is dropped: z = 2^24 (a sum of the last four chunks first would keep
+    them: 2^24 + 4).  Expert 1 holds the same values in the reverse order:
+    1 + 1 + 1 + 1 = 4 first, then 4 + 2^24 = 2^24 + 4 exactly.  Expert 2:
+    inside chunk 0, h = 0 holds 2^24 and h = 1..4 hold 1: ascending h drops
+    each 1, z = 2^24.  Expert 3: the same inside chunk 0 in the reverse
+    order (h = 0..3 hold 1, h = 4 holds 2^24): z = 2^24 + 4."""
+    H, E = 512, 4
+    one, big = 0x3F80, 0x4B80                          # bf16 1.0 and 2^24
+    x = np.full((1, H), one, np.uint16)
     wr = np.zeros((H, E), np.uint16)
-    wr[5, 0] = 0x4B80                                  # bf16 2^24
+    wr[5, 0] = big
     for c in range(4, 8):
-        wr[64 * c + 7, 0] = 0x3F80
+        wr[64 * c + 7, 0] = one
     for c in range(4):
-        wr[64 * c + 3, 1] = 0x3F80
-    wr[64 * 6 + 1, 1] = 0x4B80
+        wr[64 * c + 3, 1] = one
+    wr[64 * 6 + 1, 1] = big
+    wr[0, 2] = big
+    wr[1:5, 2] = one
+    wr[0:4, 3] = one
+    wr[4, 3] = big
     z = orc.router_logits(x, wr)
-    assert z[0, 0] == np.float32(2 ** 24 + 4)
-    assert z[0, 1] == np.float32(2 ** 24 + 4)
+    assert z[0].tolist() == [2.0 ** 24, 2.0 ** 24 + 4, 2.0 ** 24, 2.0 ** 24 + 4]
+
+
+def test_topk_weights_of_a_given_selection():
+    """Renormalised sigmoids of the chosen logits, in the order given:
+    z = 0 gives sigmoid 1/2 for every expert, so the weights are 1/k."""
+    z = np.array([[0.0, 0.0, 0.0, 0.0], [2.0, -1.0, 0.5, 3.0]], np.float32)
+    ids = np.array([[3, 0], [3, 1]], np.int32)
+    w = orc.topk_weights(z, ids)
+    assert np.allclose(w[0], 0.5, rtol=0, atol=1e-15)
+    s3, s1 = 1 / (1 + np.exp(-3.0)), 1 / (1 + np.exp(1.0))
+    assert np.allclose(w[1], [s3 / (s3 + s1), s1 / (s3 + s1)], rtol=1e-15, atol=0)
+    ids2, w2 = orc.topk(z, 2)
+    assert np.array_equal(w2, orc.topk_weights(z, ids2))
 
 
 def test_router_zero_weights_give_lowest_ids_and_equal_weights():
