@@ -81,14 +81,11 @@ __device__ __forceinline__ void dma4(const uint8_t* base, uint32_t voff, void* l
                : "memory");
 }
 
-// SwiGLU and requantisation in the grouped GEMM's epilogue use the fast
-// exponential and the hardware reciprocal (v_rcp_f32, ~1 ulp; the
-// correctly rounded __frcp_rn is a ~10-instruction division sequence): h
-// there already carries the MFMA's own accumulation error (its 128-term sums
-// are not exactly rounded), next to which a few ulp of the SiLU and of
-// v * (1/s) instead of v / s are negligible.  The scale s = amax / 448 itself
-// stays an IEEE division.  The one-token GEMV keeps the IEEE forms (its h is
-// exact to fp32 rounding).
+// SwiGLU in the grouped GEMM's epilogue uses the fast exponential and the
+// hardware reciprocal (v_rcp_f32, ~1 ulp): h there already carries the
+// MFMA's own accumulation error (its 128-term sums are not exactly rounded),
+// next to which a few ulp of the SiLU are negligible.  The requantisation of
+// h, however, follows the act_quant rule exactly (e4m3_div2).
 __device__ __forceinline__ float silu_mul_fast(float g, float u) {
   return g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
@@ -96,6 +93,32 @@ __device__ __forceinline__ float silu_mul_fast(float g, float u) {
 __device__ __forceinline__ uint32_t e4m3_1(float v) {
   v = __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xffu;
+}
+
+__device__ __forceinline__ uint32_t e4m3_2(float a, float b) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+
+// E4M3 codes (bytes 0 and 1) of fl32(a / s) and fl32(b / s): the act_quant
+// rule (IEEE division, then round to nearest even, saturating), without a
+// division per element.  With r = v_rcp_f32(s) (within 1 ulp of 1/s), t =
+// v * r is within 2^-22 |t| of fl32(v / s); the E4M3 rounding is monotone,
+// so when t (1 - 2^-20) and t (1 + 2^-20) get the same code, that is the
+// code of fl32(v / s).  Only an element whose bracket holds a rounding
+// midpoint (about 2^-16 of them) takes the correctly rounded division; so
+// does every element when s is an fp32 subnormal (its reciprocal is then not
+// within 1 ulp).
+__device__ __forceinline__ uint32_t e4m3_div2(float a, float b, float s, float r) {
+  const float ta = a * r, tb = b * r;
+  const float dn = 1.0f - 0x1p-20f, up = 1.0f + 0x1p-20f;
+  const uint32_t lo = e4m3_2(ta * dn, tb * dn), hi = e4m3_2(ta * up, tb * up);
+  const bool tiny = s < 0x1p-126f;
+  if (lo == hi && !tiny) return lo;
+  const uint32_t ca = ((lo ^ hi) & 0xffu) || tiny ? e4m3_1(a / s) : (lo & 0xffu);
+  const uint32_t cb = ((lo ^ hi) & 0xff00u) || tiny ? e4m3_1(b / s) : (lo >> 8);
+  return ca | (cb << 8);
 }
 
 // LDS byte offset of 16-byte chunk c of row r: rows of 128 bytes (E4M3, one
@@ -165,7 +188,10 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
   const int E = a.E, H = a.H, I = a.I;
   const int K = GU ? H : I;  // contraction length
   const int KS = K >> 7;
-  const int NB = GU ? (I >> 7) : (H / kTN2);  // N-blocks per M-tile
+  // N-blocks per M-tile.  For down, H may end in half an N-block (H = 128
+  // mod 256): that block's second 128 weight rows are clamped to row H-1 in
+  // the loads and never stored.
+  const int NB = GU ? (I >> 7) : ((H + kTN2 - 1) / kTN2);
 
   // m-tiles per group and their exclusive prefix (groups 0..E, E = shared)
   {
@@ -246,7 +272,8 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
       const int p = (w * NBI + i) * 64 + lane;
       const int r = FMT == 1 ? (p >> 2) : (p >> 3);
       const int c = FMT == 1 ? ((p & 3) ^ ((r >> 1) & 3)) : ((p & 7) ^ ((r >> 1) & 7));
-      offB[i] = (row_base + (uint32_t)(GU ? (r & 127) : r)) * brow_bytes + 16u * c;
+      const uint32_t row = GU ? row_base + (uint32_t)(r & 127) : min(row_base + (uint32_t)r, (uint32_t)H - 1u);
+      offB[i] = row * brow_bytes + 16u * c;
     }
     // FP4 scales: weight row w*32 + lane (lanes < 32; gate rows are waves 0-3)
     const uint32_t sbytes = (uint32_t)(K >> 5);
@@ -256,7 +283,7 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
       const uint8_t* sm = (GU && w >= 4) ? (const uint8_t*)a.us : (const uint8_t*)(GU ? a.gs : a.ds);
       baseS = sm + (size_t)g * rows_per_expert * sbytes;
       const int r = w * 32 + (lane & 31);
-      offS = (row_base + (uint32_t)(GU ? (r & 127) : r)) * sbytes;
+      offS = (GU ? row_base + (uint32_t)(r & 127) : min(row_base + (uint32_t)r, (uint32_t)H - 1u)) * sbytes;
     }
     // activation scales: token w*XL + lane (lanes < XL)
     const float* baseX = GU ? a.xs : a.hs + (size_t)row0 * KS;
@@ -271,7 +298,7 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
       for (int t = tid; t < 2 * KS; t += kGThreads) {
         const int hsel = t >= KS, ks = t - hsel * KS;
         const float* src = GU ? (const float*)(hsel ? a.us : a.gs) + ((size_t)g * (I >> 7) + nb) * KS
-                              : (const float*)a.ds + ((size_t)g * (H >> 7) + nb * 2 + hsel) * KS;
+                              : (const float*)a.ds + ((size_t)g * (H >> 7) + min(nb * 2 + hsel, (H >> 7) - 1)) * KS;
         s_wsc[hsel][ks] = src[ks];
       }
       __syncthreads();
@@ -492,10 +519,14 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
         for (int i = 0; i < 4; ++i) {
           uint32_t cw = 0;
           if (am != 0.0f) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) cw |= e4m3_1(acc[i][ti][v] * rsc) << (8 * v);
+            cw = e4m3_div2(acc[i][ti][0], acc[i][ti][1], sc, rsc) |
+                 (e4m3_div2(acc[i][ti][2], acc[i][ti][3], sc, rsc) << 16);
           }
           *reinterpret_cast<uint32_t*>(&s_out[t * 128 + 64 * wn + 16 * i + 4 * q]) = cw;
+          if (a.h_dbg && t < nrows)
+            *reinterpret_cast<float4*>(a.h_dbg + (size_t)(row0 + t) * I + nb * 128 + 64 * wn +
+                                       16 * i + 4 * q) =
+                make_float4(acc[i][ti][0], acc[i][ti][1], acc[i][ti][2], acc[i][ti][3]);
         }
         if (wn == 0 && q == 0 && t < nrows) a.hs[(size_t)(row0 + t) * I128 + nb] = sc;
       }
@@ -511,7 +542,7 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
 #pragma unroll
       for (int ti = 0; ti < NT; ++ti) {
         const int t = wt * (TM / 4) + 16 * ti + (lane & 15);
-        if (live && t < nrows) {
+        if (live && t < nrows && nb * kTN2 + 128 * wn < H) {
           float* yp = a.y_rows + (size_t)(row0 + t) * H + nb * kTN2 + 128 * wn + 4 * q;
 #pragma unroll
           for (int i = 0; i < 8; ++i)
@@ -545,10 +576,10 @@ static int grid_blocks() {
 
 template <int FMT, bool GU, int TM>
 static hipError_t launch_g(const GemmArgs& a, hipStream_t st) {
-  if (a.E + 1 > 257 || (GU ? (a.I % 128) : (a.H % kTN2)) != 0) return hipErrorInvalidValue;
-  const KernelTimer& tm = g_kernel_timer[MOE_KERNEL_GEMM_GATE_UP];
+  if (a.E + 1 > 257 || (GU ? a.I : a.H) % 128 != 0) return hipErrorInvalidValue;
+  const KernelTimer& tm = g_kernel_timer[GU ? MOE_KERNEL_GEMM_GATE_UP : MOE_KERNEL_GEMM_DOWN];
   const dim3 grid((gemm_two_per_cu(FMT, TM) ? 2 : 1) * grid_blocks());
-  if (GU && tm.start)
+  if (tm.start)
     hipExtLaunchKernelGGL(gemm_kernel<FMT, GU, TM>, grid, dim3(kGThreads), 0, st, tm.start,
                           tm.stop, 0, a);
   else

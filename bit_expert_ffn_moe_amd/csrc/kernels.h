@@ -20,7 +20,7 @@ constexpr uint32_t MOE_STATUS_BAD_EXPERT_ID_DEV = 1u;
 struct KernelTimer {
   hipEvent_t start, stop;
 };
-extern KernelTimer g_kernel_timer[3];
+extern KernelTimer g_kernel_timer[5];
 
 struct GemvArgs {
   const uint8_t *gq, *gs, *uq, *us, *dq, *ds;
@@ -52,7 +52,15 @@ struct GemmArgs {
   uint8_t* hq;
   float* hs;
   float* y_rows;
+  float* h_dbg;   // debug: fp32 h [T*k+T][I] of the gate+up kernels when set
 };
+
+// Debug sink of the grouped GEMM's fp32 h (moe_debug_store_h).
+struct HSink {
+  float* h;
+  size_t n;
+};
+extern HSink g_h_sink;
 
 // Small-T front of the layer: router (+ act_quant of x when xq is set,
 // + permutation tables when offsets is set).
