@@ -21,7 +21,7 @@ MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EALIGN, MOE_EWORKSPACE, MOE_ELAUNCH = 0, -1
 MOE_W_FP4_E2M1_UE8M0_K32, MOE_W_FP8_E4M3_F32_B128 = 1, 2
 MOE_DT_BF16, MOE_DT_F32 = 1, 2
 MOE_STATUS_BAD_EXPERT_ID, MOE_STATUS_SYNC_TIMEOUT = 1, 2
-MOE_KERNEL_GEMV_GATE_UP, MOE_KERNEL_GEMM_GATE_UP = 1, 2
+MOE_KERNEL_GEMV_GATE_UP, MOE_KERNEL_GEMM_GATE_UP, MOE_KERNEL_GEMV_DOWN, MOE_KERNEL_GEMM_DOWN = 1, 2, 3, 4
 
 if not os.path.exists(_SO):
     raise ImportError(
@@ -71,6 +71,10 @@ _sigs = {
     "moe_debug_intermediates": ([_W, _i32, _i32, _vp, _sz, ctypes.POINTER(_vp),
                                  ctypes.POINTER(_vp), ctypes.POINTER(_vp)], ctypes.c_int),
     "moe_debug_time_kernel": ([_i32, _vp, _vp], ctypes.c_int),
+    "moe_debug_store_h": ([_vp, _sz], ctypes.c_int),
+    "moe_debug_stream_read": ([_vp, _sz, _vp, _i32, _vp], ctypes.c_int),
+    "moe_debug_routing": ([_W, _i32, _i32, _vp, _sz, ctypes.POINTER(_vp), ctypes.POINTER(_vp)],
+                          ctypes.c_int),
 }
 for _name, (_args, _res) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -194,6 +198,25 @@ def moe_debug_intermediates(w, T, k, ws, ws_bytes):
                                         ctypes.byref(h), ctypes.byref(hq), ctypes.byref(hs)),
            "moe_debug_intermediates")
     return h.value, hq.value, hs.value
+
+
+def moe_debug_stream_read(src, nbytes, sink, blocks, stream=None):
+    _check(_lib.moe_debug_stream_read(_ptr(src), nbytes, _ptr(sink), blocks, _stream(stream)),
+           "moe_debug_stream_read")
+
+
+def moe_debug_store_h(h, n_floats):
+    """Set (or clear with None, 0) the MFMA gate+up kernels' fp32 h sink."""
+    _check(_lib.moe_debug_store_h(_ptr(h) if h is not None else None, n_floats),
+           "moe_debug_store_h")
+
+
+def moe_debug_routing(w, T, k, ws, ws_bytes):
+    """Device addresses (ids, weights) the last forward's router left in ws."""
+    ids, tw = _vp(), _vp()
+    _check(_lib.moe_debug_routing(ctypes.byref(w), T, k, _ptr(ws), ws_bytes, ctypes.byref(ids),
+                                  ctypes.byref(tw)), "moe_debug_routing")
+    return ids.value, tw.value
 
 
 def raw_call(name: str, *args) -> int:

@@ -220,9 +220,16 @@ template <int NB, bool COMBINE>
 static hipError_t launch_down_nb(const GemvArgs& a, hipStream_t st) {
   if (a.H % 8 != 0) return hipErrorInvalidValue;
   if (COMBINE && a.k + 1 > kGemvMaxRows) return hipErrorInvalidValue;
-  gemv_down_fp4_kernel<NB, COMBINE><<<dim3(a.H / 8), 512, 0, st>>>(
-      a.dq, a.ds, a.hq_ws, a.hs_ws, a.offsets, a.active, a.n_slots, a.n_rows, a.row_of,
-      a.topk_w, a.E, a.H, a.I, a.k, a.y_rows, a.out, a.out_bf16);
+  const KernelTimer& tm = g_kernel_timer[MOE_KERNEL_GEMV_DOWN];
+  if (tm.start)
+    hipExtLaunchKernelGGL(gemv_down_fp4_kernel<NB, COMBINE>, dim3(a.H / 8), dim3(512), 0, st,
+                          tm.start, tm.stop, 0, a.dq, a.ds, a.hq_ws, a.hs_ws, a.offsets,
+                          a.active, a.n_slots, a.n_rows, a.row_of, a.topk_w, a.E, a.H, a.I, a.k,
+                          a.y_rows, a.out, a.out_bf16);
+  else
+    gemv_down_fp4_kernel<NB, COMBINE><<<dim3(a.H / 8), 512, 0, st>>>(
+        a.dq, a.ds, a.hq_ws, a.hs_ws, a.offsets, a.active, a.n_slots, a.n_rows, a.row_of,
+        a.topk_w, a.E, a.H, a.I, a.k, a.y_rows, a.out, a.out_bf16);
   return hipGetLastError();
 }
 

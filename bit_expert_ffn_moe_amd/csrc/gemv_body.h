@@ -183,8 +183,8 @@ __device__ __forceinline__ int h_row(int lane) { return (lane >> 3) & 3; }
 //    --, returns them to zero for the next launch (each slot is written once
 //    per launch, so nothing can land after that reset), and writes the E4M3
 //    codes and scale with the act_quant rule (s = amax / 448 by IEEE
-//    division, code = E4M3(v / s), zero block -> s = 0, code 0; dpshk.com
-//    article, section "核心实现二").
+//    division, code = E4M3(v / s), zero block -> s = 0, code 0; tcti.cn
+//    post, section "补齐软件栈缺失": act_quant feeds the FP8/FP4 linears).
 // The slots start zeroed (workspace initialisation); after a timeout a late
 // write could outlive the reset, so a workspace that reported one must be
 // initialised again.

@@ -12,7 +12,8 @@
 
 namespace bef {
 
-KernelTimer g_kernel_timer[3];
+KernelTimer g_kernel_timer[5];
+HSink g_h_sink;
 
 __global__ void zero_words_kernel(uint32_t* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -22,6 +23,27 @@ __global__ void zero_words_kernel(uint32_t* p, int n) {
 hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t st) {
   zero_words_kernel<<<(n + 255) / 256, 256, 0, st>>>(p, n);
   return hipGetLastError();
+}
+
+// A plain streaming read (the practical HBM ceiling the kernels are compared
+// with): 16-byte loads, four independent ones in flight per lane, grid-stride
+// over n16 16-byte words; the XOR of everything read decides a store that
+// never happens in practice, so the loads cannot be dropped.
+__global__ __launch_bounds__(512) void stream_read_kernel(const uint4* __restrict__ p, size_t n16,
+                                                          uint32_t* sink) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^
+           d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = p[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
 namespace {
@@ -213,6 +235,8 @@ GemmArgs gemm_args(const moe_weights* w, int T, int k, const Layout& L, void* ws
   g.T = T, g.k = k, g.E = w->n_experts, g.H = w->hidden, g.I = w->inter;
   g.hq = at<uint8_t>(ws, L.hq);
   g.hs = at<float>(ws, L.hs);
+  const size_t R = (size_t)T * k + T;
+  if (g_h_sink.h && g_h_sink.n >= R * (size_t)w->inter) g.h_dbg = g_h_sink.h;
   return g;
 }
 
@@ -398,7 +422,7 @@ int moe_combine(const float* y_rows, const int32_t* row_of, const float* topk_w,
                 int32_t k, int32_t H, void* out, int32_t out_dtype, void* stream) {
   if (!y_rows || !row_of || !topk_w || !out) return MOE_EINVAL;
   if (T < 0 || k < 1) return MOE_EINVAL;
-  if (k > 16) return MOE_ENOTSUP;
+  if (k > 16 || T > kMaxTokens) return MOE_ENOTSUP;
   int rc = check_hidden(H);
   if (rc) return rc;
   if (out_dtype != MOE_DT_BF16 && out_dtype != MOE_DT_F32) return MOE_EINVAL;
@@ -412,9 +436,15 @@ int moe_combine(const float* y_rows, const int32_t* row_of, const float* topk_w,
                      (hipStream_t)stream));
 }
 
-int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint16_t* x, int32_t T,
-                     int32_t k, const int32_t* routing_ids, const float* routing_w, void* out,
-                     int32_t out_dtype, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace bef {
+namespace {
+
+// Arguments of the whole-layer call other than the workspace.
+int check_forward_args(const moe_weights* w, const uint16_t* w_router, const uint16_t* x,
+                       int32_t T, int32_t k, const int32_t* routing_ids, const float* routing_w,
+                       const void* out, int32_t out_dtype) {
   int rc = check_weights(w);
   if (rc) return rc;
   if (!x || !out) return MOE_EINVAL;
@@ -426,13 +456,15 @@ int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint1
   if (!aligned16(x) || !aligned16(out) || (w_router && !aligned16(w_router)) ||
       (routing_ids && (!aligned16(routing_ids) || !aligned16(routing_w))))
     return MOE_EALIGN;
-  if (T == 0) return MOE_OK;
+  return MOE_OK;
+}
+
+// The whole layer, arguments already checked, T >= 1, ws large enough.
+int enqueue_forward(const moe_weights* w, const uint16_t* w_router, const uint16_t* x, int32_t T,
+                    int32_t k, const int32_t* routing_ids, const float* routing_w, void* out,
+                    int32_t out_dtype, void* ws, hipStream_t st) {
+  int rc = MOE_OK;
   const Layout L = layout_w(w, T, k);
-  rc = check_ws(ws, ws_bytes, L.total);
-  if (rc) return rc;
-  rc = check_device();
-  if (rc) return rc;
-  hipStream_t st = (hipStream_t)stream;
   const int E = w->n_experts, H = w->hidden;
   WsCtl* ctl = at<WsCtl>(ws, L.ctl);
   const int32_t* ids = routing_ids;
@@ -509,6 +541,25 @@ int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint1
                       st);
 }
 
+}  // namespace
+}  // namespace bef
+
+extern "C" {
+
+int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint16_t* x, int32_t T,
+                     int32_t k, const int32_t* routing_ids, const float* routing_w, void* out,
+                     int32_t out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_forward_args(w, w_router, x, T, k, routing_ids, routing_w, out, out_dtype);
+  if (rc) return rc;
+  if (T == 0) return MOE_OK;
+  rc = check_ws(ws, ws_bytes, layout_w(w, T, k).total);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  return enqueue_forward(w, w_router, x, T, k, routing_ids, routing_w, out, out_dtype, ws,
+                         (hipStream_t)stream);
+}
+
 const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "ok";
@@ -543,8 +594,20 @@ int moe_device_status(void* ws, void* stream, uint32_t* status, int clear) {
   return MOE_OK;
 }
 
+int moe_debug_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,
+                          void* stream) {
+  if (!src || !sink || bytes < 16 || bytes % 16 != 0 || blocks < 1 || blocks > (1 << 20))
+    return MOE_EINVAL;
+  if (!aligned16(src)) return MOE_EALIGN;
+  int rc = check_device();
+  if (rc) return rc;
+  stream_read_kernel<<<blocks, 512, 0, (hipStream_t)stream>>>((const uint4*)src, bytes / 16,
+                                                               sink);
+  return launch_status(hipGetLastError());
+}
+
 int moe_debug_time_kernel(int32_t which, void* start_event, void* stop_event) {
-  if (which != MOE_KERNEL_GEMV_GATE_UP && which != MOE_KERNEL_GEMM_GATE_UP) return MOE_EINVAL;
+  if (which < MOE_KERNEL_GEMV_GATE_UP || which > MOE_KERNEL_GEMM_DOWN) return MOE_EINVAL;
   if ((start_event == nullptr) != (stop_event == nullptr)) return MOE_EINVAL;
   g_kernel_timer[which].start = (hipEvent_t)start_event;
   g_kernel_timer[which].stop = (hipEvent_t)stop_event;
@@ -565,6 +628,29 @@ int moe_debug_intermediates(const moe_weights* w, int32_t T, int32_t k, void* ws
   if (h) *h = gv ? at<float>(ws, L.h) : nullptr;
   if (hq) *hq = at<uint8_t>(ws, L.hq);
   if (hs) *hs = at<float>(ws, L.hs);
+  return MOE_OK;
+}
+
+int moe_debug_store_h(float* h, size_t n_floats) {
+  if ((h == nullptr) != (n_floats == 0)) return MOE_EINVAL;
+  if (h && !aligned16(h)) return MOE_EALIGN;
+  g_h_sink.h = h;
+  g_h_sink.n = n_floats;
+  return MOE_OK;
+}
+
+int moe_debug_routing(const moe_weights* w, int32_t T, int32_t k, void* ws, size_t ws_bytes,
+                      int32_t** ids, float** topk_w) {
+  int rc = check_weights(w);
+  if (rc) return rc;
+  rc = check_tk(T, k, w->n_experts);
+  if (rc) return rc;
+  if (T == 0) return MOE_EINVAL;  // an empty batch routes nothing
+  const Layout L = layout_w(w, T, k);
+  rc = check_ws(ws, ws_bytes, L.total);
+  if (rc) return rc;
+  if (ids) *ids = at<int32_t>(ws, L.ids);
+  if (topk_w) *topk_w = at<float>(ws, L.w);
   return MOE_OK;
 }
 

@@ -2,9 +2,13 @@
 //
 // Reading each expert's weights once for all of its tokens is what makes
 // batching pay (dpshk.com article, section "核心实现三").  The sort is
-// deterministic and atomic-free: every expert's rows are assigned by one
-// thread walking the pairs in token order, so rows inside an expert are in
-// ascending token order and repeated runs give identical tables.
+// stable and deterministic: experts' counts come from LDS atomic adds (the
+// order of the adds does not change a count), and a pair's row is its
+// expert's base plus the number of earlier pairs of the same expert, counted
+// a chunk of 256 pairs at a time -- inside a wave from ballots over the id
+// bits, across the waves of a chunk from per-wave counts in LDS, across
+// chunks from a running count -- so rows inside an expert are in ascending
+// token order and repeated runs give identical tables.
 //
 // Tables: offsets[E+2] (group g = expert g, group E = the shared expert with
 // every token), row_token[T*k+T], row_of[T][k+1].  An id outside [0, E) is

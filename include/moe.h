@@ -121,9 +121,13 @@ int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *   w_router [H][E] bf16
  *   topk_ids [T][k] int32 out: experts ordered by (logit desc, id asc)
  *   topk_w   [T][k] f32 out: sigmoid(logit) renormalised over the k chosen
- * Logits are fp32 in one fixed order: 64-wide chunk partials, each a chain
- * of fused multiply-adds in ascending h from +0; sums of 4 consecutive
- * chunks in ascending order; those group sums in ascending order.
+ * Logits are fp32 sums of the exact bf16 x bf16 products in one fixed order
+ * (64-wide chunk partials, each a chain of fused multiply-adds in ascending
+ * h from +0; sums of 4 consecutive chunks in ascending order; those group
+ * sums in ascending order), so the ids are deterministic.  They are the
+ * exact top-k of these logits; logits summed in any other order differ by
+ * rounding only, so another order can rank two experts differently only
+ * where their logits lie within rounding distance of each other.
  * ws: workspace of at least moe_workspace_bytes(.., T, k). */
 int moe_route(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H, int32_t E,
               int32_t k, int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
@@ -184,10 +188,18 @@ int moe_expert_down(const moe_weights* w, int32_t T, int32_t k, const int32_t* o
                     const int32_t* row_of, const float* topk_w, float* y_rows, void* out,
                     int32_t out_dtype, void* ws, size_t ws_bytes, void* stream);
 
-/* S7, combine: out[t] = y_rows[row_of[t][k]] + sum_{j<k} topk_w[t][j] *
- * y_rows[row_of[t][j]] in fp32 in that order (rows of -1 contribute 0),
- * written as bf16 (nearest even) or f32.
- *   out [T][H] (out_dtype MOE_DT_BF16 or MOE_DT_F32) */
+/* S7, combine: the always-on shared expert's output plus the token's routed
+ * experts' outputs weighted by their gate weights (tcti.cn post, section
+ * "DeepSeek-V4-Flash的可能性": top-6 routed experts beside one shared
+ * expert; the rows come back from the expert-major order of the batch,
+ * dpshk.com article, section "核心实现三"):
+ *   out[t] = y_rows[row_of[t][k]] + sum_{j<k} topk_w[t][j] * y_rows[row_of[t][j]]
+ * in fp32 in that order (rows of -1 contribute 0), written as bf16 (nearest
+ * even) or f32.
+ *   y_rows [rows][H] f32, row_of [T][k+1] int32, topk_w [T][k] f32
+ *   out [T][H] (out_dtype MOE_DT_BF16 or MOE_DT_F32)
+ * Limits as for every call: 1 <= k <= 16, 0 <= T <= 262144, H a multiple of
+ * 128 up to 8192. */
 int moe_combine(const float* y_rows, const int32_t* row_of, const float* topk_w, int32_t T,
                 int32_t k, int32_t H, void* out, int32_t out_dtype, void* stream);
 
@@ -215,8 +227,28 @@ int moe_device_status(void* ws, void* stream, uint32_t* status, int clear);
 int moe_debug_intermediates(const moe_weights* w, int32_t T, int32_t k, void* ws,
                             size_t ws_bytes, float** h, uint8_t** hq, float** hs);
 
-/* Kernels that moe_debug_time_kernel can time. */
-enum { MOE_KERNEL_GEMV_GATE_UP = 1, MOE_KERNEL_GEMM_GATE_UP = 2 };
+/* DEBUG/TESTS ONLY -- while set, every MFMA grouped-GEMM gate+up launch of
+ * a call with (T*k+T)*I <= n_floats also stores its fp32 h (SwiGLU output,
+ * before requantisation) into h [T*k+T][I] (device memory owned by the
+ * caller, 16-byte aligned); the VALU path keeps its h in the workspace (see
+ * moe_debug_intermediates).  NULL and 0 clear it.  Process-wide and not
+ * thread-safe.  MOE_EINVAL if exactly one of h, n_floats is zero. */
+int moe_debug_store_h(float* h, size_t n_floats);
+
+/* DEBUG/TESTS ONLY -- device pointers to the expert ids [T][k] int32 and
+ * weights [T][k] f32 that the router of the last dsv4_moe_forward call with
+ * the same (w, T, k) and no injected routing left in `ws`.  T >= 1. */
+int moe_debug_routing(const moe_weights* w, int32_t T, int32_t k, void* ws, size_t ws_bytes,
+                      int32_t** ids, float** topk_w);
+
+/* Kernels that moe_debug_time_kernel can time: the gate+up and the down
+ * kernels of the one-token VALU path (GEMV) and of the grouped GEMM. */
+enum {
+  MOE_KERNEL_GEMV_GATE_UP = 1,
+  MOE_KERNEL_GEMM_GATE_UP = 2,
+  MOE_KERNEL_GEMV_DOWN = 3,
+  MOE_KERNEL_GEMM_DOWN = 4
+};
 
 /* DEBUG/BENCHMARK ONLY -- kernel timing.  While set, every launch of kernel
  * `which` (MOE_KERNEL_*) records `start_event` and `stop_event` (hipEvent_t
@@ -225,6 +257,14 @@ enum { MOE_KERNEL_GEMV_GATE_UP = 1, MOE_KERNEL_GEMM_GATE_UP = 2 };
  * duration without queueing gaps.  Two NULL events clear it.  Process-wide
  * and not thread-safe.  MOE_EINVAL for an unknown kernel. */
 int moe_debug_time_kernel(int32_t which, void* start_event, void* stop_event);
+
+/* DEBUG/BENCHMARK ONLY -- enqueue a plain streaming read of `bytes` (a
+ * multiple of 16) at `src` by `blocks` blocks of 512 threads (16-byte
+ * loads, four in flight per lane): the practical HBM read ceiling the
+ * kernels are measured against.  `sink` (4 bytes of device memory) is
+ * written only if the XOR of the data read equals an arbitrary constant. */
+int moe_debug_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks,
+                          void* stream);
 
 #ifdef __cplusplus
 }

@@ -197,3 +197,15 @@ def test_token_count_limit():
                               big, None) == moe.MOE_ENOTSUP
     assert L.moe_route(p, p, (1 << 18) + 1, 4096, 256, 6, p, p, ws, big, None) == moe.MOE_ENOTSUP
     assert L.moe_permute(p, (1 << 18) + 1, 6, 256, p, p, p, ws, big, None) == moe.MOE_ENOTSUP
+    assert L.moe_combine(p, p, p, (1 << 18) + 1, 6, 4096, p, moe.MOE_DT_F32,
+                         None) == moe.MOE_ENOTSUP
+
+
+def test_debug_h_sink_arguments():
+    L = moe._lib
+    assert L.moe_debug_store_h(None, 16) == moe.MOE_EINVAL
+    assert L.moe_debug_store_h(0x100000, 0) == moe.MOE_EINVAL
+    assert L.moe_debug_store_h(0x100004, 16) == moe.MOE_EALIGN
+    assert L.moe_debug_store_h(0x100000, 16) == moe.MOE_OK
+    assert L.moe_debug_store_h(None, 0) == moe.MOE_OK
+
