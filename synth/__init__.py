@@ -22,6 +22,7 @@ from __future__ import annotations
 
 import ctypes
 import dataclasses
+import functools
 import os
 import subprocess
 
@@ -147,21 +148,39 @@ def _fp4_matrix(seed, stream_q, stream_s, n_exp, rows, cols):
 
 def _fp8_matrix(seed, stream, n_exp, rows, cols, sigma=0.02):
     """~N(0, sigma) weights, one fp32 scale per 128x128 block = amax / 448,
-    codes = torch's float8_e4m3fn conversion of w / scale."""
+    codes = torch's float8_e4m3fn conversion of w / scale (torch on the CPU
+    for the block maxima and the fp32 division too, for its threads)."""
     import torch
     q = np.empty((n_exp, rows, cols), np.uint8)
     s = np.empty((n_exp, rows // 128, cols // 128), np.float32)
     per = rows * cols
     for e in range(n_exp):
-        w = normal_f32(seed, stream, (rows, cols), sigma, offset=e * per)
-        blk = w.reshape(rows // 128, 128, cols // 128, 128)
-        amax = np.abs(blk).max(axis=(1, 3)).astype(np.float32)
-        sc = (amax / np.float32(448.0)).astype(np.float32)
-        s[e] = sc
-        safe = np.where(sc > 0, sc, np.float32(1.0)).astype(np.float32)
-        scaled = (blk / safe[:, None, :, None]).astype(np.float32).reshape(rows, cols)
-        q[e] = torch.from_numpy(scaled).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        w = torch.from_numpy(normal_f32(seed, stream, (rows, cols), sigma, offset=e * per))
+        blk = w.view(rows // 128, 128, cols // 128, 128)
+        sc = blk.abs().amax(dim=(1, 3)) / 448.0
+        s[e] = sc.numpy()
+        safe = torch.where(sc > 0, sc, torch.ones_like(sc))
+        scaled = (blk / safe[:, None, :, None]).reshape(rows, cols)
+        q[e] = scaled.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     return q, s
+
+
+@functools.lru_cache(maxsize=2)
+def _weights(fmt, seed, E, H, I):
+    """The stacked expert weights of a layer; they depend on neither T, k
+    nor the routing, so layers of one (fmt, seed, E, H, I) share them (the
+    caller must not modify them)."""
+    if fmt == "fp4":
+        gq, gs = _fp4_matrix(seed, 3, 4, E + 1, I, H)
+        uq, us = _fp4_matrix(seed, 5, 6, E + 1, I, H)
+        dq, ds = _fp4_matrix(seed, 7, 8, E + 1, H, I)
+    elif fmt == "fp8":
+        gq, gs = _fp8_matrix(seed, 3, E + 1, I, H)
+        uq, us = _fp8_matrix(seed, 5, E + 1, I, H)
+        dq, ds = _fp8_matrix(seed, 7, E + 1, H, I)
+    else:
+        raise ValueError(fmt)
+    return gq, gs, uq, us, dq, ds
 
 
 def zipf_routing(seed, T, E, k, s):
@@ -190,16 +209,7 @@ def make_layer(wl: Workload | str, **over) -> Layer:
     T, H, I, E, k, seed = wl.T, wl.H, wl.I, wl.E, wl.k, wl.seed
     x = normal_bf16(seed, 1, (T, H), 1.0)
     wr = normal_bf16(seed, 2, (H, E), 0.02)
-    if wl.fmt == "fp4":
-        gq, gs = _fp4_matrix(seed, 3, 4, E + 1, I, H)
-        uq, us = _fp4_matrix(seed, 5, 6, E + 1, I, H)
-        dq, ds = _fp4_matrix(seed, 7, 8, E + 1, H, I)
-    elif wl.fmt == "fp8":
-        gq, gs = _fp8_matrix(seed, 3, E + 1, I, H)
-        uq, us = _fp8_matrix(seed, 5, E + 1, I, H)
-        dq, ds = _fp8_matrix(seed, 7, E + 1, H, I)
-    else:
-        raise ValueError(wl.fmt)
+    gq, gs, uq, us, dq, ds = _weights(wl.fmt, seed, E, H, I)
     ids = w = None
     if wl.routing == "zipf":
         ids, w = zipf_routing(seed, T, E, k, wl.zipf_s)

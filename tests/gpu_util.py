@@ -6,6 +6,7 @@ import numpy as np
 import torch
 
 import bit_expert_ffn_moe_amd as moe
+from route_check import check_selection
 
 DEV = "cuda:0"
 
@@ -100,3 +101,94 @@ def f64_to_bf16_bits(v: np.ndarray) -> np.ndarray:
     r = np.round(scaled)                     # numpy rounds half to even
     out = np.ldexp(r, e - 8).astype(np.float32)  # exact: r has <= 9 bits
     return (out.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def check_gpu_selection(orc, x, wr, k, ids_g, w_g, exact=False, what=""):
+    """The GPU's expert ids must be a valid top-k of the oracle's logits
+    (route_check: equal to the oracle's, or differing only between logits
+    within the near-tie band), bit-exact when `exact`; its weights must match
+    the oracle's renormalised sigmoids of the GPU's own ids to 1e-5.
+    Returns (oracle ids, number of tokens whose ids differ)."""
+    z = orc.router_logits(x, wr)
+    ids_ref, _ = orc.topk(z, k)
+    valid, sub = check_selection(ids_g, z, ids_ref)
+    n_sub = int(sub.sum())
+    print(f"routing {what}: {ids_g.shape[0]} tokens, {n_sub} near-tie substitutions", flush=True)
+    assert valid.all(), np.nonzero(~valid)[0][:8]
+    if exact:
+        assert n_sub == 0
+    w_ref = orc.topk_weights(z, ids_g)
+    assert np.allclose(w_g, w_ref, rtol=1e-5, atol=0, equal_nan=True)
+    return ids_ref, n_sub
+
+
+def gpu_routing(D, T):
+    """ids and weights the last dsv4_moe_forward's router left in D's workspace."""
+    ip, wp = moe.moe_debug_routing(D.w, T, D.wl.k, D.ws, D.ws_bytes)
+    return d2h(ip, (T, D.wl.k), np.int32), d2h(wp, (T, D.wl.k), np.float32)
+
+
+def routed_reference(orc, W, L, ids_g=None, w_g=None, tok=None, threads=0):
+    """Oracle output of tokens `tok` (all when None).  With drawn routing
+    the oracle takes it as well.  With the router on x, the GPU's selection
+    ids_g / w_g [T][k] (read back from the workspace, or from moe_route) is
+    first checked against the oracle's logits; the oracle's layer then runs
+    its own router, except on tokens where the GPU chose differently inside
+    the near-tie band: those take the GPU's ids with the oracle's weights of
+    them."""
+    k = L.wl.k
+    if L.ids is not None:
+        return orc.forward(W, L.wr, L.x, k, ids=L.ids, w=L.w, tokens=tok, threads=threads)
+    T = L.x.shape[0]
+    sel = np.arange(T) if tok is None else np.asarray(tok)
+    ids_ref, _ = check_gpu_selection(orc, L.x[sel], L.wr, k, ids_g[sel], w_g[sel],
+                                     what=f"T={T}")
+    ref = orc.forward(W, L.wr, L.x, k, tokens=tok, threads=threads)
+    diff = np.nonzero((ids_g[sel] != ids_ref).any(axis=1))[0]
+    if diff.size:
+        z = orc.router_logits(L.x[sel[diff]], L.wr)
+        ids_all = np.zeros((T, k), np.int32)
+        w_all = np.zeros((T, k), np.float32)
+        ids_all[sel[diff]] = ids_g[sel[diff]]
+        w_all[sel[diff]] = orc.topk_weights(z, ids_g[sel[diff]]).astype(np.float32)
+        ref[diff] = orc.forward(W, L.wr, L.x, k, ids=ids_all, w=w_all,
+                                tokens=sel[diff].astype(np.int32), threads=threads)
+    return ref
+
+
+def grouped_gemm_tile(T, k, E):
+    """Tokens per M-tile of the grouped GEMM for this shape: the tile size
+    the library's launcher picks from the routed rows per expert (256 from
+    128 rows per expert on average, 128 from 32, else 64)."""
+    rows = T * k
+    return 256 if rows >= 128 * E else 128 if rows >= 32 * E else 64
+
+
+def tile_cover_tokens(orc, ids, E, TM):
+    """A small set of tokens whose rows touch every (group, M-tile) work item
+    of the grouped GEMM (groups in the stable counting-sort order, the shared
+    group E holding every token, M-tiles of TM rows) and include the last
+    row of every partly filled tile: those last rows first, then greedily the
+    token that covers the most work items still uncovered."""
+    T, k = ids.shape
+    offsets, row_token, row_of, _ = orc.permute(ids, E)
+    grp = np.searchsorted(offsets, np.arange(offsets[-1]), side="right") - 1
+    tile_base = np.zeros(E + 2, np.int64)
+    n_tiles = (np.diff(offsets) + TM - 1) // TM
+    tile_base[1:] = np.cumsum(n_tiles)
+    tile_of_row = tile_base[grp] + (np.arange(offsets[-1]) - offsets[grp]) // TM
+    cover = np.where(row_of >= 0, tile_of_row[np.maximum(row_of, 0)], -1)   # [T][k+1]
+    uncovered = np.ones(int(tile_base[-1]), bool)
+    pick = set()
+    for g in range(E + 1):
+        n = offsets[g + 1] - offsets[g]
+        if n % TM:
+            pick.add(int(row_token[offsets[g + 1] - 1]))
+    for t in pick:
+        uncovered[cover[t][cover[t] >= 0]] = False
+    while uncovered.any():
+        score = np.where(cover >= 0, uncovered[np.maximum(cover, 0)], False).sum(axis=1)
+        t = int(np.argmax(score))
+        pick.add(t)
+        uncovered[cover[t][cover[t] >= 0]] = False
+    return np.array(sorted(pick), np.int32)

@@ -16,7 +16,7 @@ if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import bit_expert_ffn_moe_amd as moe  # noqa: E402
-from gpu_util import DevLayer, d2h, rel_l2, to_dev, to_host  # noqa: E402
+from gpu_util import DevLayer, check_gpu_selection, d2h, rel_l2, to_dev, to_host  # noqa: E402
 
 orc = Oracle()
 
@@ -101,21 +101,29 @@ def test_act_quant_encoder_exhaustive_sweep():
                                      (5, 4096, 256, 6), (37, 4096, 256, 6),
                                      (300, 4096, 256, 6), (40, 1024, 100, 16),
                                      (4, 8192, 256, 16), (2, 8192, 200, 11),
-                                     (33, 8192, 200, 11), (257, 4096, 256, 6)])
-def test_route_ids_bitexact(T, H, E, k):
+                                     (33, 8192, 200, 11), (257, 4096, 256, 6),
+                                     (3, 384, 256, 6), (1024, 4096, 256, 6)])
+def test_route_ids_valid_topk(T, H, E, k):
+    """The GPU's ids are a top-k of the oracle's logits: equal to the
+    oracle's, except between logits within the near-tie band (the kernels
+    sum the same products in an order of their own); bit-exact where both
+    orders coincide (H <= 256: at most four 64-wide chunks).  Weights match
+    the oracle's renormalised sigmoids of the GPU's ids."""
     _print("route", T, H, E, k)
     x = synth.normal_bf16(900 + T, 1, (T, H), 1.0)
     wr = synth.normal_bf16(900 + T, 2, (H, E), 0.02)
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    ws_b = 1 << 24
+    ws_b = (1 << 22) + ((H // 64 + 3) // 4) * T * E * 4   # control block + group sums
     ws = torch.zeros(ws_b, dtype=torch.uint8, device="cuda")
     moe.moe_workspace_init(ws, ws_b)
-    for rep in range(2):   # second call checks the arrival counter was reset
-        moe.moe_route(to_dev(x), to_dev(wr), T, H, E, k, ids, w, ws, ws_b)
-        ir, wref = orc.route(x, wr, k)
-        assert np.array_equal(to_host(ids), ir), rep
-        assert np.allclose(to_host(w), wref, rtol=1e-5, atol=0), rep
+    moe.moe_route(to_dev(x), to_dev(wr), T, H, E, k, ids, w, ws, ws_b)
+    ig, wg = to_host(ids), to_host(w)
+    check_gpu_selection(orc, x, wr, k, ig, wg, exact=H <= 256)
+    # a second call (the arrival counters were reset) gives the same result
+    moe.moe_route(to_dev(x), to_dev(wr), T, H, E, k, ids, w, ws, ws_b)
+    assert np.array_equal(to_host(ids), ig)
+    assert np.array_equal(to_host(w), wg)
 
 
 @pytest.mark.parametrize("T", [1, 7, 64])
@@ -304,6 +312,8 @@ def _mfma_h_error_bound(L, e, xq, xs):
     ("tiny_t8", dict(T=8, fmt="fp8")),
     ("tiny_t8", dict(T=200, routing="zipf", zipf_s=0.5)),
     ("tiny_t8", dict(T=1, fmt="fp8")),
+    ("tiny_t8", dict(T=3, H=384)),            # down: half an N-block at the end of H
+    ("tiny_t8", dict(T=3, H=384, fmt="fp8")),
 ])
 def test_expert_ffn_stagewise(name, over):
     _print("expert_ffn stagewise", name, over)
@@ -320,24 +330,34 @@ def test_expert_ffn_stagewise(name, over):
     offsets, row_token, row_of, _ = orc.permute(ids, E)
     R = T * k + T
     y = torch.zeros((R, H), dtype=torch.float32, device="cuda")
-    moe.moe_expert_ffn(D.w, to_dev(xq), to_dev(xs), T, k, to_dev(offsets), to_dev(row_token), y,
-                       D.ws, D.ws_bytes)
-    yg = to_host(y)
+    # the MFMA path's fp32 h goes to a debug sink (the VALU path keeps it in ws)
+    sink = torch.full((R, I), np.nan, dtype=torch.float32, device="cuda")
+    moe.moe_debug_store_h(sink, R * I)
+    try:
+        moe.moe_expert_ffn(D.w, to_dev(xq), to_dev(xs), T, k, to_dev(offsets), to_dev(row_token),
+                           y, D.ws, D.ws_bytes)
+        yg = to_host(y)
+    finally:
+        moe.moe_debug_store_h(None, 0)
     hp, hqp, hsp = moe.moe_debug_intermediates(D.w, T, k, D.ws, D.ws_bytes)
     hq = d2h(hqp, (R, I), np.uint8)
     hs = d2h(hsp, (R, I // 128), np.float32)
-    h = d2h(hp, (R, I), np.float32) if hp is not None else None
+    gemv = hp is not None
+    h = d2h(hp, (R, I), np.float32) if gemv else to_host(sink)
+    assert np.isfinite(h).all()
     grp = np.searchsorted(offsets, np.arange(R), side="right") - 1
     y_err, y_ref_all, y_own_all = [], [], []
     for r in range(R):
         e, t = int(grp[r]), int(row_token[r])
         h_ref, hq_ref, hs_ref, y_ref = orc.expert_row(W, e, xq[t], xs[t])
-        if h is not None:
-            assert rel_l2(h[r], h_ref) <= 1e-5, r
-            q2, s2 = orc.act_quant(h[r][None, :])
-            assert np.array_equal(hq[r], q2[0]) and np.array_equal(hs[r], s2[0]), r
-        gemv = h is not None
+        # the act_quant rule applied to the GPU's own h, bit for bit (both paths)
+        q2, s2 = orc.act_quant(h[r][None, :])
+        assert np.array_equal(hq[r], q2[0]) and np.array_equal(hs[r], s2[0]), r
         h_err = None if gemv else _mfma_h_error_bound(L, e, xq[t], xs[t])
+        if gemv:
+            assert rel_l2(h[r], h_ref) <= 1e-5, r
+        else:
+            assert np.all(np.abs(h[r].astype(np.float64) - h_ref) <= h_err), r
         diff, near = _tie_band(h_ref, hs[r], hq[r], hq_ref, BAND_GEMV, h_err)
         assert np.all(near[diff]), (r, int(diff.sum()))
         assert np.allclose(hs[r], hs_ref, rtol=1e-5 if gemv else 2e-4, atol=0), r

@@ -16,8 +16,9 @@ if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import bit_expert_ffn_moe_amd as moe  # noqa: E402
-from gpu_util import (DevLayer, bf16_bits_to_f32, d2h, f64_to_bf16_bits, max_rel,  # noqa: E402
-                      rel_l2, to_dev, to_host)
+from gpu_util import (DevLayer, bf16_bits_to_f32, check_gpu_selection, d2h,  # noqa: E402
+                      f64_to_bf16_bits, gpu_routing, grouped_gemm_tile, max_rel, rel_l2,
+                      routed_reference, tile_cover_tokens, to_dev, to_host)
 
 orc = Oracle()
 REL_L2, MAX_ABS = 2e-3, 1e-2
@@ -52,14 +53,27 @@ def _sample_tokens(ids, T, n, seed=0):
 
 
 def _run(name, sample=None, threads=0, **over):
+    """Forward on the GPU, then the oracle on all tokens, on `sample` random
+    ones, or (sample="tiles") on tokens whose rows cover every (group,
+    M-tile) work item of the grouped GEMM and the last row of every partly
+    filled tile."""
     L = synth.make_layer(name, **over)
     wl = L.wl
     D = DevLayer(L)
     _print("layer", name, over, "T", wl.T, "fmt", wl.fmt, "routing", wl.routing)
     out = to_host(D.forward())
     W = Weights.from_layer(L)
-    tok = None if sample is None else _sample_tokens(L.ids, wl.T, sample)
-    ref = orc.forward(W, L.wr, L.x, wl.k, ids=L.ids, w=L.w, tokens=tok, threads=threads)
+    ids_g, w_g = gpu_routing(D, wl.T) if L.ids is None else (None, None)
+    if sample == "tiles":
+        ids = L.ids if L.ids is not None else ids_g
+        TM = grouped_gemm_tile(wl.T, wl.k, wl.E)
+        tok = np.union1d(tile_cover_tokens(orc, ids, wl.E, TM), [0, wl.T - 1]).astype(np.int32)
+        _print(f"  {tok.size} tokens cover every work item of {TM}-token tiles")
+    elif sample is not None:
+        tok = _sample_tokens(L.ids, wl.T, sample)
+    else:
+        tok = None
+    ref = routed_reference(orc, W, L, ids_g, w_g, tok=tok, threads=threads)
     got = out if tok is None else out[tok]
     _check(got, ref, f"{name} {over}")
     assert moe.moe_device_status(D.ws) == 0
@@ -69,7 +83,9 @@ def _run(name, sample=None, threads=0, **over):
 @pytest.mark.parametrize("over", [dict(), dict(fmt="fp8"), dict(T=1), dict(T=1, fmt="fp8"),
                                   dict(T=2), dict(T=3, E=3, k=3), dict(T=4, fmt="fp8"),
                                   dict(T=5), dict(T=130, routing="zipf", zipf_s=1.0),
-                                  dict(E=1, k=1, T=9), dict(E=3, k=3, T=17)])
+                                  dict(E=1, k=1, T=9), dict(E=3, k=3, T=17),
+                                  dict(T=3, H=384), dict(T=3, H=384, fmt="fp8"),
+                                  dict(T=1, H=384), dict(T=40, H=640, fmt="fp8")])
 def test_tiny_layer(over):
     _run("tiny_t8", **over)
 
@@ -94,11 +110,15 @@ def test_decode_t1_full_shapes_many_tokens():
     """One token per call at hidden 4096 / intermediate 2048 / 256 experts top-6."""
     L = synth.make_layer("decode_t1", T=24)
     D = DevLayer(L, max_tokens=1)
-    outs = []
+    outs, ids_g, w_g = [], [], []
     for t in range(L.wl.T):
         outs.append(to_host(D.forward(x=D.x[t:t + 1], T=1))[0])
+        i1, w1 = gpu_routing(D, 1)
+        ids_g.append(i1[0])
+        w_g.append(w1[0])
     out = np.stack(outs)
-    ref = orc.forward(Weights.from_layer(L), L.wr, L.x, L.wl.k)
+    ids_g, w_g = np.stack(ids_g), np.stack(w_g)
+    ref = routed_reference(orc, Weights.from_layer(L), L, ids_g, w_g)
     _check(out, ref, "decode_t1 x24")
     assert moe.moe_device_status(D.ws) == 0
     ids = torch.empty((L.wl.T, 6), dtype=torch.int32, device="cuda")
@@ -108,8 +128,7 @@ def test_decode_t1_full_shapes_many_tokens():
     rws = torch.zeros(rb, dtype=torch.uint8, device="cuda")
     moe.moe_workspace_init(rws, rb)
     moe.moe_route(D.x, D.wr, L.wl.T, 4096, 256, 6, ids, w, rws, rb)
-    ir, _ = orc.route(L.x, L.wr, 6)
-    assert np.array_equal(to_host(ids), ir)
+    check_gpu_selection(orc, L.x, L.wr, 6, to_host(ids), to_host(w), what="24 tokens at once")
 
 
 def test_decode_t1_repeated_expert_ids():
@@ -130,7 +149,10 @@ def test_decode_t1_repeated_expert_ids():
     for _ in range(2):
         moe.dsv4_moe_forward(D2.w, D2.wr, D2.x, 1, 6, None, None, out2, moe.MOE_DT_F32, D.ws,
                              D.ws_bytes)
-        _check(to_host(out2), orc.forward(Weights.from_layer(L2), L2.wr, L2.x, 6), "decode I=1024")
+        ip, wp = moe.moe_debug_routing(D2.w, 1, 6, D.ws, D.ws_bytes)
+        ref2 = routed_reference(orc, Weights.from_layer(L2), L2, d2h(ip, (1, 6), np.int32),
+                                d2h(wp, (1, 6), np.float32))
+        _check(to_host(out2), ref2, "decode I=1024")
     _check(to_host(D.forward()), ref, "decode repeated ids, after I=1024")
     assert moe.moe_device_status(D.ws) == 0
 
@@ -150,19 +172,20 @@ def test_decode_layer_matches_stagewise_kernels(name, over):
     R = k + 1
     D = DevLayer(L)
     W = Weights.from_layer(L)
-    ids, _ = orc.route(L.x, L.wr, k)
-    xq, xs = orc.act_quant(L.x)
-    offsets, row_token, row_of, _ = orc.permute(ids, E)
-    grp = np.searchsorted(offsets, np.arange(R), side="right") - 1
-    rows_ref = [orc.expert_row(W, int(grp[r]), xq[0], xs[0]) for r in range(R)]
-    ref = orc.forward(W, L.wr, L.x, k)
-    # the separate kernels, on a workspace of their own
+    # the separate kernels, on a workspace of their own; the GPU's selection
+    # (a valid top-k of the oracle's logits) is the routing of the oracle's rows
     ws2 = torch.zeros(D.ws_bytes, dtype=torch.uint8, device="cuda")
     moe.moe_workspace_init(ws2, D.ws_bytes)
     gids = torch.empty((1, k), dtype=torch.int32, device="cuda")
     gw = torch.empty((1, k), dtype=torch.float32, device="cuda")
     moe.moe_route(D.x, D.wr, 1, H, E, k, gids, gw, ws2, D.ws_bytes)
-    assert np.array_equal(to_host(gids), ids)
+    ids, tw = to_host(gids), to_host(gw)
+    check_gpu_selection(orc, L.x, L.wr, k, ids, tw)
+    xq, xs = orc.act_quant(L.x)
+    offsets, row_token, row_of, _ = orc.permute(ids, E)
+    grp = np.searchsorted(offsets, np.arange(R), side="right") - 1
+    rows_ref = [orc.expert_row(W, int(grp[r]), xq[0], xs[0]) for r in range(R)]
+    ref = routed_reference(orc, W, L, ids, tw)
     moe.moe_expert_gate_up(D.w, to_dev(xq), to_dev(xs), 1, k, to_dev(offsets), to_dev(row_token),
                            ws2, D.ws_bytes)
     out2 = torch.empty((1, H), dtype=torch.float32, device="cuda")
@@ -173,6 +196,7 @@ def test_decode_layer_matches_stagewise_kernels(name, over):
         out = to_host(D.forward())
         _check(out, ref, f"decode {name} {over} call {call}")
         assert np.array_equal(out, o2), call
+        assert np.array_equal(gpu_routing(D, 1)[0], ids), call
         hp, hqp, hsp = moe.moe_debug_intermediates(D.w, 1, k, D.ws, D.ws_bytes)
         h = d2h(hp, (R, I), np.float32)
         hq = d2h(hqp, (R, I), np.uint8)
@@ -190,15 +214,25 @@ def test_verify_t32_full_shapes():
 
 
 def test_prefill_fp4_partial_batch():
-    _run("prefill_fp4_t4096", T=512, sample=24)
+    _run("prefill_fp4_t4096", T=512, sample="tiles", threads=16)     # 64-token tiles
 
 
-def test_prefill_fp4_full_sampled():
-    _run("prefill_fp4_t4096", sample=24)
+def test_prefill_fp4_full_tiles():
+    _run("prefill_fp4_t4096", sample="tiles", threads=16)            # 128-token tiles
 
 
-def test_prefill_fp8_full_sampled():
-    _run("prefill_fp8_t8192", sample=24)
+def test_prefill_fp4_256_token_tiles():
+    """6144 tokens: 256-token FP4 tiles with hidden 4096 (32 K steps through
+    the stage ring from rotated starts), hot groups of many M-tiles."""
+    _run("prefill_fp4_t4096", T=6144, sample="tiles", threads=16)
+
+
+def test_prefill_fp8_full_tiles():
+    _run("prefill_fp8_t8192", sample="tiles", threads=16)            # 256-token tiles
+
+
+def test_prefill_fp8_128_token_tiles():
+    _run("prefill_fp8_t8192", T=4096, sample="tiles", threads=16)
 
 
 def test_all_tokens_on_the_same_experts():
