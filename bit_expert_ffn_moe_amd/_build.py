@@ -33,9 +33,25 @@ FLAGS = [
 
 
 def build(verbose: bool = False, extra: list[str] | None = None, out: str | None = None) -> str:
+    """Compile each source to an object (in parallel), then link the library."""
+    from concurrent.futures import ThreadPoolExecutor
     out = out or SO
-    cmd = [HIPCC, *FLAGS, *(extra or []), *[os.path.join(CSRC, s) for s in SOURCES], "-o",
-           out + ".tmp"]
+    objdir = os.path.join(ROOT, "_build", os.path.basename(out) + ".objs")
+    os.makedirs(objdir, exist_ok=True)
+    cflags = [f for f in FLAGS if f != "-shared"]
+
+    def compile_one(src):
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        cmd = [HIPCC, *cflags, *(extra or []), "-c",
+               os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), file=sys.stderr)
+        subprocess.run(cmd, check=True)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True)
