@@ -100,6 +100,7 @@ def src_hash():
 
 class Hip:
     def __init__(self):
+        import torch  # noqa: F401  (first: its HIP runtime is the one every caller binds to)
         L = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch loaded
         vp, pvp = ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)
         for name, args in [("hipStreamBeginCapture", [vp, ctypes.c_int]),
@@ -220,61 +221,80 @@ class Bench:
                              moe.MOE_DT_BF16, self.ws, self.ws_bytes, self.sp)
 
 
-def moe_kernel_id(moe, path):
-    return moe.MOE_KERNEL_GEMV_GATE_UP if path == "gemv" else moe.MOE_KERNEL_GEMM_GATE_UP
+def kernel_ids(moe, path):
+    """(gate+up, down) kernel ids of the timing hook for the path."""
+    if path == "gemv":
+        return moe.MOE_KERNEL_GEMV_GATE_UP, moe.MOE_KERNEL_GEMV_DOWN
+    return moe.MOE_KERNEL_GEMM_GATE_UP, moe.MOE_KERNEL_GEMM_DOWN
 
 
-def run(args):
+def time_kernel(B, which, n_ev):
+    """Average duration (s) of kernel `which` over n_ev eager product steps,
+    from HIP events the library records in that kernel's own dispatch."""
     import numpy as np
     import torch
-
-    import synth
-    wl = synth.WORKLOADS[args.workload]
-    copies = args.copies or (8 if wl.name == "decode_t1" else 2 if wl.T <= 64 else 1)
-    B = Bench(wl.name, copies, 64)
-    B.hip = Hip()
-    per_graph = args.graph_steps or (64 if wl.T == 1 else 8 if wl.T <= 64 else 1)
-    per_graph = max(1, min(per_graph, args.steps))
-    # eager warm-up (also caches the library's one-time device check)
-    for i in range(max(2, min(args.warmup, 16))):
-        B.product_step(i)
-    torch.cuda.synchronize()
-    # graph of `per_graph` product steps
-    g1, ex1 = B.hip.capture(B.sp, lambda: [B.product_step(i) for i in range(per_graph)])
-    reps = max(1, args.steps // per_graph)
-    steps = reps * per_graph
-    wreps = max(1, args.warmup // per_graph)
-    L = B.hip.L
-    for _ in range(wreps):
-        B.hip.ok(L.hipGraphLaunch(ex1, B.sp), "hipGraphLaunch")
-    torch.cuda.synchronize()
-    # timed region: plain graph replays
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        B.hip.ok(L.hipGraphLaunch(ex1, B.sp), "hipGraphLaunch")
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    # dominant-kernel timing: the same product steps, run eagerly, with the
-    # gate+up kernel's launches recording a pair of HIP events at that
-    # kernel's own begin and end (the library's debug timing hook puts them
-    # in the kernel's dispatch: no queueing gap is counted)
-    n_ev = max(1, min(256, steps))
     evs = [(B.hip.event(), B.hip.event()) for _ in range(n_ev)]
-    which = moe_kernel_id(B.moe, B.path)
     for i in range(n_ev):
         B.moe.moe_debug_time_kernel(which, evs[i][0], evs[i][1])
         B.product_step(i)
     B.moe.moe_debug_time_kernel(which, None, None)
     torch.cuda.synchronize()
-    gu_ms = [B.hip.elapsed_ms(a, b) for a, b in evs]
+    ms = [B.hip.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        B.hip.L.hipEventDestroy(a)
+        B.hip.L.hipEventDestroy(b)
+    return float(np.mean(ms)) * 1e-3, float(np.percentile(ms, 10)) * 1e-3, \
+        float(np.percentile(ms, 90)) * 1e-3
+
+
+def measure(wl_name, steps, warmup, copies=0, graph_steps=0, hip=None):
+    """Time `steps` whole-layer steps of a workload (graph replays) and its
+    gate+up and down kernels; returns the figures as a dict."""
+    import numpy as np
+    import torch
+
+    import synth
+    wl = synth.WORKLOADS[wl_name]
+    copies = copies or (8 if wl.name == "decode_t1" else 2 if wl.T <= 64 else 1)
+    B = Bench(wl.name, copies, 64)
+    B.hip = hip or Hip()
+    per_graph = graph_steps or (64 if wl.T == 1 else 8 if wl.T <= 64 else 1)
+    per_graph = max(1, min(per_graph, steps))
+    # eager warm-up (also caches the library's one-time device check)
+    for i in range(max(2, min(warmup, 16))):
+        B.product_step(i)
+    torch.cuda.synchronize()
+    g1, ex1 = B.hip.capture(B.sp, lambda: [B.product_step(i) for i in range(per_graph)])
+    reps = max(1, steps // per_graph)
+    steps = reps * per_graph
+    L = B.hip.L
+    for _ in range(max(1, warmup // per_graph)):
+        B.hip.ok(L.hipGraphLaunch(ex1, B.sp), "hipGraphLaunch")
+    torch.cuda.synchronize()
+    # timed region: plain graph replays, one event pair per replay as well
+    ev = [B.hip.event() for _ in range(reps + 1)]
+    t0 = time.perf_counter()
+    B.hip.ok(L.hipEventRecord(ev[0], B.sp), "hipEventRecord")
+    for r in range(reps):
+        B.hip.ok(L.hipGraphLaunch(ex1, B.sp), "hipGraphLaunch")
+        B.hip.ok(L.hipEventRecord(ev[r + 1], B.sp), "hipEventRecord")
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    rep_ms = [B.hip.elapsed_ms(ev[r], ev[r + 1]) / per_graph for r in range(reps)]
+    for e in ev:
+        L.hipEventDestroy(e)
     L.hipGraphExecDestroy(ex1)
     L.hipGraphDestroy(g1)
+    n_ev = max(1, min(256 if wl.T <= 64 else 16, steps))
+    gu_id, dn_id = kernel_ids(B.moe, B.path)
+    gu_avg_s, gu_p10, gu_p90 = time_kernel(B, gu_id, n_ev)
+    dn_avg_s, _, _ = time_kernel(B, dn_id, n_ev)
     # algorithmic work of the steps
     if wl.routing == "zipf":
         ids_steps = [B.layer.ids]
     else:
         ids_steps = []
-        for i in range(per_graph):
+        for i in range(min(per_graph, 64)):
             x = B.x_of(i)
             B.moe.moe_route(x, B.wr, B.T, wl.H, wl.E, wl.k, B.ids, B.tw, B.ws, B.ws_bytes, B.sp)
             torch.cuda.synchronize()
@@ -282,8 +302,6 @@ def run(args):
     works = [work(wl, ids, B.path) for ids in ids_steps]
     avg = {key: float(np.mean([w[key] for w in works])) for key in works[0]}
     ms_per_step = elapsed * 1e3 / steps
-    value = B.T * steps / elapsed
-    gu_avg_s = float(np.mean(gu_ms)) * 1e-3
     gu_gbs = avg["gu_bytes"] / gu_avg_s / 1e9
     gu_tflops = avg["gu_flops"] / gu_avg_s / 1e12
     t_hbm = avg["gu_bytes"] / (HBM_PEAK_GBS * 1e9)
@@ -296,14 +314,82 @@ def run(args):
                     unit="TFLOP/s", frac=round(gu_tflops / FP8_PEAK_TFLOPS, 4))
     kern = DOMINANT[B.path]
     roof.update(kernel=kern, kernel_avg_us=round(gu_avg_s * 1e6, 2),
+                kernel_p10_us=round(gu_p10 * 1e6, 2), kernel_p90_us=round(gu_p90 * 1e6, 2),
                 algorithmic_bytes=int(avg["gu_bytes"]), algorithmic_flops=int(avg["gu_flops"]),
+                hbm_gbs=round(gu_gbs, 1), hbm_frac=round(gu_gbs / HBM_PEAK_GBS, 4),
                 mfma_tflops=round(gu_tflops, 2),
                 mfma_frac=round(gu_tflops / FP8_PEAK_TFLOPS, 4),
                 traffic=traffic_from_profiles(kern, wl.name))
     step_gbs = avg["step_bytes"] / (ms_per_step * 1e-3) / 1e9
+    res = dict(workload=wl.name, steps=steps, ms_per_step=round(ms_per_step, 6),
+               ms_p10=round(float(np.percentile(rep_ms, 10)), 6),
+               ms_p90=round(float(np.percentile(rep_ms, 90)), 6),
+               tokens_per_s=round(B.T * steps / elapsed, 2), path=B.path,
+               step_hbm_gbs=round(step_gbs, 1), step_roofline_frac=round(step_gbs / HBM_PEAK_GBS, 4),
+               touched_experts_avg=round(avg["touched"], 2), layer_copies=copies,
+               graph_steps=per_graph, roofline=roof,
+               down_kernel_avg_us=round(dn_avg_s * 1e6, 2))
+    if B.path == "gemm":
+        # the grouped GEMM as a whole (gate+up and down): flops of every row
+        ff = 2 * 3 * wl.H * wl.I * avg["rows"]
+        t = gu_avg_s + dn_avg_s
+        res["grouped_gemm"] = dict(gate_up_us=round(gu_avg_s * 1e6, 1),
+                                   down_us=round(dn_avg_s * 1e6, 1),
+                                   flops=int(ff), tflops=round(ff / t / 1e12, 1),
+                                   mfma_frac=round(ff / t / 1e12 / FP8_PEAK_TFLOPS, 4))
+    del B
+    torch.cuda.empty_cache()
+    return res
+
+
+def stream_ceiling(hip):
+    """Plain streaming read (the library's debug read kernel) of a buffer
+    the size of the decode gate+up's weights and of a 2 GiB buffer: the
+    practical HBM read ceiling, as GB/s (best grid of a few)."""
+    import torch
+
+    import bit_expert_ffn_moe_amd as moe
+    out = {}
+    sink = torch.zeros(4, dtype=torch.uint8, device="cuda:0")
+    L = hip.L
+    for label, nbytes in (("54MB", 53_481_600 // 16 * 16), ("2GiB", 2 << 30)):
+        n_buf = max(1, min(16, (1 << 30) // nbytes)) if nbytes < (1 << 30) else 1
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda:0") for _ in range(n_buf)]
+        best = None
+        for blocks in (512, 1024, 2048, 4096):
+            e0, e1 = hip.event(), hip.event()
+            reps = 32 if nbytes < (1 << 30) else 4
+            for i in range(4):
+                moe.moe_debug_stream_read(bufs[i % n_buf], nbytes, sink, blocks)
+            torch.cuda.synchronize()
+            st = torch.cuda.current_stream().cuda_stream
+            L.hipEventRecord(e0, st)
+            for i in range(reps):
+                moe.moe_debug_stream_read(bufs[i % n_buf], nbytes, sink, blocks)
+            L.hipEventRecord(e1, st)
+            torch.cuda.synchronize()
+            gbs = nbytes * reps / (hip.elapsed_ms(e0, e1) * 1e-3) / 1e9
+            best = gbs if best is None or gbs > best else best
+            L.hipEventDestroy(e0)
+            L.hipEventDestroy(e1)
+        out[label] = round(best, 1)
+        del bufs
+    torch.cuda.empty_cache()
+    return out
+
+
+SUB_WORKLOADS = (("tiny_t8", 256, 32), ("verify_t32", 64, 8),
+                 ("prefill_fp4_t4096", 10, 3), ("prefill_fp8_t8192", 10, 3))
+
+
+def run(args):
+    import synth
+    wl = synth.WORKLOADS[args.workload]
+    hip = Hip()
+    head = measure(wl.name, args.steps, args.warmup, args.copies, args.graph_steps, hip)
     line = {
-        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
-        "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": head["steps"], "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": ("fp8e4m3 x fp4e2m1, fp32 accumulate" if wl.fmt == "fp4"
                   else "fp8e4m3 x fp8e4m3, fp32 accumulate"),
@@ -311,13 +397,26 @@ def run(args):
         "config": {"workload": wl.name, "tokens": wl.T, "hidden": wl.H, "inter": wl.I,
                    "experts": wl.E, "top_k": wl.k, "shared_experts": 1,
                    "weights": wl.fmt, "routing": wl.routing if wl.routing == "router"
-                   else f"zipf s={wl.zipf_s} (injected)", "layer_copies": copies,
-                   "graph_steps": per_graph, "touched_experts_avg": round(avg["touched"], 2),
-                   "step_hbm_gbs": round(step_gbs, 1),
-                   "step_roofline_frac": round(step_gbs / HBM_PEAK_GBS, 4)},
-        "roofline": roof,
-        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(wl, args),
+                   else f"zipf s={wl.zipf_s} (injected)", "layer_copies": head["layer_copies"],
+                   "graph_steps": head["graph_steps"],
+                   "touched_experts_avg": head["touched_experts_avg"],
+                   "step_hbm_gbs": head["step_hbm_gbs"],
+                   "step_roofline_frac": head["step_roofline_frac"],
+                   "ms_p10": head["ms_p10"], "ms_p90": head["ms_p90"],
+                   "down_kernel_avg_us": head["down_kernel_avg_us"]},
+        "roofline": head["roofline"],
     }
+    if not args.no_sub and args.workload == "decode_t1":
+        ceil = stream_ceiling(hip)
+        line["hbm_read_ceiling_gbs"] = ceil
+        line["roofline"]["frac_of_measured_ceiling"] = round(
+            head["roofline"]["hbm_gbs"] / ceil["54MB"], 4)
+        subs = {}
+        for name, st, wu in SUB_WORKLOADS:
+            print(f"# sub-workload {name}", file=sys.stderr, flush=True)
+            subs[name] = measure(name, st, wu, hip=hip)
+        line["workloads"] = subs
+    line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(wl, args)
     print(json.dumps(line), flush=True)
 
 
@@ -338,29 +437,47 @@ def traffic_from_profiles(kern, wl_name):
         return None
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(wl, args):
-    """The oracle as it stands, on the host cores, on a bounded sample."""
+    """The oracle as it stands, on the host cores, on a bounded sample; and
+    one thread on a smaller sample."""
     import synth
     from oracle import Oracle, Weights
-    threads = min(16, os.cpu_count() or 1)
+    nproc = os.cpu_count() or 1
+    threads = min(16, nproc)
     orc = Oracle()
-    if wl.name == "decode_t1":
-        L = synth.make_layer(wl.name, T=max(1, threads * 2))
-        n = L.wl.T
-        tokens = None
-        sample = f"{n} single-token decode forwards (router on x), all layer shapes as timed"
-    else:
-        L = synth.make_layer(wl.name)
-        n = min(wl.T, max(threads * 2, 8))
-        tokens = list(range(0, wl.T, max(1, wl.T // n)))[:n]
-        sample = f"{len(tokens)} of the {wl.T} tokens of the timed batch (same weights and routing)"
-    W = Weights.from_layer(L)
-    t0 = time.perf_counter()
-    orc.forward(W, L.wr, L.x, L.wl.k, ids=L.ids, w=L.w, tokens=tokens, threads=threads)
-    el = time.perf_counter() - t0
-    ntok = n if tokens is None else len(tokens)
-    return {"value": round(ntok / el, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": sample, "seconds": round(el, 2)}
+
+    def timed(n_tok, thr):
+        if wl.name == "decode_t1":
+            L = synth.make_layer(wl.name, T=n_tok)
+            tokens = None
+            sample = f"{n_tok} single-token decode forwards (router on x), all layer shapes as timed"
+        else:
+            L = synth.make_layer(wl.name)
+            tokens = list(range(0, wl.T, max(1, wl.T // n_tok)))[:n_tok]
+            sample = f"{len(tokens)} of the {wl.T} tokens of the timed batch (same weights and routing)"
+        W = Weights.from_layer(L)
+        t0 = time.perf_counter()
+        orc.forward(W, L.wr, L.x, L.wl.k, ids=L.ids, w=L.w, tokens=tokens, threads=thr)
+        el = time.perf_counter() - t0
+        return n_tok / el, el, sample
+
+    v, el, sample = timed(max(8, threads * 2), threads)
+    v1, el1, sample1 = timed(2, 1)
+    return {"value": round(v, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(el, 2), "nproc": nproc,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"), "cpu_model": _cpu_model(),
+            "single_thread": {"value": round(v1, 4), "unit": "tokens/s", "seconds": round(el1, 2),
+                              "sample": sample1}}
 
 
 # --------------------------------------------------------------------------
@@ -435,6 +552,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0)
     ap.add_argument("--graph-steps", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="time only --workload (no read ceiling, no other workloads)")
     ap.add_argument("--calib-mib", type=int, default=0,
                     help="after timing, run a plain float32 add of this many MiB (counter calibration)")
     ap.add_argument("--summarize", default=None)
