@@ -22,6 +22,7 @@ MOE_W_FP4_E2M1_UE8M0_K32, MOE_W_FP8_E4M3_F32_B128 = 1, 2
 MOE_DT_BF16, MOE_DT_F32 = 1, 2
 MOE_STATUS_BAD_EXPERT_ID, MOE_STATUS_SYNC_TIMEOUT = 1, 2
 MOE_KERNEL_GEMV_GATE_UP, MOE_KERNEL_GEMM_GATE_UP, MOE_KERNEL_GEMV_DOWN, MOE_KERNEL_GEMM_DOWN = 1, 2, 3, 4
+MOE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 if not os.path.exists(_SO):
     raise ImportError(
@@ -65,6 +66,8 @@ _sigs = {
     "moe_combine": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp], ctypes.c_int),
     "dsv4_moe_forward": ([_W, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _i32, _vp, _sz, _vp],
                          ctypes.c_int),
+    "dsv4_moe_forward_noalloc": ([_W, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _i32, _vp],
+                                 ctypes.c_int),
     "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "moe_device_status": ([_vp, _vp, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int],
                           ctypes.c_int),
@@ -176,6 +179,14 @@ def dsv4_moe_forward(w, w_router, x, T, k, routing_ids, routing_w, out, out_dtyp
     return _check(_lib.dsv4_moe_forward(ctypes.byref(w), _ptr(w_router), _ptr(x), T, k,
                                         _ptr(routing_ids), _ptr(routing_w), _ptr(out), out_dtype,
                                         _ptr(ws), ws_bytes, _stream(stream)), "dsv4_moe_forward")
+
+
+def dsv4_moe_forward_noalloc(w, w_router, x, T, k, routing_ids, routing_w, out, out_dtype,
+                             stream=None) -> int:
+    return _check(_lib.dsv4_moe_forward_noalloc(ctypes.byref(w), _ptr(w_router), _ptr(x), T, k,
+                                                _ptr(routing_ids), _ptr(routing_w), _ptr(out),
+                                                out_dtype, _stream(stream)),
+                  "dsv4_moe_forward_noalloc")
 
 
 def moe_device_status(ws, stream=None, clear: bool = False) -> int:

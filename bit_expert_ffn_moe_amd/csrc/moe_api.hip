@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -541,6 +542,45 @@ int enqueue_forward(const moe_weights* w, const uint16_t* w_router, const uint16
                       st);
 }
 
+// ---- the allocation-free forward: a file-scope device array as workspace --
+
+// At most this much workspace per call: the one-token and small-batch
+// shapes (at hidden 4096, intermediate 2048, top-6, about 100 tokens).
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+static_assert(kStaticScratchBytes == MOE_NOALLOC_SCRATCH_BYTES, "moe.h limit");
+
+// In host code `scratch` names a host-side stand-in, not the device array:
+// its device address on each GPU comes from hipGetSymbolAddress, once per
+// device, and only that address is ever handed to a kernel.
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64];
+
+// Device address of this device's `scratch`, looked up (with the device
+// current) on its first use, when its control block is also cleared by a
+// fill kernel on `st` (the kernels keep it zero from then on).
+int static_scratch(void** ptr, hipStream_t st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return MOE_ENOTSUP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return MOE_ELAUNCH;
+    }
+    int rc = launch_status(launch_zero_words((uint32_t*)p, (int)(kCtlBytes / 4), st));
+    if (rc) return rc;
+    g_scratch_dev[dev] = p;
+  }
+  *ptr = g_scratch_dev[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 }  // namespace bef
 
@@ -555,6 +595,22 @@ int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint1
   rc = check_ws(ws, ws_bytes, layout_w(w, T, k).total);
   if (rc) return rc;
   rc = check_device();
+  if (rc) return rc;
+  return enqueue_forward(w, w_router, x, T, k, routing_ids, routing_w, out, out_dtype, ws,
+                         (hipStream_t)stream);
+}
+
+int dsv4_moe_forward_noalloc(const moe_weights* w, const uint16_t* w_router, const uint16_t* x,
+                             int32_t T, int32_t k, const int32_t* routing_ids,
+                             const float* routing_w, void* out, int32_t out_dtype, void* stream) {
+  int rc = check_forward_args(w, w_router, x, T, k, routing_ids, routing_w, out, out_dtype);
+  if (rc) return rc;
+  if (T == 0) return MOE_OK;
+  if (layout_w(w, T, k).total > kStaticScratchBytes) return MOE_ENOTSUP;
+  rc = check_device();
+  if (rc) return rc;
+  void* ws = nullptr;
+  rc = static_scratch(&ws, (hipStream_t)stream);
   if (rc) return rc;
   return enqueue_forward(w, w_router, x, T, k, routing_ids, routing_w, out, out_dtype, ws,
                          (hipStream_t)stream);

@@ -212,6 +212,26 @@ int dsv4_moe_forward(const moe_weights* w, const uint16_t* w_router, const uint1
                      int32_t k, const int32_t* routing_ids, const float* routing_w, void* out,
                      int32_t out_dtype, void* ws, size_t ws_bytes, void* stream);
 
+/* The whole layer as dsv4_moe_forward, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): no workspace argument, no allocation of
+ * any kind.  The workspace is a file-scope device array of the library,
+ * MOE_NOALLOC_SCRATCH_BYTES bytes on each GPU it runs on, held until the
+ * process ends; its device address is looked up on the first call on a
+ * device (that device current), and its control block is then cleared by a
+ * fill kernel enqueued on `stream`.  A call whose workspace need
+ * (moe_workspace_bytes(w, T, k)) exceeds the array returns MOE_ENOTSUP with
+ * nothing enqueued -- about 100 tokens at hidden 4096, intermediate 2048,
+ * top-6.  Every call on one GPU shares that array: two calls in flight at
+ * once on one GPU (different streams, or different threads) race and give
+ * wrong results.  Results equal dsv4_moe_forward's bit for bit (same
+ * kernels).  Its status word cannot be read (moe_device_status needs a
+ * workspace); bad expert ids are still skipped. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int dsv4_moe_forward_noalloc(const moe_weights* w, const uint16_t* w_router, const uint16_t* x,
+                             int32_t T, int32_t k, const int32_t* routing_ids,
+                             const float* routing_w, void* out, int32_t out_dtype, void* stream);
+
 /* A static string naming a status code. */
 const char* moe_status_string(int status);
 

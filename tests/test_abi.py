@@ -209,3 +209,21 @@ def test_debug_h_sink_arguments():
     assert L.moe_debug_store_h(0x100000, 16) == moe.MOE_OK
     assert L.moe_debug_store_h(None, 0) == moe.MOE_OK
 
+
+def test_noalloc_forward_checks_arguments_and_size_on_host():
+    """The allocation-free forward validates like dsv4_moe_forward and
+    refuses a call whose workspace need exceeds its static array, before
+    touching a device."""
+    p = 0x100000
+    w = _w(ptr=p)
+    wb = ctypes.byref(w)
+    L = moe._lib
+    f = L.dsv4_moe_forward_noalloc
+    assert moe.moe_workspace_bytes(w, 4096, 6) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert f(wb, p, p, 4096, 6, None, None, p, moe.MOE_DT_F32, None) == moe.MOE_ENOTSUP
+    assert f(wb, p, p, 0, 6, None, None, p, moe.MOE_DT_F32, None) == moe.MOE_OK
+    assert f(wb, p, p, 1, 6, None, None, None, moe.MOE_DT_F32, None) == moe.MOE_EINVAL
+    assert f(wb, p, p, 1, 6, None, None, p, 7, None) == moe.MOE_EINVAL
+    assert f(wb, p, p, 1, 6, p, None, p, moe.MOE_DT_F32, None) == moe.MOE_EINVAL
+    assert f(wb, p, p + 2, 1, 6, None, None, p, moe.MOE_DT_F32, None) == moe.MOE_EALIGN
+    assert f(wb, p, p, 1, 17, None, None, p, moe.MOE_DT_F32, None) == moe.MOE_ENOTSUP
