@@ -42,13 +42,13 @@ METRIC = ("MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA TFLOPS (prefil
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, published (FP8 x FP4 runs at this rate)
 PROFILES = os.path.join(ROOT, "profiles")
-DOMINANT = {"gemv": "gemv_gate_up_fp4_kernel", "gemm": "gemm_kernel_gate_up"}
+DOMINANT = {"gemv": "gemv_gate_up_kernel", "gemm": "gemm_kernel_gate_up"}
 
 
 def is_dominant(kernel_name, path):
     """Does a profiler kernel name belong to the path's dominant kernel?"""
     if path == "gemv":
-        return "gemv_gate_up_fp4_kernel" in kernel_name
+        return "gemv_gate_up_kernel" in kernel_name
     # gemm_kernel<FMT, GU, TM>: the gate+up instances
     return "gemm_kernel<" in kernel_name and ", true," in kernel_name
 
@@ -148,7 +148,7 @@ class Hip:
 # --------------------------------------------------------------------------
 
 class Bench:
-    def __init__(self, wl_name, copies, n_tokens_pool):
+    def __init__(self, wl_name, copies, n_tokens_pool, over=None):
         import numpy as np
         import torch
 
@@ -156,13 +156,12 @@ class Bench:
         import synth
 
         self.torch, self.moe, self.np = torch, moe, np
-        over = {}
-        if wl_name == "decode_t1":
-            over = dict(T=n_tokens_pool)        # a pool of seeded tokens, one per step
-        L = synth.make_layer(wl_name, **over)
-        self.layer = L
-        self.wl = synth.WORKLOADS[wl_name]
+        import dataclasses
+        self.wl = dataclasses.replace(synth.WORKLOADS[wl_name], **(over or {}))
         wl = self.wl
+        self.pool = wl.T == 1                    # one token per step, from a pool of seeded tokens
+        L = synth.make_layer(wl, **(dict(T=n_tokens_pool) if self.pool else {}))
+        self.layer = L
         dev = "cuda:0"
         self.stream = torch.cuda.Stream()
         self.sp = self.stream.cuda_stream
@@ -198,10 +197,13 @@ class Bench:
             self.y = torch.empty((R, H), dtype=f32, device=dev)
             self.out = torch.empty((T, H), dtype=torch.uint16, device=dev)
         torch.cuda.synchronize()
-        self.path = "gemv" if (wl.fmt == "fp4" and T == 1 and k + 1 <= 8) else "gemm"
+        # the expert path the library takes for this shape: only the VALU
+        # GEMV path keeps an fp32 h in the workspace
+        h, _, _ = moe.moe_debug_intermediates(self.w[0], T, k, self.ws, self.ws_bytes)
+        self.path = "gemv" if h is not None else "gemm"
 
     def x_of(self, step):
-        if self.wl.name == "decode_t1":
+        if self.pool:
             t = step % self.x_all.shape[0]
             return self.x_all[t:t + 1]
         return self.x_all
@@ -247,16 +249,19 @@ def time_kernel(B, which, n_ev):
         float(np.percentile(ms, 90)) * 1e-3
 
 
-def measure(wl_name, steps, warmup, copies=0, graph_steps=0, hip=None):
+def measure(wl_name, steps, warmup, copies=0, graph_steps=0, hip=None, over=None):
     """Time `steps` whole-layer steps of a workload (graph replays) and its
-    gate+up and down kernels; returns the figures as a dict."""
+    gate+up and down kernels; returns the figures as a dict.  `over` changes
+    the workload's T or weight format (the small-batch sweep)."""
+    import dataclasses
+
     import numpy as np
     import torch
 
     import synth
-    wl = synth.WORKLOADS[wl_name]
-    copies = copies or (8 if wl.name == "decode_t1" else 2 if wl.T <= 64 else 1)
-    B = Bench(wl.name, copies, 64)
+    wl = dataclasses.replace(synth.WORKLOADS[wl_name], **(over or {}))
+    copies = copies or (8 if wl.T == 1 else 2 if wl.T <= 64 else 1)
+    B = Bench(wl_name, copies, 64, over)
     B.hip = hip or Hip()
     per_graph = graph_steps or (64 if wl.T == 1 else 8 if wl.T <= 64 else 1)
     per_graph = max(1, min(per_graph, steps))
@@ -378,6 +383,25 @@ def stream_ceiling(hip):
     return out
 
 
+def sweep(hip):
+    """Single-token decode shapes (hidden 4096, intermediate 2048, 256
+    experts top-6 + shared, router on x) at T = 1 .. 256 tokens, FP4 and FP8
+    weights: whole-step time, tokens/s, which expert path ran (VALU GEMV or
+    MFMA grouped GEMM) and its gate+up / down kernel times."""
+    out = {}
+    for fmt in ("fp4", "fp8"):
+        out[fmt] = {}
+        for T in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+            print(f"# sweep {fmt} T={T}", file=sys.stderr, flush=True)
+            r = measure("decode_t1", 64 if T <= 32 else 16, 8, hip=hip,
+                        over=dict(T=T, fmt=fmt))
+            out[fmt][T] = dict(ms_per_step=r["ms_per_step"], tokens_per_s=r["tokens_per_s"],
+                               path=r["path"], gate_up_us=r["roofline"]["kernel_avg_us"],
+                               down_us=r["down_kernel_avg_us"],
+                               gate_up_hbm_frac=r["roofline"]["hbm_frac"])
+    return out
+
+
 SUB_WORKLOADS = (("tiny_t8", 256, 32), ("verify_t32", 64, 8),
                  ("prefill_fp4_t4096", 10, 3), ("prefill_fp8_t8192", 10, 3))
 
@@ -416,6 +440,7 @@ def run(args):
             print(f"# sub-workload {name}", file=sys.stderr, flush=True)
             subs[name] = measure(name, st, wu, hip=hip)
         line["workloads"] = subs
+        line["small_batch_sweep"] = sweep(hip)
     line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(wl, args)
     print(json.dumps(line), flush=True)
 
@@ -552,6 +577,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0)
     ap.add_argument("--graph-steps", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep-only", action="store_true",
+                    help="run only the small-batch sweep (T = 1 .. 256, FP4 and FP8)")
     ap.add_argument("--no-sub", action="store_true",
                     help="time only --workload (no read ceiling, no other workloads)")
     ap.add_argument("--calib-mib", type=int, default=0,
@@ -562,6 +589,10 @@ def main():
     args = ap.parse_args()
     if args.summarize:
         return summarize(args)
+    if args.sweep_only:
+        import torch  # noqa: F401
+        print(json.dumps({"small_batch_sweep": sweep(Hip())}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
               "(the layer is not sharded across GPUs here).", file=sys.stderr)

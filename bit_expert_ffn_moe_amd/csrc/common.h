@@ -286,8 +286,8 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 struct WsCtl {
   uint32_t status;
   uint32_t pad[63];
-  // one-token GEMV path: h slots [row 8][4096] (publish_h)
-  uint64_t h_slots[8 * 4096];
+  // VALU GEMV path: h slots [row 32][4096] (publish_h)
+  uint64_t h_slots[32 * 4096];
   // small-T router: group sums [H/256 <= 32][T <= 4][E <= 256]
   uint64_t route_slots[32 * 4 * 256];
 };

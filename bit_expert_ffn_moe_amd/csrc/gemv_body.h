@@ -11,6 +11,7 @@
 // and up share one quantised input).
 #pragma once
 #include "common.h"
+#include "kernels.h"
 
 namespace bef {
 
@@ -165,6 +166,98 @@ __device__ __forceinline__ float gate_up_rows(const GUWeights& w, int g, int n0,
   return silu_mul_accurate(tot, up);   // valid in h_lane() lanes
 }
 
+// FP8 weights (fp8_gemm at decode: tcti.cn post, section "补齐软件栈缺失"):
+// codes [E+1][I][H] u8 and one fp32 scale per 128x128 block
+// [E+1][I/128][H/128].  A 32-element chunk of a row is 32 bytes (two 16-byte
+// loads); codes go to fp16 pairwise (exact) and into v_dot2_f32_f16 with the
+// activation pairs; the block scale of rows n0..n0+3 (one 128-row block, n0
+// a multiple of 4) and the chunk's 128 columns is folded into the
+// activation scale, once per chunk.
+struct GUWeights8 {
+  const uint8_t *gq, *uq;
+  const float *gs, *us;
+  int E, H, I;
+};
+
+__device__ __forceinline__ float dot32_fp8(const uint4 w0, const uint4 w1, const Act16& a0,
+                                           const Act16& a1) {
+  Act16 b0, b1;
+  e4m3x16_to_h2(w0, b0);
+  e4m3x16_to_h2(w1, b1);
+  float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    acc0 = dot2(b0.p[i], a0.p[i], acc0);
+    acc1 = dot2(b1.p[i], a1.p[i], acc1);
+  }
+  return acc0 + acc1;
+}
+
+template <int NB>
+__device__ __forceinline__ float gate_up_rows_fp8(const GUWeights8& w, int g, int n0, int lane,
+                                                  const uint4 (&aq)[NB][2],
+                                                  const float (&xs_raw)[NB]) {
+  constexpr int RUN = kGuRun, DEPTH = 2;
+  const int H = w.H, I = w.I;
+  const int nch = H >> 5;
+  const size_t rowq = (size_t)H;
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  int co[NB];
+  float wsg[NB], wsu[NB];
+  const size_t sb = ((size_t)g * (I >> 7) + (n0 >> 7)) * (size_t)(H >> 7);
+#pragma unroll
+  for (int c = 0; c < NB; ++c) {
+    const int ch = min(ln + 64 * c, nch - 1);
+    co[c] = 32 * ch;
+    wsg[c] = w.gs[sb + (ch >> 2)];
+    wsu[c] = w.us[sb + (ch >> 2)];
+  }
+  const uint8_t* gqb = w.gq + ((size_t)g * I + n0) * rowq;
+  const uint8_t* uqb = w.uq + ((size_t)g * I + n0) * rowq;
+  uint4 pg[DEPTH][NB][2], pu[DEPTH][NB][2];
+  int dep = 0;
+#define BEF_GU8_LOAD(SLOT, ROW)                                                           \
+  _Pragma("unroll") for (int c = 0; c < NB; ++c) {                                        \
+    pg[SLOT][c][0] = *reinterpret_cast<const uint4*>(gqb + (ROW) * rowq + co[c] + dep);   \
+    pg[SLOT][c][1] = *reinterpret_cast<const uint4*>(gqb + (ROW) * rowq + co[c] + 16 + dep); \
+    pu[SLOT][c][0] = *reinterpret_cast<const uint4*>(uqb + (ROW) * rowq + co[c] + dep);   \
+    pu[SLOT][c][1] = *reinterpret_cast<const uint4*>(uqb + (ROW) * rowq + co[c] + 16 + dep); \
+  }
+  BEF_GU8_LOAD(0, 0)
+  Act16 a0[NB], a1[NB];
+  float sg[NB], su[NB];
+#pragma unroll
+  for (int c = 0; c < NB; ++c) {
+    e4m3x16_to_h2(aq[c][0], a0[c]);
+    e4m3x16_to_h2(aq[c][1], a1[c]);
+    const float xsc = (lane + 64 * c < nch) ? xs_raw[c] : 0.0f;
+    sg[c] = xsc * wsg[c];
+    su[c] = xsc * wsu[c];
+  }
+  float part[2 * RUN];
+#pragma unroll
+  for (int i = 0; i < RUN; ++i) {
+    if (i + 1 < RUN) {
+      BEF_GU8_LOAD((i + 1) % DEPTH, i + 1)
+    }
+    const int sl = i % DEPTH;
+    float ag = 0.0f, au = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      ag += dot32_fp8(pg[sl][c][0], pg[sl][c][1], a0[c], a1[c]) * sg[c];
+      au += dot32_fp8(pu[sl][c][0], pu[sl][c][1], a0[c], a1[c]) * su[c];
+    }
+    part[i] = ag;
+    part[RUN + i] = au;
+    asm volatile("" : "+v"(dep) : "v"(ag), "v"(au));
+  }
+#undef BEF_GU8_LOAD
+  const float tot = butterfly8(part);
+  const float up = xchg32(tot);
+  return silu_mul_accurate(tot, up);
+}
+
 // The lanes that hold a finished h value after gate_up_rows (bit 5 = 0 and
 // bits 2..0 = 0: one per row), and the row n0 + h_row(lane) they hold.
 __device__ __forceinline__ bool h_lane(int lane) { return (lane & 39) == 0; }
@@ -189,7 +282,7 @@ __device__ __forceinline__ int h_row(int lane) { return (lane >> 3) & 3; }
 // write could outlive the reset, so a workspace that reported one must be
 // initialised again.
 constexpr int kHSlotStride = 4096;   // largest I on the one-token path
-constexpr int kHSlotRows = 8;
+constexpr int kHSlotRows = kHSlotRowsHost;   // rows T*k + T of the VALU path
 constexpr uint32_t kSpinLimit = 1u << 16;
 constexpr uint32_t kStatusSyncTimeout = 2u;  // MOE_STATUS_SYNC_TIMEOUT
 constexpr uint64_t kSlotValid = 1ull << 32;

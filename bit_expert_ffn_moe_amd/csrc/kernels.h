@@ -13,6 +13,8 @@ constexpr int kRouteSplitT = 256;         // router: experts also split in quart
 constexpr int kPermuteSmallPairs = 2048;  // permute: single block up to this many pairs
 constexpr int kPermuteTokBlock = 256;     // permute: tokens per block above that
 constexpr int kGemvMaxRows = 8;           // VALU GEMV path: rows (k + 1) per token
+constexpr int kGemvMaxT = 4;              // VALU GEMV path: at most this many tokens
+constexpr int kHSlotRowsHost = 32;        // VALU GEMV path: rows T*(k+1) (h exchange slots)
 constexpr uint32_t MOE_STATUS_BAD_EXPERT_ID_DEV = 1u;
 
 // Optional start/stop events of one kernel's launches (debug timing; set by
@@ -38,7 +40,9 @@ struct GemvArgs {
   float* hs_ws;
   uint64_t* h_slots;    // tagged slots of the h exchange (zero between launches)
   uint32_t* status;
-  int n_rows;           // down with an active list: T*k + T rows, the last the shared one
+  int n_rows;           // down with an active list: T*k + T rows, the last T the shared ones
+  int fmt;              // 1: FP4 weights, 2: FP8
+  int T;                // tokens
 };
 
 struct GemmArgs {
@@ -78,7 +82,9 @@ struct FrontArgs {
   int4* active;           // routed groups {group, first row, end row}, -1 padded
   int n_active_slots;
   // shared expert's gate+up rows run in the same kernel when sh_h is set
+  // (fmt 1: FP4 weights, 2: FP8)
   const uint8_t *sh_gq, *sh_gs, *sh_uq, *sh_us;
+  int fmt;
   int I;
   float* sh_h;
   uint8_t* sh_hq;         // requantised h (rows of the shared expert)

@@ -67,9 +67,15 @@ struct Layout {
   size_t end_permute, end_route, end_ffn;
 };
 
+// The VALU GEMV path (weights streamed once per token row from registers,
+// no MFMA tile to fill) for a few tokens; the grouped GEMM otherwise.  The
+// crossover in T per format is the measured one (small-batch sweep of the
+// benchmark at hidden 4096, intermediate 2048, 256 experts top-6).
+constexpr int kGemvCrossT[3] = {0, 4, 4};  // by format: FP4, FP8
+
 bool gemv_path(int fmt, int T, int k, int H, int I) {
-  return fmt == MOE_W_FP4_E2M1_UE8M0_K32 && T == 1 && k + 1 <= kGemvMaxRows && H <= 8192 &&
-         I <= 4096;
+  return T >= 1 && T <= kGemvMaxT && T <= kGemvCrossT[fmt == MOE_W_FP8_E4M3_F32_B128 ? 2 : 1] &&
+         k + 1 <= kGemvMaxRows && T * (k + 1) <= kHSlotRowsHost && H <= 8192 && I <= 4096;
 }
 
 Layout layout_for(int E, int H, int I, int T, int k, bool with_h) {
@@ -214,6 +220,7 @@ GemvArgs gemv_args(const moe_weights* w, int T, int k, const Layout& L, void* ws
   a.dq = (const uint8_t*)w->down_q;
   a.ds = (const uint8_t*)w->down_s;
   a.E = w->n_experts, a.H = w->hidden, a.I = w->inter, a.k = k;
+  a.fmt = w->format, a.T = T;
   a.n_slots = (T * k < w->n_experts ? T * k : w->n_experts) + 1;
   a.h = at<float>(ws, L.h);
   a.hq_ws = at<uint8_t>(ws, L.hq);
@@ -485,6 +492,7 @@ int enqueue_forward(const moe_weights* w, const uint16_t* w_router, const uint16
       // one token on the VALU path: the front kernel also quantises x, runs
       // the shared expert's gate+up (its waves quantise x themselves, same
       // rule) and lists the routed groups for the gate+up kernel
+      fa.fmt = w->format;
       fa.sh_gq = (const uint8_t*)w->gate_q;  // the kernel reads group E (the shared expert)
       fa.sh_uq = (const uint8_t*)w->up_q;
       fa.sh_gs = (const uint8_t*)w->gate_s;

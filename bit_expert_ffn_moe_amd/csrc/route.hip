@@ -113,7 +113,7 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, in
 //    asked, writes the permutation tables (the single-block form of S4) and
 //    the list of active routed groups.
 // ---------------------------------------------------------------------------
-template <int NB>
+template <int NB, int FMT>
 __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
   const int nc = a.H / 64;                 // 64-row chunks
   const int ng = (nc + 3) / 4;             // groups of 4 chunks
@@ -128,13 +128,20 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
       const int t = b / bpg, lane = tid & 63;
       const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
       const int n0b = (b - t * bpg) * 4 * kGuRun;
-      const GUWeights w = {a.sh_gq, a.sh_gs, a.sh_uq, a.sh_us, E, H, a.I};
       const HExchange hx = {a.h_slots, a.sh_h, a.sh_hq, a.sh_hs, a.status};
       uint4 aq[NB][2];
       float xsc[NB];
       quant_act_codes<NB>(a.x + (size_t)t * H, H, lane, aq, xsc);
       const int n0 = n0b + wv * kGuRun;
-      const float hv = gate_up_rows<NB>(w, E, n0, lane, aq, xsc);
+      float hv;
+      if (FMT == 1) {
+        const GUWeights w = {a.sh_gq, a.sh_gs, a.sh_uq, a.sh_us, E, H, a.I};
+        hv = gate_up_rows<NB>(w, E, n0, lane, aq, xsc);
+      } else {
+        const GUWeights8 w = {a.sh_gq, a.sh_uq, reinterpret_cast<const float*>(a.sh_gs),
+                              reinterpret_cast<const float*>(a.sh_us), E, H, a.I};
+        hv = gate_up_rows_fp8<NB>(w, E, n0, lane, aq, xsc);
+      }
       publish_h(hx, hv, T * k + t, a.I, n0, n0b, tid, lane);
       return;
     }
@@ -617,12 +624,17 @@ hipError_t launch_route_front(const FrontArgs& a, hipStream_t st) {
   const int nr = (a.H / 64 + 3) / 4 * ((a.E + 63) / 64);
   const dim3 grid(nr + nsh + nq);
   const int nb = (a.H / 32 + 63) / 64;
-  if (nb <= 1)
-    route_front_kernel<1><<<grid, dim3(256), 0, st>>>(a);
-  else if (nb <= 2)
-    route_front_kernel<2><<<grid, dim3(256), 0, st>>>(a);
-  else
-    route_front_kernel<4><<<grid, dim3(256), 0, st>>>(a);
+  const bool f8 = a.sh_h && a.fmt == 2;  // the shared expert's rows are FP8
+  if (nb <= 1) {
+    if (f8) route_front_kernel<1, 2><<<grid, dim3(256), 0, st>>>(a);
+    else route_front_kernel<1, 1><<<grid, dim3(256), 0, st>>>(a);
+  } else if (nb <= 2) {
+    if (f8) route_front_kernel<2, 2><<<grid, dim3(256), 0, st>>>(a);
+    else route_front_kernel<2, 1><<<grid, dim3(256), 0, st>>>(a);
+  } else {
+    if (f8) route_front_kernel<4, 2><<<grid, dim3(256), 0, st>>>(a);
+    else route_front_kernel<4, 1><<<grid, dim3(256), 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -166,8 +166,10 @@ int moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_
  *   xq [T][H] u8, xs [T][H/128] f32 (act_quant_fp8 of x)
  *   offsets, row_token as produced by moe_permute
  *   y_rows [T*k+T][H] f32 out (rows of dropped pairs are left untouched)
- * T <= 1 with k+1 <= 8 and the FP4 format runs the VALU GEMV kernels; any
- * other shape runs the MFMA grouped GEMM kernels. */
+ * A few tokens -- 1 <= T <= 4 with k+1 <= 8, T*(k+1) <= 32, H <= 8192 and
+ * I <= 4096, either weight format -- run the VALU GEMV kernels (weights
+ * streamed from HBM into registers, no matrix-core tile to fill); any other
+ * shape runs the MFMA grouped GEMM kernels. */
 int moe_expert_ffn(const moe_weights* w, const uint8_t* xq, const float* xs, int32_t T, int32_t k,
                    const int32_t* offsets, const int32_t* row_token, float* y_rows, void* ws,
                    size_t ws_bytes, void* stream);

@@ -21,7 +21,8 @@ from gpu_util import DevLayer, to_host  # noqa: E402
 
 @pytest.mark.parametrize("over", [
     dict(T=1),               # one token: front kernel + VALU GEMV with the h exchange
-    dict(T=3, fmt="fp8"),    # front kernel + grouped GEMM
+    dict(T=3, fmt="fp8"),    # front kernel + VALU GEMV (FP8), 3 tokens
+    dict(T=6),               # mid-size router with act_quant, permute, grouped GEMM, combine
     dict(T=40),              # mid-size router with act_quant, permute, grouped GEMM, combine
 ])
 def test_graph_replays_equal_the_eager_forward(over):

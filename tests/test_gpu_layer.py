@@ -85,6 +85,7 @@ def _run(name, sample=None, threads=0, **over):
                                   dict(T=5), dict(T=130, routing="zipf", zipf_s=1.0),
                                   dict(E=1, k=1, T=9), dict(E=3, k=3, T=17),
                                   dict(T=3, H=384), dict(T=3, H=384, fmt="fp8"),
+                                  dict(T=5, H=384), dict(T=5, H=384, fmt="fp8"),
                                   dict(T=1, H=384), dict(T=40, H=640, fmt="fp8")])
 def test_tiny_layer(over):
     _run("tiny_t8", **over)
@@ -158,46 +159,54 @@ def test_decode_t1_repeated_expert_ids():
 
 
 @pytest.mark.parametrize("name,over", [("decode_t1", dict(T=1)), ("tiny_t8", dict(T=1)),
-                                       ("decode_t1", dict(T=1, I=1024, seed=2002))])
+                                       ("decode_t1", dict(T=1, I=1024, seed=2002)),
+                                       ("decode_t1", dict(T=4)),
+                                       ("decode_t1", dict(T=3, seed=2003)),
+                                       ("decode_t1", dict(T=1, fmt="fp8", E=16)),
+                                       ("decode_t1", dict(T=2, fmt="fp8", E=16)),
+                                       ("tiny_t8", dict(T=4, fmt="fp8"))])
 def test_decode_layer_matches_stagewise_kernels(name, over):
-    """The router's one-token path (front kernel with the shared expert's
-    gate+up, gate+up kernel, down+combine kernel) against the oracle's h rows
-    and the act_quant of its own h, and bit for bit against the separate
-    gate+up and down+combine calls on the same routing (same arithmetic in
-    the same order); three calls in a row reuse the workspace."""
+    """The router's small-T VALU path (front kernel with the shared expert's
+    gate+up, gate+up kernel, down+combine kernel; FP4 or FP8 weights, 1 to 4
+    tokens) against the oracle's h rows and the act_quant of its own h, and
+    bit for bit against the separate gate+up and down+combine calls on the
+    same routing (same arithmetic in the same order); three calls in a row
+    reuse the workspace."""
     _print("decode vs stagewise", name, over)
     L = synth.make_layer(name, **over)
     wl = L.wl
-    k, E, H, I = wl.k, wl.E, wl.H, wl.I
-    R = k + 1
+    T, k, E, H, I = wl.T, wl.k, wl.E, wl.H, wl.I
+    R = T * k + T
     D = DevLayer(L)
     W = Weights.from_layer(L)
     # the separate kernels, on a workspace of their own; the GPU's selection
     # (a valid top-k of the oracle's logits) is the routing of the oracle's rows
     ws2 = torch.zeros(D.ws_bytes, dtype=torch.uint8, device="cuda")
     moe.moe_workspace_init(ws2, D.ws_bytes)
-    gids = torch.empty((1, k), dtype=torch.int32, device="cuda")
-    gw = torch.empty((1, k), dtype=torch.float32, device="cuda")
-    moe.moe_route(D.x, D.wr, 1, H, E, k, gids, gw, ws2, D.ws_bytes)
+    gids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_route(D.x, D.wr, T, H, E, k, gids, gw, ws2, D.ws_bytes)
     ids, tw = to_host(gids), to_host(gw)
     check_gpu_selection(orc, L.x, L.wr, k, ids, tw)
     xq, xs = orc.act_quant(L.x)
     offsets, row_token, row_of, _ = orc.permute(ids, E)
     grp = np.searchsorted(offsets, np.arange(R), side="right") - 1
-    rows_ref = [orc.expert_row(W, int(grp[r]), xq[0], xs[0]) for r in range(R)]
+    rows_ref = [orc.expert_row(W, int(grp[r]), xq[row_token[r]], xs[row_token[r]])
+                for r in range(R)]
     ref = routed_reference(orc, W, L, ids, tw)
-    moe.moe_expert_gate_up(D.w, to_dev(xq), to_dev(xs), 1, k, to_dev(offsets), to_dev(row_token),
+    moe.moe_expert_gate_up(D.w, to_dev(xq), to_dev(xs), T, k, to_dev(offsets), to_dev(row_token),
                            ws2, D.ws_bytes)
-    out2 = torch.empty((1, H), dtype=torch.float32, device="cuda")
-    moe.moe_expert_down(D.w, 1, k, to_dev(offsets), to_dev(row_of), gw, None, out2,
+    out2 = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    moe.moe_expert_down(D.w, T, k, to_dev(offsets), to_dev(row_of), gw, None, out2,
                         moe.MOE_DT_F32, ws2, D.ws_bytes)
     o2 = to_host(out2)
     for call in range(3):
         out = to_host(D.forward())
         _check(out, ref, f"decode {name} {over} call {call}")
         assert np.array_equal(out, o2), call
-        assert np.array_equal(gpu_routing(D, 1)[0], ids), call
-        hp, hqp, hsp = moe.moe_debug_intermediates(D.w, 1, k, D.ws, D.ws_bytes)
+        assert np.array_equal(gpu_routing(D, T)[0], ids), call
+        hp, hqp, hsp = moe.moe_debug_intermediates(D.w, T, k, D.ws, D.ws_bytes)
+        assert hp is not None          # the VALU path ran
         h = d2h(hp, (R, I), np.float32)
         hq = d2h(hqp, (R, I), np.uint8)
         hs = d2h(hsp, (R, I // 128), np.float32)
@@ -207,6 +216,18 @@ def test_decode_layer_matches_stagewise_kernels(name, over):
             assert np.array_equal(hq[r], q2[0]) and np.array_equal(hs[r], s2[0]), (call, r)
     assert moe.moe_device_status(D.ws) == 0
     assert moe.moe_device_status(ws2) == 0
+
+
+@pytest.mark.parametrize("fmt,T", [("fp4", 2), ("fp4", 4), ("fp8", 4)])
+def test_small_batch_drawn_routing(fmt, T):
+    """2 to 4 tokens with drawn routing (Zipf s=1.0: tokens share experts,
+    so groups hold several rows) through the VALU path at decode shapes."""
+    over = dict(T=T, routing="zipf", zipf_s=1.0, fmt=fmt)
+    if fmt == "fp8":
+        over["E"] = 16
+    L, D, out, ref, _ = _run("decode_t1", **over)
+    hp, _, _ = moe.moe_debug_intermediates(D.w, T, L.wl.k, D.ws, D.ws_bytes)
+    assert hp is not None
 
 
 def test_verify_t32_full_shapes():
