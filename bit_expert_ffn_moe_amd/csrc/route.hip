@@ -327,25 +327,34 @@ struct ActQuantArgs {
 };
 
 // ---------------------------------------------------------------------------
-// T > 4, in two kernels.  route_group_kernel: block (g, tile) owns tokens
-// 32 tile .. +31, all E (<= 256) experts and rows 256 g .. 256 g + 255 (chunks
-// 4g .. 4g+3), 4 waves.  Per 64-row chunk the router rows go to LDS
-// converted to fp32 (each element once per block) and x as fp32; thread
-// (ty, tx) accumulates tokens 4ty..4ty+3 x experts 8tx..8tx+7 in the fixed
-// order (chunk chains from +0 in ascending h, the group's chunks in
-// ascending order), reading its 8 experts with two 16-byte LDS reads and x
-// four rows at a time, while the next chunk's rows load into registers.  It
-// writes the group sums G[g][t][e].  route_reduce_kernel: a block per 4
-// tokens adds the group sums in ascending group order (thread e owns expert
-// e) and one wave per token runs the top-k.  Splitting over H keeps the
-// GPU busy at moderate T (32 tokens: 16 blocks instead of one).
+// T > 4, in two kernels.  route_group_kernel (T >= kRouteSplitT): block
+// (g, tile) owns tokens 32 tile .. +31, all E (<= 256) experts and rows
+// 256 g .. 256 g + 255 (chunks 4g .. 4g+3), 4 waves.  Per 64-row chunk the
+// block stages x and the router rows in LDS as bf16 pairs of consecutive h
+// (x: the pair as it lies in memory; router: rows h and h+1 of an expert
+// packed into one dword), and thread (ty, tx) accumulates tokens
+// 4ty..4ty+3 x experts 8tx..8tx+7 with v_dot2_f32_bf16 -- two exact
+// products per instruction, in ascending h from +0 per chunk, the group's
+// chunks in ascending order -- reading its 8 experts' pairs with two
+// 16-byte LDS reads and x four pairs at a time, while the next chunk's rows
+// load into registers.  It writes the group sums G[g][t][e].
+// route_reduce_kernel: a block per 4 tokens adds the group sums in
+// ascending group order (thread e owns expert e) and one wave per token
+// runs the top-k.  Splitting over H keeps the GPU busy at moderate T.
 // ---------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 __global__ __launch_bounds__(256) void route_group_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ wr, int T,
                                                           int H, int E,
                                                           float* __restrict__ gsum) {
-  __shared__ __align__(16) float sx[32][68];    // [token][h of the chunk], padded rows
-  __shared__ __align__(16) float sw[64][256];   // [h of the chunk][expert]
+  __shared__ __align__(16) uint32_t sx2[32][36];   // [token][h pair of the chunk], padded rows
+  __shared__ __align__(16) uint32_t sw2[32][256];  // [h pair of the chunk][expert]
   const int g = blockIdx.x, t0 = blockIdx.y * 32;
   const int tid = threadIdx.x;
   const int ty = tid >> 5, tx = tid & 31;
@@ -353,46 +362,44 @@ __global__ __launch_bounds__(256) void route_group_kernel(const uint16_t* __rest
   const int c0 = 4 * g, c1 = min(4 * g + 4, nc);
   float grp[4][8];
   // this thread's share of a chunk: x row tid/8, 8 bf16 at (tid%8)*8; router
-  // 16-byte pieces q = tid + 256 i: row q/32, experts (q%32)*8 .. +7
+  // pieces q = tid + 256 i (i < 4): rows 2 (q/32) and 2 (q/32) + 1, experts
+  // (q%32)*8 .. +7
   const int xr = tid >> 3, xc = (tid & 7) * 8;
   const bool xin = t0 + xr < T;
   uint4 px;
-  uint4 pw[8];
+  uint4 pw[4][2];
+  auto load_row8 = [&](int h, int e8) -> uint4 {
+    const uint16_t* src = wr + (size_t)h * E + e8;
+    if (E == 256) return *reinterpret_cast<const uint4*>(src);
+    uint16_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = (e8 + u < E) ? src[u] : (uint16_t)0;
+    return make_uint4(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
+                      v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16));
+  };
   auto load_chunk = [&](int c) {
     px = xin ? *reinterpret_cast<const uint4*>(x + (size_t)(t0 + xr) * H + 64 * c + xc)
              : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = tid + 256 * i, h = q >> 5, e8 = (q & 31) * 8;
-      const uint16_t* src = wr + (size_t)(64 * c + h) * E + e8;
-      if (E == 256) {
-        pw[i] = *reinterpret_cast<const uint4*>(src);
-      } else {
-        uint16_t v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = (e8 + u < E) ? src[u] : (uint16_t)0;
-        pw[i] = make_uint4(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
-                           v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16));
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i, hp = q >> 5, e8 = (q & 31) * 8;
+      pw[i][0] = load_row8(64 * c + 2 * hp, e8);
+      pw[i][1] = load_row8(64 * c + 2 * hp + 1, e8);
     }
   };
+  // (lo halves of a and b) and (hi halves of a and b) as two bf16 pairs
+  auto lo2 = [](uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); };
+  auto hi2 = [](uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); };
   auto store_chunk = [&]() {
-    *reinterpret_cast<float4*>(&sx[xr][xc]) =
-        make_float4(bf16_to_f32(px.x & 0xffffu), bf16_to_f32(px.x >> 16),
-                    bf16_to_f32(px.y & 0xffffu), bf16_to_f32(px.y >> 16));
-    *reinterpret_cast<float4*>(&sx[xr][xc + 4]) =
-        make_float4(bf16_to_f32(px.z & 0xffffu), bf16_to_f32(px.z >> 16),
-                    bf16_to_f32(px.w & 0xffffu), bf16_to_f32(px.w >> 16));
+    *reinterpret_cast<uint4*>(&sx2[xr][xc >> 1]) = px;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = tid + 256 * i, h = q >> 5, e8 = (q & 31) * 8;
-      const uint4 r = pw[i];
-      *reinterpret_cast<float4*>(&sw[h][e8]) =
-          make_float4(bf16_to_f32(r.x & 0xffffu), bf16_to_f32(r.x >> 16),
-                      bf16_to_f32(r.y & 0xffffu), bf16_to_f32(r.y >> 16));
-      *reinterpret_cast<float4*>(&sw[h][e8 + 4]) =
-          make_float4(bf16_to_f32(r.z & 0xffffu), bf16_to_f32(r.z >> 16),
-                      bf16_to_f32(r.w & 0xffffu), bf16_to_f32(r.w >> 16));
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i, hp = q >> 5, e8 = (q & 31) * 8;
+      const uint4 a = pw[i][0], b = pw[i][1];
+      *reinterpret_cast<uint4*>(&sw2[hp][e8]) =
+          make_uint4(lo2(a.x, b.x), hi2(a.x, b.x), lo2(a.y, b.y), hi2(a.y, b.y));
+      *reinterpret_cast<uint4*>(&sw2[hp][e8 + 4]) =
+          make_uint4(lo2(a.z, b.z), hi2(a.z, b.z), lo2(a.w, b.w), hi2(a.w, b.w));
     }
   };
   load_chunk(c0);
@@ -406,20 +413,20 @@ __global__ __launch_bounds__(256) void route_group_kernel(const uint16_t* __rest
 #pragma unroll
       for (int j = 0; j < 8; ++j) p[i][j] = 0.0f;
 #pragma unroll 2
-    for (int h4 = 0; h4 < 64; h4 += 4) {
-      float4 xv[4];
+    for (int hp4 = 0; hp4 < 32; hp4 += 4) {
+      uint4 xv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xv[i] = *reinterpret_cast<const float4*>(&sx[4 * ty + i][h4]);
+      for (int i = 0; i < 4; ++i) xv[i] = *reinterpret_cast<const uint4*>(&sx2[4 * ty + i][hp4]);
 #pragma unroll
       for (int hh = 0; hh < 4; ++hh) {
-        const float4 w0 = *reinterpret_cast<const float4*>(&sw[h4 + hh][8 * tx]);
-        const float4 w1 = *reinterpret_cast<const float4*>(&sw[h4 + hh][8 * tx + 4]);
-        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        const uint4 w0 = *reinterpret_cast<const uint4*>(&sw2[hp4 + hh][8 * tx]);
+        const uint4 w1 = *reinterpret_cast<const uint4*>(&sw2[hp4 + hh][8 * tx + 4]);
+        const uint32_t wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float xs = hh == 0 ? xv[i].x : hh == 1 ? xv[i].y : hh == 2 ? xv[i].z : xv[i].w;
+          const uint32_t xs = hh == 0 ? xv[i].x : hh == 1 ? xv[i].y : hh == 2 ? xv[i].z : xv[i].w;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) p[i][j] = fmaf(xs, wv[j], p[i][j]);
+          for (int j = 0; j < 8; ++j) p[i][j] = dot2_bf16(xs, wv[j], p[i][j]);
         }
       }
     }
