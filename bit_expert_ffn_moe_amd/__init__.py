@@ -51,8 +51,18 @@ class moe_weights(ctypes.Structure):
                 ("down_q", ctypes.c_void_p), ("down_s", ctypes.c_void_p)]
 
 
+class moe_expert_cache(ctypes.Structure):
+    _fields_ = [("n_experts", ctypes.c_int32), ("n_slots", ctypes.c_int32),
+                ("slot_of", ctypes.c_void_p), ("expert_of", ctypes.c_void_p),
+                ("last_use", ctypes.c_void_p), ("calls", ctypes.c_uint64),
+                ("shared_resident", ctypes.c_int32), ("pad_", ctypes.c_int32),
+                ("hits", ctypes.c_uint64), ("misses", ctypes.c_uint64),
+                ("bytes_copied", ctypes.c_uint64)]
+
+
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _W = ctypes.POINTER(moe_weights)
+_C = ctypes.POINTER(moe_expert_cache)
 _sigs = {
     "moe_workspace_bytes": ([_W, _i32, _i32], _sz),
     "moe_workspace_init": ([_vp, _sz, _vp], ctypes.c_int),
@@ -68,6 +78,10 @@ _sigs = {
                          ctypes.c_int),
     "dsv4_moe_forward_noalloc": ([_W, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _i32, _vp],
                                  ctypes.c_int),
+    "moe_host_experts_workspace_bytes": ([_W, _i32, _i32], _sz),
+    "moe_host_experts_scratch_bytes": ([_i32, _i32, _i32], _sz),
+    "moe_forward_host_experts": ([_W, _W, _C, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _sz, _vp, _sz,
+                                  _vp, _vp, _vp], ctypes.c_int),
     "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "moe_device_status": ([_vp, _vp, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int],
                           ctypes.c_int),
@@ -187,6 +201,38 @@ def dsv4_moe_forward_noalloc(w, w_router, x, T, k, routing_ids, routing_w, out, 
                                                 _ptr(routing_ids), _ptr(routing_w), _ptr(out),
                                                 out_dtype, _stream(stream)),
                   "dsv4_moe_forward_noalloc")
+
+
+class ExpertCache:
+    """Host-side LRU state of one layer's expert cache (the moe_expert_cache
+    of include/moe.h) in numpy arrays, in its initial (empty) state."""
+
+    def __init__(self, n_experts: int, n_slots: int):
+        import numpy as np
+        self.slot_of = np.full(n_experts, -1, np.int32)
+        self.expert_of = np.full(n_slots, -1, np.int32)
+        self.last_use = np.zeros(n_slots, np.uint64)
+        self.c = moe_expert_cache(n_experts, n_slots, self.slot_of.ctypes.data,
+                                  self.expert_of.ctypes.data, self.last_use.ctypes.data,
+                                  0, 0, 0, 0, 0, 0)
+
+
+def moe_host_experts_workspace_bytes(host_w, max_tokens, top_k) -> int:
+    return _lib.moe_host_experts_workspace_bytes(ctypes.byref(host_w), max_tokens, top_k)
+
+
+def moe_host_experts_scratch_bytes(n_experts, max_tokens, top_k) -> int:
+    return _lib.moe_host_experts_scratch_bytes(n_experts, max_tokens, top_k)
+
+
+def moe_forward_host_experts(host_w, slot_w, cache, w_router, x, T, k, out, out_dtype, ws,
+                             ws_bytes, host_scratch, host_scratch_bytes, copies_done,
+                             stream=None, copy_stream=None) -> int:
+    c = cache.c if isinstance(cache, ExpertCache) else cache
+    return _check(_lib.moe_forward_host_experts(
+        ctypes.byref(host_w), ctypes.byref(slot_w), ctypes.byref(c), _ptr(w_router), _ptr(x),
+        T, k, _ptr(out), out_dtype, _ptr(ws), ws_bytes, _ptr(host_scratch), host_scratch_bytes,
+        _ptr(copies_done), _stream(stream), _stream(copy_stream)), "moe_forward_host_experts")
 
 
 def moe_device_status(ws, stream=None, clear: bool = False) -> int:

@@ -337,8 +337,8 @@ __device__ __forceinline__ int find_group_item(const int32_t* __restrict__ offse
   int ca = 0, cb = 0;
   if (ga < G) ca = offsets[ga + 1] - offsets[ga];
   if (gb < G) cb = offsets[gb + 1] - offsets[gb];
-  const int ua = (ga < G) ? units_of(ca) : 0;
-  const int ub = (gb < G) ? units_of(cb) : 0;
+  const int ua = (ga < G) ? units_of(ga, ca) : 0;
+  const int ub = (gb < G) ? units_of(gb, cb) : 0;
   if (t == 0) {
     s_tmp[4] = -1;
     s_tmp[5] = 0;

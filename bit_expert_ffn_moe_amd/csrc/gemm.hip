@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
   // m-tiles per group and their exclusive prefix (groups 0..E, E = shared)
   {
     int my_mt = 0;
-    if (tid <= E) {
+    if (tid <= E && (!a.group_mask || a.group_mask[tid])) {
       const int c = a.offsets[tid + 1] - a.offsets[tid];
       my_mt = (c + TM - 1) / TM;
     }

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
     GUWeights w, const uint8_t* __restrict__ xq, const float* __restrict__ xs,
     const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ row_token, const int4* __restrict__ active,
-    HExchange hx) {
+    const uint8_t* __restrict__ group_mask, HExchange hx) {
   __shared__ int stmp[8];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
@@ -50,7 +50,9 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
   } else {
     int unused;
     g = find_group_item(
-        offsets, w.E + 1, slot, [](int c) { return c > 0 ? 1 : 0; }, stmp, &unused);
+        offsets, w.E + 1, slot,
+        [group_mask](int gg, int c) { return (c > 0 && (!group_mask || group_mask[gg])) ? 1 : 0; },
+        stmp, &unused);
     if (g >= 0) r0 = offsets[g], r1 = offsets[g + 1];
   }
   if (g < 0) return;
@@ -98,8 +100,8 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(
     const uint8_t* __restrict__ hq, const float* __restrict__ hs,
     const int32_t* __restrict__ offsets, const int4* __restrict__ active, int n_slots,
     int n_rows, const int32_t* __restrict__ row_of, const float* __restrict__ topk_w, int E,
-    int H, int I, int k, int T, float* __restrict__ y_rows, void* __restrict__ out,
-    int out_bf16) {
+    int H, int I, int k, int T, const uint8_t* __restrict__ group_mask,
+    float* __restrict__ y_rows, void* __restrict__ out, int out_bf16) {
   constexpr int RMAX = kHSlotRows, KMAX = kGemvMaxRows, RUN = 8, DEPTH = 3, NW = 8;
   __shared__ int s_rowexp[RMAX];
   __shared__ float s_y[RMAX][RUN];
@@ -140,6 +142,7 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(
       }
     } else {
       g = s_rowexp[r];
+      if (group_mask && !group_mask[g]) continue;  // a skipped group: row left untouched
     }
     // chunk indices clamped into the row (unconditional loads); a chunk past
     // the end gets scale 0 and adds exactly 0
@@ -253,7 +256,8 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(
     }
   } else {
     for (int i = tid; i < R * RUN; i += 512)
-      y_rows[(size_t)(i / RUN) * H + m0 + (i % RUN)] = s_y[i / RUN][i % RUN];
+      if (active || !group_mask || group_mask[s_rowexp[i / RUN]])
+        y_rows[(size_t)(i / RUN) * H + m0 + (i % RUN)] = s_y[i / RUN][i % RUN];
   }
 }
 
@@ -267,10 +271,11 @@ static hipError_t launch_gate_up_nb(const GemvArgs& a, hipStream_t st) {
   const KernelTimer& tm = g_kernel_timer[MOE_KERNEL_GEMV_GATE_UP];
   if (tm.start)
     hipExtLaunchKernelGGL(gemv_gate_up_kernel<NB, FMT>, grid, dim3(256), 0, st, tm.start,
-                          tm.stop, 0, w, a.xq, a.xs, a.offsets, a.row_token, a.active, hx);
+                          tm.stop, 0, w, a.xq, a.xs, a.offsets, a.row_token, a.active,
+                          a.group_mask, hx);
   else
     gemv_gate_up_kernel<NB, FMT><<<grid, 256, 0, st>>>(w, a.xq, a.xs, a.offsets, a.row_token,
-                                                       a.active, hx);
+                                                       a.active, a.group_mask, hx);
   return hipGetLastError();
 }
 
@@ -283,11 +288,11 @@ static hipError_t launch_down_nb(const GemvArgs& a, hipStream_t st) {
     hipExtLaunchKernelGGL(gemv_down_kernel<NB, COMBINE, FMT>, dim3(a.H / 8), dim3(512), 0, st,
                           tm.start, tm.stop, 0, a.dq, a.ds, a.hq_ws, a.hs_ws, a.offsets,
                           a.active, a.n_slots, a.n_rows, a.row_of, a.topk_w, a.E, a.H, a.I, a.k,
-                          a.T, a.y_rows, a.out, a.out_bf16);
+                          a.T, a.group_mask, a.y_rows, a.out, a.out_bf16);
   else
     gemv_down_kernel<NB, COMBINE, FMT><<<dim3(a.H / 8), 512, 0, st>>>(
         a.dq, a.ds, a.hq_ws, a.hs_ws, a.offsets, a.active, a.n_slots, a.n_rows, a.row_of,
-        a.topk_w, a.E, a.H, a.I, a.k, a.T, a.y_rows, a.out, a.out_bf16);
+        a.topk_w, a.E, a.H, a.I, a.k, a.T, a.group_mask, a.y_rows, a.out, a.out_bf16);
   return hipGetLastError();
 }
 

@@ -43,6 +43,7 @@ struct GemvArgs {
   int n_rows;           // down with an active list: T*k + T rows, the last T the shared ones
   int fmt;              // 1: FP4 weights, 2: FP8
   int T;                // tokens
+  const uint8_t* group_mask;  // [E+1] or null: groups with 0 are skipped (no active list)
 };
 
 struct GemmArgs {
@@ -57,6 +58,7 @@ struct GemmArgs {
   float* hs;
   float* y_rows;
   float* h_dbg;   // debug: fp32 h [T*k+T][I] of the gate+up kernels when set
+  const uint8_t* group_mask;  // [E+1] or null: groups with 0 are skipped
 };
 
 // Debug sink of the grouped GEMM's fp32 h (moe_debug_store_h).

@@ -251,29 +251,34 @@ GemmArgs gemm_args(const moe_weights* w, int T, int k, const Layout& L, void* ws
 // S5: gate + up + SwiGLU (+ requantised h in ws).
 int enqueue_gate_up(const moe_weights* w, const uint8_t* xq, const float* xs, int T, int k,
                     const int32_t* offsets, const int32_t* row_token, const Layout& L, void* ws,
-                    hipStream_t st) {
+                    hipStream_t st, const uint8_t* mask = nullptr) {
   if (gemv_path(w->format, T, k, w->hidden, w->inter)) {
     GemvArgs a = gemv_args(w, T, k, L, ws);
     a.xq = xq, a.xs = xs, a.offsets = offsets, a.row_token = row_token;
+    a.group_mask = mask;
     return launch_status(launch_gemv_gate_up(a, st));
   }
   GemmArgs g = gemm_args(w, T, k, L, ws);
   g.xq = xq, g.xs = xs, g.offsets = offsets, g.row_token = row_token;
+  g.group_mask = mask;
   return launch_status(launch_gemm_gate_up(g, st));
 }
 
 // S6 (+ S7 when out is set): down projection of the h left in ws.
 int enqueue_down(const moe_weights* w, int T, int k, const int32_t* offsets,
                  const int32_t* row_of, const float* topk_w, float* y_rows, void* out,
-                 int out_dtype, const Layout& L, void* ws, hipStream_t st) {
+                 int out_dtype, const Layout& L, void* ws, hipStream_t st,
+                 const uint8_t* mask = nullptr) {
   if (gemv_path(w->format, T, k, w->hidden, w->inter)) {
     GemvArgs a = gemv_args(w, T, k, L, ws);
     a.offsets = offsets, a.row_of = row_of, a.topk_w = topk_w;
     a.y_rows = y_rows, a.out = out, a.out_bf16 = out_dtype == MOE_DT_BF16;
+    a.group_mask = mask;
     return launch_status(launch_gemv_down(a, out != nullptr, st));
   }
   GemmArgs g = gemm_args(w, T, k, L, ws);
   g.offsets = offsets, g.y_rows = y_rows;
+  g.group_mask = mask;
   int rc = launch_status(launch_gemm_down(g, st));
   if (rc || !out) return rc;
   return launch_status(launch_combine(y_rows, row_of, topk_w, T, k, w->hidden, out,
@@ -589,6 +594,60 @@ int static_scratch(void** ptr, hipStream_t st) {
   return MOE_OK;
 }
 
+// ---- host-resident experts: an LRU cache of expert slots in HBM ----------
+
+// Bytes of one expert's matrix (codes, scales) in either format.
+struct MatBytes {
+  size_t gq, gs, dq, ds;
+};
+MatBytes mat_bytes(const moe_weights* w) {
+  const size_t H = (size_t)w->hidden, I = (size_t)w->inter;
+  if (w->format == MOE_W_FP4_E2M1_UE8M0_K32) return {I * H / 2, I * H / 32, H * I / 2, H * I / 32};
+  return {I * H, (I / 128) * (H / 128) * 4, H * I, (H / 128) * (I / 128) * 4};
+}
+
+// The call's own layout: sized for the routed-expert count E of the router
+// (the slot space has at most E groups), plus its slot ids and group masks.
+struct HostLayout {
+  Layout L;
+  size_t slot_ids, masks, total;
+};
+HostLayout host_layout(const moe_weights* host_w, int T, int k) {
+  HostLayout h;
+  const int E = host_w->n_experts;
+  h.L = layout_for(E, host_w->hidden, host_w->inter, T, k,
+                   gemv_path(host_w->format, T, k, host_w->hidden, host_w->inter));
+  h.slot_ids = h.L.total;
+  h.masks = h.slot_ids + up((size_t)T * k * 4);
+  h.total = h.masks + up((size_t)2 * (E + 1));
+  return h;
+}
+// Pinned host scratch: ids read back [T][k], slot ids [T][k], masks [2][E+1].
+size_t host_scratch_need(int E, int T, int k) {
+  return up((size_t)T * k * 4) * 2 + up((size_t)2 * (E + 1));
+}
+
+// Enqueue the copy of expert e's six arrays (host_w) into slot s (slot_w).
+int copy_expert(const moe_weights* host_w, const moe_weights* slot_w, int e, int s,
+                hipStream_t cs, uint64_t* bytes) {
+  const MatBytes b = mat_bytes(host_w);
+  const void* src[6] = {host_w->gate_q, host_w->gate_s, host_w->up_q,
+                        host_w->up_s,   host_w->down_q, host_w->down_s};
+  const void* dst[6] = {slot_w->gate_q, slot_w->gate_s, slot_w->up_q,
+                        slot_w->up_s,   slot_w->down_q, slot_w->down_s};
+  const size_t n[6] = {b.gq, b.gs, b.gq, b.gs, b.dq, b.ds};
+  for (int i = 0; i < 6; ++i) {
+    if (hipMemcpyAsync((uint8_t*)dst[i] + (size_t)s * n[i],
+                       (const uint8_t*)src[i] + (size_t)e * n[i], n[i], hipMemcpyHostToDevice,
+                       cs) != hipSuccess) {
+      (void)hipGetLastError();
+      return MOE_ELAUNCH;
+    }
+    *bytes += n[i];
+  }
+  return MOE_OK;
+}
+
 }  // namespace
 }  // namespace bef
 
@@ -622,6 +681,164 @@ int dsv4_moe_forward_noalloc(const moe_weights* w, const uint16_t* w_router, con
   if (rc) return rc;
   return enqueue_forward(w, w_router, x, T, k, routing_ids, routing_w, out, out_dtype, ws,
                          (hipStream_t)stream);
+}
+
+size_t moe_host_experts_workspace_bytes(const moe_weights* host_w, int32_t max_tokens,
+                                        int32_t top_k) {
+  if (check_weights(host_w) != MOE_OK || max_tokens < 1) return 0;
+  if (check_tk(max_tokens, top_k, host_w->n_experts) != MOE_OK) return 0;
+  size_t a = host_layout(host_w, max_tokens, top_k).total;
+  size_t b = host_layout(host_w, 1, top_k).total;
+  return a > b ? a : b;
+}
+
+size_t moe_host_experts_scratch_bytes(int32_t n_experts, int32_t max_tokens, int32_t top_k) {
+  if (n_experts < 1 || max_tokens < 1 || top_k < 1) return 0;
+  return host_scratch_need(n_experts, max_tokens, top_k);
+}
+
+int moe_forward_host_experts(const moe_weights* host_w, const moe_weights* slot_w,
+                             moe_expert_cache* cache, const uint16_t* w_router, const uint16_t* x,
+                             int32_t T, int32_t k, void* out, int32_t out_dtype, void* ws,
+                             size_t ws_bytes, void* host_scratch, size_t host_scratch_bytes,
+                             void* copies_done, void* stream, void* copy_stream) {
+  int rc = check_weights(host_w);
+  if (rc) return rc;
+  rc = check_weights(slot_w);
+  if (rc) return rc;
+  if (!cache || !cache->slot_of || !cache->expert_of || !cache->last_use || !w_router || !x ||
+      !out || !host_scratch || !copies_done)
+    return MOE_EINVAL;
+  const int E = host_w->n_experts, NS = cache->n_slots;
+  if (host_w->format != slot_w->format || host_w->hidden != slot_w->hidden ||
+      host_w->inter != slot_w->inter || cache->n_experts != E || slot_w->n_experts != NS ||
+      NS < 1 || NS > E)
+    return MOE_EINVAL;
+  if (out_dtype != MOE_DT_BF16 && out_dtype != MOE_DT_F32) return MOE_EINVAL;
+  rc = check_tk(T, k, E);
+  if (rc) return rc;
+  if ((int64_t)T * k > NS && NS < E) return MOE_ENOTSUP;  // every expert of a call fits at once
+  if (!aligned16(x) || !aligned16(out) || !aligned16(w_router) || !aligned16(host_scratch))
+    return MOE_EALIGN;
+  if (T == 0) return MOE_OK;
+  const HostLayout HL = host_layout(host_w, T, k);
+  const Layout& L = HL.L;
+  rc = check_ws(ws, ws_bytes, HL.total);
+  if (rc) return rc;
+  if (host_scratch_bytes < host_scratch_need(E, T, k)) return MOE_EWORKSPACE;
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream, cs = (hipStream_t)copy_stream;
+  const int H = host_w->hidden;
+  WsCtl* ctl = at<WsCtl>(ws, L.ctl);
+  int32_t* ids_dev = at<int32_t>(ws, L.ids);
+  float* tw_dev = at<float>(ws, L.w);
+  uint8_t* xq = at<uint8_t>(ws, L.xq);
+  float* xs = at<float>(ws, L.xs);
+  // 1. the router (with the act_quant of x) on the GPU; the ids to the host
+  rc = launch_status(launch_route(x, w_router, T, H, E, k, ids_dev, tw_dev, ctl,
+                                  at<float>(ws, L.gsum), st, xq, xs));
+  if (rc) return rc;
+  int32_t* h_ids = (int32_t*)host_scratch;
+  int32_t* h_slot_ids = (int32_t*)((uint8_t*)host_scratch + up((size_t)T * k * 4));
+  uint8_t* h_masks = (uint8_t*)host_scratch + 2 * up((size_t)T * k * 4);
+  if (hipMemcpyAsync(h_ids, ids_dev, (size_t)T * k * 4, hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_ELAUNCH;
+  }
+  // 2. the cache: hits keep their slots; each miss takes a free slot or the
+  // least recently used slot no expert of this call needs, and its weights
+  // go over on the copy stream
+  const uint64_t now = ++cache->calls;
+  uint8_t* mask_a = h_masks;          // groups computed at once: hits + shared
+  uint8_t* mask_b = h_masks + E + 1;  // groups computed on arrival: misses
+  memset(h_masks, 0, (size_t)2 * (E + 1));
+  for (int i = 0; i < T * k; ++i) {
+    const int e = h_ids[i];
+    if (e < 0 || e >= E) continue;
+    const int sl = cache->slot_of[e];
+    if (sl >= 0 && cache->last_use[sl] != now) {
+      cache->last_use[sl] = now;
+      mask_a[sl] = 1;
+      cache->hits++;
+    }
+  }
+  int n_miss = 0;
+  if (!cache->shared_resident) {
+    rc = copy_expert(host_w, slot_w, E, NS, cs, &cache->bytes_copied);
+    if (rc) return rc;
+    cache->shared_resident = 1;
+    mask_b[NS] = 1;
+    ++n_miss;
+  } else {
+    mask_a[NS] = 1;
+  }
+  for (int i = 0; i < T * k; ++i) {
+    const int e = h_ids[i];
+    if (e < 0 || e >= E || cache->slot_of[e] >= 0) continue;
+    int victim = -1;
+    for (int sl = 0; sl < NS; ++sl) {
+      if (cache->last_use[sl] == now) continue;
+      if (victim < 0 || cache->last_use[sl] < cache->last_use[victim]) victim = sl;
+    }
+    if (victim < 0) return MOE_ENOTSUP;  // unreachable: NS >= distinct experts of the call
+    if (cache->expert_of[victim] >= 0) cache->slot_of[cache->expert_of[victim]] = -1;
+    cache->expert_of[victim] = e;
+    cache->slot_of[e] = victim;
+    cache->last_use[victim] = now;
+    rc = copy_expert(host_w, slot_w, e, victim, cs, &cache->bytes_copied);
+    if (rc) return rc;
+    mask_b[victim] = 1;
+    cache->misses++;
+    ++n_miss;
+  }
+  if (n_miss && hipEventRecord((hipEvent_t)copies_done, cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_ELAUNCH;
+  }
+  // 3. slot ids and masks to the device
+  for (int i = 0; i < T * k; ++i) {
+    const int e = h_ids[i];
+    h_slot_ids[i] = (e >= 0 && e < E) ? cache->slot_of[e] : -1;
+  }
+  int32_t* slot_ids = at<int32_t>(ws, HL.slot_ids);
+  uint8_t* masks = at<uint8_t>(ws, HL.masks);
+  if (hipMemcpyAsync(slot_ids, h_slot_ids, (size_t)T * k * 4, hipMemcpyHostToDevice, st) !=
+          hipSuccess ||
+      hipMemcpyAsync(masks, h_masks, (size_t)2 * (E + 1), hipMemcpyHostToDevice, st) !=
+          hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_ELAUNCH;
+  }
+  // 4. the experts in slot space: resident groups now, the copied ones on
+  // arrival, then the combine
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* row_token = at<int32_t>(ws, L.row_token);
+  int32_t* row_of = at<int32_t>(ws, L.row_of);
+  float* y = at<float>(ws, L.y);
+  rc = launch_status(launch_permute(slot_ids, T, k, NS, offsets, row_token, row_of,
+                                    at<int32_t>(ws, L.cnt), at<int32_t>(ws, L.base),
+                                    &ctl->status, st));
+  if (rc) return rc;
+  rc = enqueue_gate_up(slot_w, xq, xs, T, k, offsets, row_token, L, ws, st, masks);
+  if (rc) return rc;
+  rc = enqueue_down(slot_w, T, k, offsets, nullptr, nullptr, y, nullptr, 0, L, ws, st, masks);
+  if (rc) return rc;
+  if (n_miss) {
+    if (hipStreamWaitEvent(st, (hipEvent_t)copies_done, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      return MOE_ELAUNCH;
+    }
+    rc = enqueue_gate_up(slot_w, xq, xs, T, k, offsets, row_token, L, ws, st, masks + E + 1);
+    if (rc) return rc;
+    rc = enqueue_down(slot_w, T, k, offsets, nullptr, nullptr, y, nullptr, 0, L, ws, st,
+                      masks + E + 1);
+    if (rc) return rc;
+  }
+  return launch_status(
+      launch_combine(y, row_of, tw_dev, T, k, H, out, out_dtype == MOE_DT_BF16, st));
 }
 
 const char* moe_status_string(int status) {

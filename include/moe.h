@@ -235,6 +235,71 @@ int dsv4_moe_forward_noalloc(const moe_weights* w, const uint16_t* w_router, con
                              int32_t T, int32_t k, const int32_t* routing_ids,
                              const float* routing_w, void* out, int32_t out_dtype, void* stream);
 
+/* ---- Host-resident experts ------------------------------------------------
+ * For layers whose routed experts do not all fit in HBM, the pages keep the
+ * routed experts in host memory and move each to the GPU when a token needs
+ * it, computing on arrival, with a per-layer LRU cache of experts on the GPU
+ * and double-buffered copies (dpshk.com article, sections "核心实现一" and
+ * "核心实现二"; tcti.cn post, section "DeepSeek-V4-Flash的可能性": routed
+ * experts in host memory).  Here: one layer's cache is n_slots expert slots
+ * in HBM plus one slot for the shared expert; a call routes on the GPU,
+ * reads the ids back (it synchronises `stream` once for that), keeps hits in
+ * their slots, copies each miss into a free or least-recently-used slot on
+ * `copy_stream`, runs the experts already resident at once and the copied
+ * ones when `copies_done` (recorded after the last copy) has fired, then
+ * combines.  Expert math and the combine order are those of
+ * dsv4_moe_forward.
+ *
+ * The cache state lives in caller-owned HOST memory:
+ *   n_experts = E of the layer, n_slots = slots in HBM (1..E),
+ *   slot_of [E] (slot of expert e or -1), expert_of [n_slots] (-1 if free),
+ *   last_use [n_slots] (call count of last use), initially all -1 / -1 / 0,
+ *   calls = 0, shared_resident = 0 (the first call copies the shared
+ *   expert into slot n_slots, where it stays); hits, misses, bytes_copied
+ *   count distinct experts per call and bytes sent to the GPU. */
+typedef struct moe_expert_cache {
+  int32_t n_experts;
+  int32_t n_slots;
+  int32_t* slot_of;
+  int32_t* expert_of;
+  uint64_t* last_use;
+  uint64_t calls;
+  int32_t shared_resident;
+  int32_t pad_;
+  uint64_t hits, misses, bytes_copied;
+} moe_expert_cache;
+
+/* Workspace bytes (device) of moe_forward_host_experts for up to max_tokens
+ * tokens of the layer `host_w` (0 on invalid arguments). */
+size_t moe_host_experts_workspace_bytes(const moe_weights* host_w, int32_t max_tokens,
+                                        int32_t top_k);
+
+/* Pinned host scratch bytes of moe_forward_host_experts (ids read back, slot
+ * ids and group masks staged for upload). */
+size_t moe_host_experts_scratch_bytes(int32_t n_experts, int32_t max_tokens, int32_t top_k);
+
+/* The whole layer with routed experts in host memory (see above).
+ *   host_w: the layer's E+1 experts in HOST memory (pinned for asynchronous
+ *           copies), layout as moe_weights;
+ *   slot_w: the cache's slots in DEVICE memory, n_experts = n_slots: slot s
+ *           of each array holds one expert, slot n_slots the shared expert;
+ *   w_router [H][E], x [T][H] bf16 on the device; out [T][H] bf16 or f32;
+ *   ws: device workspace of moe_host_experts_workspace_bytes (moe_workspace_init
+ *       once), host_scratch: pinned host memory of
+ *       moe_host_experts_scratch_bytes;
+ *   copies_done: a hipEvent_t (void*) the call records on copy_stream;
+ *   stream: compute stream; copy_stream: host-to-device copies.
+ * Requires every expert of a call to fit at once: T*k <= n_slots unless
+ * n_slots = E (MOE_ENOTSUP otherwise).  Synchronises `stream` once (the ids
+ * must reach the host to choose the copies); returns with the copies and the
+ * layer enqueued.  Reentrant only for distinct caches, slots, workspaces and
+ * streams. */
+int moe_forward_host_experts(const moe_weights* host_w, const moe_weights* slot_w,
+                             moe_expert_cache* cache, const uint16_t* w_router, const uint16_t* x,
+                             int32_t T, int32_t k, void* out, int32_t out_dtype, void* ws,
+                             size_t ws_bytes, void* host_scratch, size_t host_scratch_bytes,
+                             void* copies_done, void* stream, void* copy_stream);
+
 /* A static string naming a status code. */
 const char* moe_status_string(int status);
 

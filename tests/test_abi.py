@@ -227,3 +227,25 @@ def test_noalloc_forward_checks_arguments_and_size_on_host():
     assert f(wb, p, p, 1, 6, p, None, p, moe.MOE_DT_F32, None) == moe.MOE_EINVAL
     assert f(wb, p, p + 2, 1, 6, None, None, p, moe.MOE_DT_F32, None) == moe.MOE_EALIGN
     assert f(wb, p, p, 1, 17, None, None, p, moe.MOE_DT_F32, None) == moe.MOE_ENOTSUP
+
+
+def test_host_experts_call_checks_arguments_on_host():
+    """The host-resident-experts call refuses malformed caches and calls
+    whose experts cannot all be cached at once, before touching a device."""
+    import numpy as np
+    p = 0x100000
+    host_w = _w(E=32, ptr=p)
+    slot_w = _w(E=8, ptr=p)
+    cache = moe.ExpertCache(32, 8)
+    f = moe._lib.moe_forward_host_experts
+    C = ctypes.byref(cache.c)
+    args = lambda T, k, cw=slot_w: (ctypes.byref(host_w), ctypes.byref(cw), C, p, p, T, k, p,
+                                    moe.MOE_DT_F32, p, 1 << 30, p, 1 << 20, p, None, None)
+    assert f(*args(2, 6)) == moe.MOE_ENOTSUP            # 12 experts may not fit in 8 slots
+    assert f(*args(1, 6, _w(E=9, ptr=p))) == moe.MOE_EINVAL   # slots != cache.n_slots
+    assert f(*args(0, 6)) == moe.MOE_OK                 # empty batch
+    assert cache.c.calls == 0
+    assert moe.moe_host_experts_workspace_bytes(host_w, 4, 6) > \
+        moe.moe_workspace_bytes(host_w, 4, 6)
+    assert moe.moe_host_experts_scratch_bytes(32, 4, 6) >= 2 * 4 * 6 * 4 + 2 * 33
+    assert np.all(cache.slot_of == -1)
