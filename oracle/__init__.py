@@ -14,14 +14,18 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "liboracle.so")
+# a build of the oracle to load instead (the pins' mutation test points this
+# at copies of moe_oracle.c with a planted mistake)
+_SO_OVERRIDE = os.environ.get("BEF_ORACLE_LIB")
 FMT_FP4, FMT_FP8 = 1, 2
 
 
-def build(compiler: str = "gcc", out: str | None = None, extra=()) -> str:
+def build(compiler: str = "gcc", out: str | None = None, extra=(), src: str | None = None) -> str:
     """Compile moe_oracle.c (C99, -O2, no fast-math, no FP contraction)."""
     out = out or _SO
+    src = src or os.path.join(_HERE, "moe_oracle.c")
     cmd = [compiler, "-O2", "-std=c99", "-Wall", "-Wextra", "-ffp-contract=off", "-fopenmp",
-           "-fPIC", "-shared", *extra, os.path.join(_HERE, "moe_oracle.c"), "-o", out, "-lm"]
+           "-fPIC", "-shared", f"-I{_HERE}", *extra, src, "-o", out, "-lm"]
     subprocess.run(cmd, check=True)
     return out
 
@@ -41,6 +45,9 @@ def _load(path: str | None = None):
     if path is not None:
         return _bind(ctypes.CDLL(path))
     if _lib is None:
+        if _SO_OVERRIDE:
+            _lib = _bind(ctypes.CDLL(_SO_OVERRIDE))
+            return _lib
         if not os.path.exists(_SO):
             build()
         _lib = _bind(ctypes.CDLL(_SO))
