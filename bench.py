@@ -402,6 +402,63 @@ def sweep(hip):
     return out
 
 
+def host_experts(hip):
+    """Routed experts in pinned host memory (decode shapes: hidden 4096,
+    intermediate 2048, FP4, 256 experts top-6 + shared, router on x): 64
+    single-token calls through an LRU cache of n_slots expert slots in HBM,
+    after 64 calls that fill it.  Each call reads its ids back to the host
+    (one synchronisation) and copies its misses over PCIe on a second stream,
+    computing the resident experts meanwhile.  Per n_slots: ms per token,
+    hit rate, bytes copied per token and the copy rate over the timed calls."""
+    import numpy as np
+    import torch
+
+    import bit_expert_ffn_moe_amd as moe
+    import synth
+    names = ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")
+    L = synth.make_layer("decode_t1", T=64)
+    wl = L.wl
+    dev = "cuda:0"
+    host = {n: torch.from_numpy(np.ascontiguousarray(getattr(L, n))).pin_memory() for n in names}
+    fmt = moe.MOE_W_FP4_E2M1_UE8M0_K32
+    host_w = moe.make_weights(fmt, wl.E, wl.H, wl.I, *[host[n] for n in names])
+    x = torch.from_numpy(L.x).to(dev)
+    wr = torch.from_numpy(L.wr).to(dev)
+    out = torch.empty((1, wl.H), dtype=torch.uint16, device=dev)
+    cs = torch.cuda.Stream()
+    ev = hip.event().value
+    res = {}
+    for ns in (16, 64, 256):
+        slots = {n: torch.empty((ns + 1,) + tuple(host[n].shape[1:]), dtype=host[n].dtype,
+                                device=dev) for n in names}
+        slot_w = moe.make_weights(fmt, ns, wl.H, wl.I, *[slots[n] for n in names])
+        cache = moe.ExpertCache(wl.E, ns)
+        wsb = moe.moe_host_experts_workspace_bytes(host_w, 1, wl.k)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        moe.moe_workspace_init(ws, wsb)
+        scb = moe.moe_host_experts_scratch_bytes(wl.E, 1, wl.k)
+        scratch = torch.empty(scb, dtype=torch.uint8, pin_memory=True)
+        for rep in range(2):
+            c0 = (cache.c.hits, cache.c.misses, cache.c.bytes_copied)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for t in range(64):
+                moe.moe_forward_host_experts(host_w, slot_w, cache, wr, x[t:t + 1], 1, wl.k, out,
+                                             moe.MOE_DT_BF16, ws, wsb, scratch, scb, ev,
+                                             copy_stream=cs)
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t0
+        dh, dm = cache.c.hits - c0[0], cache.c.misses - c0[1]
+        db = cache.c.bytes_copied - c0[2]
+        res[ns] = dict(ms_per_token=round(el * 1e3 / 64, 4), tokens_per_s=round(64 / el, 1),
+                       hit_rate=round(dh / max(1, dh + dm), 4),
+                       mb_copied_per_token=round(db / 64 / 1e6, 2),
+                       copy_gbs=round(db / el / 1e9, 2))
+        del slots, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 SUB_WORKLOADS = (("tiny_t8", 256, 32), ("verify_t32", 64, 8),
                  ("prefill_fp4_t4096", 10, 3), ("prefill_fp8_t8192", 10, 3))
 
@@ -441,6 +498,8 @@ def run(args):
             subs[name] = measure(name, st, wu, hip=hip)
         line["workloads"] = subs
         line["small_batch_sweep"] = sweep(hip)
+        print("# host-resident experts", file=sys.stderr, flush=True)
+        line["host_resident_experts"] = host_experts(hip)
     line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(wl, args)
     print(json.dumps(line), flush=True)
 
@@ -532,6 +591,32 @@ def summarize(args):
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     assert files, f"no counter_collection.csv under {d}"
     rows = list(csv.DictReader(open(files[0])))
+    if args.kind == "counters":
+        # per kernel: the average per dispatch of every collected counter
+        per = {}
+        for r in rows:
+            name = r["Kernel_Name"].split("(")[0][:90]
+            per.setdefault(name, {}).setdefault(r["Counter_Name"], {}).setdefault(
+                r.get("Dispatch_Id", ""), 0.0)
+            per[name][r["Counter_Name"]][r.get("Dispatch_Id", "")] += float(r["Counter_Value"])
+        names = sorted({c for v in per.values() for c in v})
+        out = os.path.join(PROFILES, f"kernels_{args.workload}_counters.md")
+        with open(out, "w") as f:
+            f.write(f"# rocprofv3 counters per dispatch (average): workload {args.workload}\n\n")
+            f.write(f"Command: `{args.command}`\n\nSource hash: {src_hash()}\n\n")
+            f.write("MfmaUtil = 100 * SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs), the "
+                    "profiler's derived metric.\n\n")
+            f.write("| kernel | dispatches | " + " | ".join(names) + " |\n")
+            f.write("|---|---|" + "---|" * len(names) + "\n")
+            for k, cs in per.items():
+                nd = max(len(v) for v in cs.values())
+                vals = []
+                for c in names:
+                    v = cs.get(c)
+                    vals.append(f"{sum(v.values()) / len(v):.4g}" if v else "")
+                f.write(f"| {k} | {nd} | " + " | ".join(vals) + " |\n")
+        print(out)
+        return
     counter = "FETCH_SIZE" if args.kind == "fetch" else "WRITE_SIZE"
     per = {}
     for r in rows:
@@ -577,6 +662,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0)
     ap.add_argument("--graph-steps", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--host-experts-only", action="store_true",
+                    help="run only the host-resident-experts measurement")
     ap.add_argument("--sweep-only", action="store_true",
                     help="run only the small-batch sweep (T = 1 .. 256, FP4 and FP8)")
     ap.add_argument("--no-sub", action="store_true",
@@ -592,6 +679,10 @@ def main():
     if args.sweep_only:
         import torch  # noqa: F401
         print(json.dumps({"small_batch_sweep": sweep(Hip())}), flush=True)
+        return
+    if args.host_experts_only:
+        import torch  # noqa: F401
+        print(json.dumps({"host_resident_experts": host_experts(Hip())}), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
