@@ -327,48 +327,53 @@ struct ActQuantArgs {
 };
 
 // ---------------------------------------------------------------------------
-// T > 4, in two kernels.  route_group_kernel (T >= kRouteSplitT): block
-// (g, tile) owns tokens 32 tile .. +31, all E (<= 256) experts and rows
-// 256 g .. 256 g + 255 (chunks 4g .. 4g+3), 4 waves.  Per 64-row chunk the
-// block stages x and the router rows in LDS as bf16 pairs of consecutive h
-// (x: the pair as it lies in memory; router: rows h and h+1 of an expert
-// packed into one dword), and thread (ty, tx) accumulates tokens
-// 4ty..4ty+3 x experts 8tx..8tx+7 with v_dot2_f32_bf16 -- two exact
-// products per instruction, in ascending h from +0 per chunk, the group's
-// chunks in ascending order -- reading its 8 experts' pairs with two
-// 16-byte LDS reads and x four pairs at a time, while the next chunk's rows
-// load into registers.  It writes the group sums G[g][t][e].
-// route_reduce_kernel: a block per 4 tokens adds the group sums in
-// ascending group order (thread e owns expert e) and one wave per token
-// runs the top-k.  Splitting over H keeps the GPU busy at moderate T.
+// T > 4, in two kernels: the group sums G[g][t][e] over rows 256 g .. 256 g +
+// 255 (route_group_mfma_kernel from kRouteSplitT tokens on, else
+// route_group_quarter_kernel), then route_reduce_kernel: a block per 4
+// tokens adds the group sums in ascending group order (thread e owns expert
+// e) and one wave per token runs the top-k.  Splitting over H keeps the GPU
+// busy at moderate T.
 // ---------------------------------------------------------------------------
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// The group sums on the matrix cores (T >= kRouteSplitT): block (g,
+// tile) takes rows 256 g .. +255 (fewer in the last group) for 256 tokens
+// and all E <= 256 experts with v_mfma_f32_16x16x32_bf16 (bf16 products are
+// exact; the matrix cores add them in fp32 in an order of their own, so the
+// ids are a top-k of these logits like the VALU kernels').  The block's
+// router rows go to LDS once, transposed to [expert][h] (rows h, h+1 of an
+// expert packed into one dword; rows padded to 132 dwords so the 16 lanes of
+// a fragment read spread over the banks).  8 waves, each 32 tokens x all
+// experts (2 x 16 tiles of 16 x 16); a lane's token fragment (8 consecutive
+// h of one token, 16 contiguous bytes) comes straight from x, all K steps'
+// fragments loaded before the multiplies.  Writes G[g][t][e] for the reduce.
+constexpr int kRmStride = 132;  // dwords per transposed router row in LDS
 
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-__global__ __launch_bounds__(256) void route_group_kernel(const uint16_t* __restrict__ x,
-                                                          const uint16_t* __restrict__ wr, int T,
-                                                          int H, int E,
-                                                          float* __restrict__ gsum) {
-  __shared__ __align__(16) uint32_t sx2[32][36];   // [token][h pair of the chunk], padded rows
-  __shared__ __align__(16) uint32_t sw2[32][256];  // [h pair of the chunk][expert]
-  const int g = blockIdx.x, t0 = blockIdx.y * 32;
-  const int tid = threadIdx.x;
-  const int ty = tid >> 5, tx = tid & 31;
-  const int nc = H / 64;
-  const int c0 = 4 * g, c1 = min(4 * g + 4, nc);
-  float grp[4][8];
-  // this thread's share of a chunk: x row tid/8, 8 bf16 at (tid%8)*8; router
-  // pieces q = tid + 256 i (i < 4): rows 2 (q/32) and 2 (q/32) + 1, experts
-  // (q%32)*8 .. +7
-  const int xr = tid >> 3, xc = (tid & 7) * 8;
-  const bool xin = t0 + xr < T;
-  uint4 px;
-  uint4 pw[4][2];
-  auto load_row8 = [&](int h, int e8) -> uint4 {
+__global__ __launch_bounds__(512) void route_group_mfma_kernel(const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ wr,
+                                                               int T, int H, int E,
+                                                               float* __restrict__ gsum) {
+  __shared__ __align__(16) uint32_t swt[256 * kRmStride];
+  const int g = blockIdx.x, t0 = blockIdx.y * 256;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h0 = 256 * g, nh = min(256, H - h0);  // 128 or 256 rows
+  const int q = lane >> 4, r = lane & 15;
+  // this lane's token fragments for every K step, loads issued first
+  constexpr int KS = 8;
+  uint4 av[KS][2];
+#pragma unroll
+  for (int mf = 0; mf < 2; ++mf) {
+    const int t = min(t0 + 32 * w + 16 * mf + r, T - 1);
+    const uint16_t* xr = x + (size_t)t * H + h0 + 8 * q;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      av[ks][mf] = (32 * ks < nh) ? *reinterpret_cast<const uint4*>(xr + 32 * ks)
+                                  : make_uint4(0, 0, 0, 0);
+  }
+  // the router rows, transposed into LDS as (h, h+1) pairs per expert
+  auto lo2 = [](uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); };
+  auto hi2 = [](uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); };
+  auto row8 = [&](int h, int e8) -> uint4 {
     const uint16_t* src = wr + (size_t)h * E + e8;
     if (E == 256) return *reinterpret_cast<const uint4*>(src);
     uint16_t v[8];
@@ -377,81 +382,49 @@ __global__ __launch_bounds__(256) void route_group_kernel(const uint16_t* __rest
     return make_uint4(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
                       v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16));
   };
-  auto load_chunk = [&](int c) {
-    px = xin ? *reinterpret_cast<const uint4*>(x + (size_t)(t0 + xr) * H + 64 * c + xc)
-             : make_uint4(0, 0, 0, 0);
+  // consecutive lanes take consecutive row pairs of one 8-expert column
+  // block, so their LDS writes (one dword per expert) fall in consecutive banks
+  const int np = nh / 2;
+  for (int it = tid; it < np * 32; it += 512) {
+    const int p = it % np, e8 = (it / np) * 8;
+    const uint4 a = row8(h0 + 2 * p, e8), b = row8(h0 + 2 * p + 1, e8);
+    const uint32_t pr[8] = {lo2(a.x, b.x), hi2(a.x, b.x), lo2(a.y, b.y), hi2(a.y, b.y),
+                            lo2(a.z, b.z), hi2(a.z, b.z), lo2(a.w, b.w), hi2(a.w, b.w)};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + 256 * i, hp = q >> 5, e8 = (q & 31) * 8;
-      pw[i][0] = load_row8(64 * c + 2 * hp, e8);
-      pw[i][1] = load_row8(64 * c + 2 * hp + 1, e8);
-    }
-  };
-  // (lo halves of a and b) and (hi halves of a and b) as two bf16 pairs
-  auto lo2 = [](uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); };
-  auto hi2 = [](uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); };
-  auto store_chunk = [&]() {
-    *reinterpret_cast<uint4*>(&sx2[xr][xc >> 1]) = px;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + 256 * i, hp = q >> 5, e8 = (q & 31) * 8;
-      const uint4 a = pw[i][0], b = pw[i][1];
-      *reinterpret_cast<uint4*>(&sw2[hp][e8]) =
-          make_uint4(lo2(a.x, b.x), hi2(a.x, b.x), lo2(a.y, b.y), hi2(a.y, b.y));
-      *reinterpret_cast<uint4*>(&sw2[hp][e8 + 4]) =
-          make_uint4(lo2(a.z, b.z), hi2(a.z, b.z), lo2(a.w, b.w), hi2(a.w, b.w));
-    }
-  };
-  load_chunk(c0);
-  for (int c = c0; c < c1; ++c) {
-    store_chunk();
-    __syncthreads();
-    if (c + 1 < c1) load_chunk(c + 1);  // in flight while this chunk multiplies
-    float p[4][8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) p[i][j] = 0.0f;
-#pragma unroll 2
-    for (int hp4 = 0; hp4 < 32; hp4 += 4) {
-      uint4 xv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xv[i] = *reinterpret_cast<const uint4*>(&sx2[4 * ty + i][hp4]);
-#pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        const uint4 w0 = *reinterpret_cast<const uint4*>(&sw2[hp4 + hh][8 * tx]);
-        const uint4 w1 = *reinterpret_cast<const uint4*>(&sw2[hp4 + hh][8 * tx + 4]);
-        const uint32_t wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t xs = hh == 0 ? xv[i].x : hh == 1 ? xv[i].y : hh == 2 ? xv[i].z : xv[i].w;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) p[i][j] = dot2_bf16(xs, wv[j], p[i][j]);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) grp[i][j] = (c == c0) ? p[i][j] : grp[i][j] + p[i][j];
-    __syncthreads();
+    for (int u = 0; u < 8; ++u) swt[(e8 + u) * kRmStride + p] = pr[u];
   }
+  __syncthreads();
+  v4f_t acc[2][16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + 4 * ty + i;
-    if (t >= T) continue;
-    float* dst = gsum + ((size_t)g * T + t) * E;
-    if (E == 256) {
-      *reinterpret_cast<float4*>(dst + 8 * tx) =
-          make_float4(grp[i][0], grp[i][1], grp[i][2], grp[i][3]);
-      *reinterpret_cast<float4*>(dst + 8 * tx + 4) =
-          make_float4(grp[i][4], grp[i][5], grp[i][6], grp[i][7]);
-    } else {
+  for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (8 * tx + j < E) dst[8 * tx + j] = grp[i][j];
+    for (int f = 0; f < 16; ++f) acc[mf][f] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (32 * ks >= nh) break;
+    const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, av[ks][0]);
+    const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, av[ks][1]);
+#pragma unroll
+    for (int f = 0; f < 16; ++f) {
+      const uint4 bv =
+          *reinterpret_cast<const uint4*>(&swt[(16 * f + r) * kRmStride + 16 * ks + 4 * q]);
+      const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bv);
+      acc[0][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc[0][f], 0, 0, 0);
+      acc[1][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc[1][f], 0, 0, 0);
     }
   }
+  // tile (mf, f): lane holds experts 16 f + r, tokens 16 mf + 4 q + v of the wave's 32
+#pragma unroll
+  for (int mf = 0; mf < 2; ++mf)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t = t0 + 32 * w + 16 * mf + 4 * q + v;
+      if (t >= T) continue;
+      float* dst = gsum + ((size_t)g * T + t) * E;
+#pragma unroll
+      for (int f = 0; f < 16; ++f)
+        if (16 * f + r < E) dst[16 * f + r] = acc[mf][f][v];
+    }
 }
 
 // Fewer tokens (T < kRouteSplitT): the same group sums with the experts split
@@ -594,10 +567,9 @@ hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int H, int
   const int ng = (H / 64 + 3) / 4;
   if (T < kRouteSplitT) {
     // act_quant of x (when xq is set) in extra x-slices of the router's grid:
-    // one launch fewer.  (Not at more tokens: extra blocks of
-    // route_group_kernel would each hold its 73 KB of LDS and crowd out the
-    // router blocks -- measured at 8192 tokens, +42 us; a launch of its own
-    // follows instead.)
+    // one launch fewer.  (From kRouteSplitT tokens on, the matrix-core
+    // router's blocks hold 132 KB of LDS each, and the act_quant runs as a
+    // launch of its own.)
     ActQuantArgs aq = {x, xq, xs, (int64_t)T * (H / 128), 0};
     if (xq) aq.nb = (aq.nblocks * 16 + 255) / 256;
     const int ny = (E + 63) / 64, nz = (T + 31) / 32;
@@ -605,7 +577,8 @@ hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int H, int
     route_group_quarter_kernel<<<dim3(ng + nqx, ny, nz), dim3(256), 0, st>>>(x, wr, T, H, E,
                                                                             gsum, aq);
   } else {
-    route_group_kernel<<<dim3(ng, (T + 31) / 32), dim3(256), 0, st>>>(x, wr, T, H, E, gsum);
+    route_group_mfma_kernel<<<dim3(ng, (T + 255) / 256), dim3(512), 0, st>>>(x, wr, T, H, E,
+                                                                            gsum);
   }
   route_reduce_kernel<<<dim3((T + 3) / 4), dim3(256), 0, st>>>(gsum, T, H, E, k, ids, w);
   if (xq && T >= kRouteSplitT) return launch_act_quant(x, true, T, H, xq, xs, st);

@@ -122,10 +122,11 @@ int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *   topk_ids [T][k] int32 out: experts ordered by (logit desc, id asc)
  *   topk_w   [T][k] f32 out: sigmoid(logit) renormalised over the k chosen
  * Logits are fp32 sums of the exact bf16 x bf16 products in a fixed order
- * for a given T (64-wide chunk partials, each a chain in ascending h from +0
- * -- of fused multiply-adds below 256 tokens, of two-product dot steps from
- * 256 tokens on; sums of 4 consecutive chunks in ascending order; those
- * group sums in ascending order), so the ids are deterministic.  They are the
+ * for a given T: below 256 tokens, 64-wide chunk partials (chains of fused
+ * multiply-adds in ascending h from +0), sums of 4 consecutive chunks in
+ * ascending order, those group sums in ascending order; from 256 tokens on,
+ * the same 256-row group sums formed on the matrix cores (bf16 MFMA, fp32
+ * accumulation in the hardware's order).  The ids are deterministic.  They are the
  * exact top-k of these logits; logits summed in any other order differ by
  * rounding only, so another order can rank two experts differently only
  * where their logits lie within rounding distance of each other.
