@@ -45,6 +45,8 @@
 // time, so those stream from HBM about once.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -341,17 +343,25 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int ti = 0; ti < NT; ++ti) acc[i][ti] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
-    // a wave whose 64 tokens are all past the group's rows skips the
-    // multiplies (the tokens of a partly filled band are multiplied anyway:
-    // clamped copies of a real row, never stored)
-    const bool live = nrows > wt * (TM / 4);
+    // Token fragments of 16 per wave: NT for a full tile; in a 256-token
+    // tile, NT - 1 when the group's rows fit in three quarters of it (each
+    // token wave then takes
+    // 16 (NT - 1) tokens, so a tile of at most 3/4 TM rows spends a quarter
+    // fewer multiplies and token fragment reads, all four SIMDs still
+    // equally busy).  A wave whose tokens are all past the group's rows
+    // skips the multiplies (the tokens of a partly filled band are
+    // multiplied anyway: clamped copies of a real row, never stored).
+    const bool part = NT == 4 && nrows <= 64 * (NT - 1);
+    const int TS = part ? 16 * (NT - 1) : 16 * NT;  // tokens per token wave
+    const bool live = nrows > wt * TS;
     auto wrow = [&](int i) {
       return GU ? ((i < 4 ? 0 : 128) + 64 * wn + 16 * (i & 3) + (lane & 15))
                 : (128 * wn + 16 * i + (lane & 15));
     };
 
-    auto compute = [&](int ks, const uint8_t* sA, const uint8_t* sB, const uint32_t* sS,
-                       const float* sX) {
+    auto compute = [&](auto ntl, int ks, const uint8_t* sA, const uint8_t* sB,
+                       const uint32_t* sS, const float* sX) {
+      constexpr int NTL = decltype(ntl)::value;  // token fragments of this wave
       if (!live) return;
       auto read_w = [&](int i, v8i_t& wv, int& sw) {
         const int n = wrow(i);
@@ -371,10 +381,10 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
       // order): the scales (a few bytes; the first fold needs them), weight
       // fragment 0, then the wave's 4 token fragments, so that the first
       // MFMA waits only for its own two fragments
-      float cx[NT], cy[NT];
+      float cx[NTL], cy[NTL];
 #pragma unroll
-      for (int ti = 0; ti < NT; ++ti) {
-        const float x = sX[wt * (TM / 4) + 16 * ti + (lane & 15)];
+      for (int ti = 0; ti < NTL; ++ti) {
+        const float x = sX[wt * 16 * NTL + 16 * ti + (lane & 15)];
         cx[ti] = x;
         cy[ti] = x;
       }
@@ -387,10 +397,10 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
       v8i_t wv[2];
       int sw[2];
       read_w(0, wv[0], sw[0]);
-      v8i_t tv[NT];
+      v8i_t tv[NTL];
 #pragma unroll
-      for (int ti = 0; ti < NT; ++ti) {
-        const int r = wt * (TM / 4) + 16 * ti + (lane & 15);
+      for (int ti = 0; ti < NTL; ++ti) {
+        const int r = wt * 16 * NTL + 16 * ti + (lane & 15);
         const uint4 a0 = *reinterpret_cast<const uint4*>(sA + sw128(r, q));
         const uint4 a1 = *reinterpret_cast<const uint4*>(sA + sw128(r, q + 4));
         tv[ti] = (v8i_t){(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
@@ -398,7 +408,7 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
       }
       if (FMT == 2) {
 #pragma unroll
-        for (int ti = 0; ti < NT; ++ti) {
+        for (int ti = 0; ti < NTL; ++ti) {
           cy[ti] = cx[ti] * f1;
           cx[ti] = cx[ti] * f0;
         }
@@ -408,13 +418,13 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
       for (int i = 0; i < 8; ++i) {
         // fragment i+1 is read while fragment i multiplies
         if (i + 1 < 8) read_w(i + 1, wv[(i + 1) & 1], sw[(i + 1) & 1]);
-        v4f_t d[NT];
+        v4f_t d[NTL];
 #pragma unroll
-        for (int ti = 0; ti < NT; ++ti)
+        for (int ti = 0; ti < NTL; ++ti)
           d[ti] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               wv[i & 1], tv[ti], zero, FMT == 1 ? 4 : 0, 0, 0, sw[i & 1], 0, 127);
 #pragma unroll
-        for (int ti = 0; ti < NT; ++ti) {
+        for (int ti = 0; ti < NTL; ++ti) {
           const float c = (GU && i >= 4) ? cy[ti] : cx[ti];
           acc[i][ti][0] = fmaf(c, d[ti][0], acc[i][ti][0]);
           acc[i][ti][1] = fmaf(c, d[ti][1], acc[i][ti][1]);
@@ -462,23 +472,37 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
         issue(i, st.a, st.b, st.s, st.x);
       }
     }
-    for (int kb = 0; kb < KS; kb += NST) {
-#pragma unroll
-      for (int j = 0; j < NST; ++j) {
-        const int ks = kb + j;
-        if (ks < KS) {
-          wait_stages(min(NST - 2, KS - 1 - ks));
-          __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-          block_barrier();
-          if (ks + NST - 1 < KS) {
-            const Stage nx = stage((j + NST - 1) % NST);
-            issue(ks + NST - 1, nx.a, nx.b, nx.s, nx.x);
-          }
-          const Stage cu = stage(j);
-          compute(ks, cu.a, cu.b, cu.s, cu.x);
-        }
-      }
+    // the loop, for NTL token fragments per wave.  (Measured on the
+    // compiler at hand: the 256-token tile runs faster with its two loops in
+    // a generic lambda, the smaller tiles, with one loop, without: written
+    // once as a macro, it serves both.)
+#define BEF_KLOOP(NTL)                                                      \
+  for (int kb = 0; kb < KS; kb += NST) {                                    \
+    _Pragma("unroll") for (int j = 0; j < NST; ++j) {                       \
+      const int ks = kb + j;                                                \
+      if (ks < KS) {                                                        \
+        wait_stages(min(NST - 2, KS - 1 - ks));                             \
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);                             \
+        block_barrier();                                                    \
+        if (ks + NST - 1 < KS) {                                            \
+          const Stage nx = stage((j + NST - 1) % NST);                      \
+          issue(ks + NST - 1, nx.a, nx.b, nx.s, nx.x);                      \
+        }                                                                   \
+        const Stage cu = stage(j);                                          \
+        compute(std::integral_constant<int, NTL>{}, ks, cu.a, cu.b, cu.s, cu.x); \
+      }                                                                     \
+    }                                                                       \
+  }
+    if constexpr (NT == 4) {
+      auto kloop = [&](auto ntl) { BEF_KLOOP(decltype(ntl)::value) };
+      if (part)
+        kloop(std::integral_constant<int, 3>{});
+      else
+        kloop(std::integral_constant<int, 4>{});
+    } else {
+      BEF_KLOOP(NT)
     }
+#undef BEF_KLOOP
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     block_barrier();
 
@@ -504,14 +528,15 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
       for (int ti = 0; ti < NT; ++ti) {
         m[ti] = fmaxf(m[ti], __shfl_xor(m[ti], 16, kWave));
         m[ti] = fmaxf(m[ti], __shfl_xor(m[ti], 32, kWave));
-        if (q == 0) s_amax[wn][wt * (TM / 4) + 16 * ti + lane] = m[ti];
+        if (q == 0 && (!part || ti < NT - 1)) s_amax[wn][wt * TS + 16 * ti + lane] = m[ti];
       }
       __syncthreads();
       uint8_t* s_out = sA0;  // [token][128 codes]
       const int I128 = I >> 7;
 #pragma unroll
       for (int ti = 0; ti < NT; ++ti) {
-        const int t = wt * (TM / 4) + 16 * ti + (lane & 15);
+        if (part && ti == NT - 1) continue;
+        const int t = wt * TS + 16 * ti + (lane & 15);
         const float am = fmaxf(s_amax[0][t], s_amax[1][t]);
         const float sc = am / 448.0f;
         const float rsc = __builtin_amdgcn_rcpf(sc);
@@ -541,8 +566,8 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
     } else {
 #pragma unroll
       for (int ti = 0; ti < NT; ++ti) {
-        const int t = wt * (TM / 4) + 16 * ti + (lane & 15);
-        if (live && t < nrows && nb * kTN2 + 128 * wn < H) {
+        const int t = wt * TS + 16 * ti + (lane & 15);
+        if (live && (!part || ti < NT - 1) && t < nrows && nb * kTN2 + 128 * wn < H) {
           float* yp = a.y_rows + (size_t)(row0 + t) * H + nb * kTN2 + 128 * wn + 4 * q;
 #pragma unroll
           for (int i = 0; i < 8; ++i)
