@@ -13,10 +13,11 @@ the 256 MB Infinity Cache.  Steps are captured once into a HIP graph and the
 graph is replayed, so host launch overhead does not pace the GPU.
 
 Prints ONE JSON line.  `value` is tokens/s of the whole step; `roofline`
-describes the dominant kernel (gate+up, S5): its algorithmic bytes (or
-flops) per launch divided by its average duration, measured with HIP events
-on the launch stream around S5 of stage-by-stage steps that run back to back
-behind a backlog of graph replays.  `cpu_baseline` times the oracle on
+describes the dominant kernel -- for one token with FP4 weights the fused
+expert kernel (routed gate+up, down of every expert, combine), otherwise the
+gate+up kernel (S5) -- : its algorithmic bytes (or flops) per launch divided
+by its average duration, measured with HIP events that the library records
+in that kernel's own dispatch over eager product steps run back to back.  `cpu_baseline` times the oracle on
 a bounded sample on the host cores.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -42,13 +43,14 @@ METRIC = ("MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA TFLOPS (prefil
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, published (FP8 x FP4 runs at this rate)
 PROFILES = os.path.join(ROOT, "profiles")
-DOMINANT = {"gemv": "gemv_gate_up_kernel", "gemm": "gemm_kernel_gate_up"}
+DOMINANT = {"fused": "decode_ffn_kernel", "gemv": "gemv_gate_up_kernel",
+            "gemm": "gemm_kernel_gate_up"}
 
 
 def is_dominant(kernel_name, path):
     """Does a profiler kernel name belong to the path's dominant kernel?"""
-    if path == "gemv":
-        return "gemv_gate_up_kernel" in kernel_name
+    if path in ("fused", "gemv"):
+        return DOMINANT[path] in kernel_name
     # gemm_kernel<FMT, GU, TM>: the gate+up instances
     return "gemm_kernel<" in kernel_name and ", true," in kernel_name
 
@@ -68,9 +70,11 @@ def expert_bytes(wl):
 
 
 def work(wl, ids, path):
-    """Algorithmic bytes / flops of a step and of the dominant kernel (the
-    gate+up kernel; on the one-token VALU path it streams the routed experts
-    only -- the shared expert's gate+up runs in the front kernel)."""
+    """Algorithmic bytes / flops of a step and of the dominant kernel: the
+    gate+up kernel (on the VALU path it streams the routed experts only --
+    the shared expert's gate+up runs in the front kernel), or the fused
+    one-token kernel (the routed experts' gate+up and every touched expert's
+    down)."""
     T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
     routed = len(set(ids.ravel().tolist()))
     touched = routed + 1                                  # + shared expert
@@ -78,9 +82,12 @@ def work(wl, ids, path):
     R = T * k + T
     step_bytes = touched * per_exp + H * E * 2 + T * H * 2 + T * H * 2
     step_flops = 2 * 3 * H * I * R + 2 * T * H * E
-    gu_exp, gu_rows = (routed, T * k) if path == "gemv" else (touched, R)
+    gu_exp, gu_rows = (touched, R) if path == "gemm" else (routed, T * k)
     gu_bytes = gu_exp * per_exp_gu + T * H + T * (H // 128) * 4
     gu_flops = 2 * 2 * H * I * gu_rows
+    if path == "fused":
+        gu_bytes += touched * (per_exp - per_exp_gu)
+        gu_flops += 2 * H * I * R
     return dict(touched=touched, step_bytes=step_bytes, step_flops=step_flops,
                 gu_bytes=gu_bytes, gu_flops=gu_flops, rows=R)
 
@@ -148,7 +155,7 @@ class Hip:
 # --------------------------------------------------------------------------
 
 class Bench:
-    def __init__(self, wl_name, copies, n_tokens_pool, over=None):
+    def __init__(self, wl_name, copies, n_tokens_pool, over=None, fused=False):
         import numpy as np
         import torch
 
@@ -198,9 +205,15 @@ class Bench:
             self.out = torch.empty((T, H), dtype=torch.uint16, device=dev)
         torch.cuda.synchronize()
         # the expert path the library takes for this shape: only the VALU
-        # GEMV path keeps an fp32 h in the workspace
+        # GEMV path keeps an fp32 h in the workspace; of it, one token with
+        # FP4 weights runs the fused kernel where it fits (the library's
+        # rule, checked by the fused kernel's tests through the timing hook)
         h, _, _ = moe.moe_debug_intermediates(self.w[0], T, k, self.ws, self.ws_bytes)
         self.path = "gemv" if h is not None else "gemm"
+        if (self.path == "gemv" and fused and T == 1 and wl.fmt == "fp4" and k + 1 <= 8
+                and I_fits(wl) and H % 16 == 0 and H <= 4096
+                and H // 16 <= torch.cuda.get_device_properties(0).multi_processor_count):
+            self.path = "fused"
 
     def x_of(self, step):
         if self.pool:
@@ -223,8 +236,15 @@ class Bench:
                              moe.MOE_DT_BF16, self.ws, self.ws_bytes, self.sp)
 
 
+def I_fits(wl):
+    return wl.I <= 2048 and wl.I % 128 == 0
+
+
 def kernel_ids(moe, path):
-    """(gate+up, down) kernel ids of the timing hook for the path."""
+    """(dominant, down) kernel ids of the timing hook for the path (the fused
+    kernel has no separate down)."""
+    if path == "fused":
+        return moe.MOE_KERNEL_DECODE_FFN, None
     if path == "gemv":
         return moe.MOE_KERNEL_GEMV_GATE_UP, moe.MOE_KERNEL_GEMV_DOWN
     return moe.MOE_KERNEL_GEMM_GATE_UP, moe.MOE_KERNEL_GEMM_DOWN
@@ -249,10 +269,21 @@ def time_kernel(B, which, n_ev):
         float(np.percentile(ms, 90)) * 1e-3
 
 
-def measure(wl_name, steps, warmup, copies=0, graph_steps=0, hip=None, over=None):
+def measure(wl_name, steps, warmup, copies=0, graph_steps=0, hip=None, over=None, fused=False):
     """Time `steps` whole-layer steps of a workload (graph replays) and its
-    gate+up and down kernels; returns the figures as a dict.  `over` changes
-    the workload's T or weight format (the small-batch sweep)."""
+    dominant and down kernels; returns the figures as a dict.  `over` changes
+    the workload's T or weight format (the small-batch sweep); fused=True
+    runs the one-token FP4 path with the fused expert kernel (opt-in; the
+    library's default is the separate gate+up and down+combine kernels)."""
+    import bit_expert_ffn_moe_amd as moe
+    moe.moe_debug_set_decode_fused(1 if fused else 0)
+    try:
+        return _measure(wl_name, steps, warmup, copies, graph_steps, hip, over, fused)
+    finally:
+        moe.moe_debug_set_decode_fused(0)
+
+
+def _measure(wl_name, steps, warmup, copies, graph_steps, hip, over, fused):
     import dataclasses
 
     import numpy as np
@@ -261,7 +292,7 @@ def measure(wl_name, steps, warmup, copies=0, graph_steps=0, hip=None, over=None
     import synth
     wl = dataclasses.replace(synth.WORKLOADS[wl_name], **(over or {}))
     copies = copies or (8 if wl.T == 1 else 2 if wl.T <= 64 else 1)
-    B = Bench(wl_name, copies, 64, over)
+    B = Bench(wl_name, copies, 64, over, fused)
     B.hip = hip or Hip()
     per_graph = graph_steps or (64 if wl.T == 1 else 8 if wl.T <= 64 else 1)
     per_graph = max(1, min(per_graph, steps))
@@ -293,7 +324,7 @@ def measure(wl_name, steps, warmup, copies=0, graph_steps=0, hip=None, over=None
     n_ev = max(1, min(256 if wl.T <= 64 else 16, steps))
     gu_id, dn_id = kernel_ids(B.moe, B.path)
     gu_avg_s, gu_p10, gu_p90 = time_kernel(B, gu_id, n_ev)
-    dn_avg_s, _, _ = time_kernel(B, dn_id, n_ev)
+    dn_avg_s = time_kernel(B, dn_id, n_ev)[0] if dn_id is not None else None
     # algorithmic work of the steps
     if wl.routing == "zipf":
         ids_steps = [B.layer.ids]
@@ -311,7 +342,7 @@ def measure(wl_name, steps, warmup, copies=0, graph_steps=0, hip=None, over=None
     gu_tflops = avg["gu_flops"] / gu_avg_s / 1e12
     t_hbm = avg["gu_bytes"] / (HBM_PEAK_GBS * 1e9)
     t_mfma = avg["gu_flops"] / (FP8_PEAK_TFLOPS * 1e12)
-    if B.path == "gemv" or t_hbm >= t_mfma:
+    if B.path != "gemm" or t_hbm >= t_mfma:
         roof = dict(bound="hbm", achieved=round(gu_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(gu_gbs / HBM_PEAK_GBS, 4))
     else:
@@ -333,7 +364,7 @@ def measure(wl_name, steps, warmup, copies=0, graph_steps=0, hip=None, over=None
                step_hbm_gbs=round(step_gbs, 1), step_roofline_frac=round(step_gbs / HBM_PEAK_GBS, 4),
                touched_experts_avg=round(avg["touched"], 2), layer_copies=copies,
                graph_steps=per_graph, roofline=roof,
-               down_kernel_avg_us=round(dn_avg_s * 1e6, 2))
+               down_kernel_avg_us=None if dn_avg_s is None else round(dn_avg_s * 1e6, 2))
     if B.path == "gemm":
         # the grouped GEMM as a whole (gate+up and down): flops of every row
         ff = 2 * 3 * wl.H * wl.I * avg["rows"]
@@ -347,17 +378,17 @@ def measure(wl_name, steps, warmup, copies=0, graph_steps=0, hip=None, over=None
     return res
 
 
-def stream_ceiling(hip):
+def stream_ceiling(hip, dom_bytes):
     """Plain streaming read (the library's debug read kernel) of a buffer
-    the size of the decode gate+up's weights and of a 2 GiB buffer: the
-    practical HBM read ceiling, as GB/s (best grid of a few)."""
+    the size of the dominant decode kernel's weights and of a 2 GiB buffer:
+    the practical HBM read ceiling, as GB/s (best grid of a few)."""
     import torch
 
     import bit_expert_ffn_moe_amd as moe
     out = {}
     sink = torch.zeros(4, dtype=torch.uint8, device="cuda:0")
     L = hip.L
-    for label, nbytes in (("54MB", 53_481_600 // 16 * 16), ("2GiB", 2 << 30)):
+    for label, nbytes in ((f"{dom_bytes / 1e6:.0f}MB", dom_bytes // 16 * 16), ("2GiB", 2 << 30)):
         n_buf = max(1, min(16, (1 << 30) // nbytes)) if nbytes < (1 << 30) else 1
         bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda:0") for _ in range(n_buf)]
         best = None
@@ -468,6 +499,17 @@ def run(args):
     wl = synth.WORKLOADS[args.workload]
     hip = Hip()
     head = measure(wl.name, args.steps, args.warmup, args.copies, args.graph_steps, hip)
+    if wl.T == 1 and wl.fmt == "fp4":
+        # the same steps with the fused one-token expert kernel (opt-in)
+        print("# one-token path with the fused expert kernel", file=sys.stderr, flush=True)
+        fu = measure(wl.name, min(args.steps, 1024), args.warmup, args.copies,
+                     args.graph_steps, hip, fused=True)
+        if fu["path"] == "fused":
+            head["fused_kernel"] = dict(
+                ms_per_step=fu["ms_per_step"], tokens_per_s=fu["tokens_per_s"],
+                kernel_avg_us=fu["roofline"]["kernel_avg_us"],
+                algorithmic_bytes=fu["roofline"]["algorithmic_bytes"],
+                hbm_gbs=fu["roofline"]["hbm_gbs"], hbm_frac=fu["roofline"]["hbm_frac"])
     line = {
         "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": head["steps"], "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
@@ -484,14 +526,17 @@ def run(args):
                    "step_hbm_gbs": head["step_hbm_gbs"],
                    "step_roofline_frac": head["step_roofline_frac"],
                    "ms_p10": head["ms_p10"], "ms_p90": head["ms_p90"],
-                   "down_kernel_avg_us": head["down_kernel_avg_us"]},
+                   "path": head["path"],
+                   "down_kernel_avg_us": head["down_kernel_avg_us"],
+                   "fused_kernel": head.get("fused_kernel")},
         "roofline": head["roofline"],
     }
     if not args.no_sub and args.workload == "decode_t1":
-        ceil = stream_ceiling(hip)
+        dom = head["roofline"]["algorithmic_bytes"]
+        ceil = stream_ceiling(hip, dom)
         line["hbm_read_ceiling_gbs"] = ceil
         line["roofline"]["frac_of_measured_ceiling"] = round(
-            head["roofline"]["hbm_gbs"] / ceil["54MB"], 4)
+            head["roofline"]["hbm_gbs"] / ceil[f"{dom / 1e6:.0f}MB"], 4)
         subs = {}
         for name, st, wu in SUB_WORKLOADS:
             print(f"# sub-workload {name}", file=sys.stderr, flush=True)

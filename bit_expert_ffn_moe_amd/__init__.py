@@ -22,6 +22,7 @@ MOE_W_FP4_E2M1_UE8M0_K32, MOE_W_FP8_E4M3_F32_B128 = 1, 2
 MOE_DT_BF16, MOE_DT_F32 = 1, 2
 MOE_STATUS_BAD_EXPERT_ID, MOE_STATUS_SYNC_TIMEOUT = 1, 2
 MOE_KERNEL_GEMV_GATE_UP, MOE_KERNEL_GEMM_GATE_UP, MOE_KERNEL_GEMV_DOWN, MOE_KERNEL_GEMM_DOWN = 1, 2, 3, 4
+MOE_KERNEL_DECODE_FFN = 5
 MOE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 if not os.path.exists(_SO):
@@ -88,6 +89,7 @@ _sigs = {
     "moe_debug_intermediates": ([_W, _i32, _i32, _vp, _sz, ctypes.POINTER(_vp),
                                  ctypes.POINTER(_vp), ctypes.POINTER(_vp)], ctypes.c_int),
     "moe_debug_time_kernel": ([_i32, _vp, _vp], ctypes.c_int),
+    "moe_debug_set_decode_fused": ([_i32], ctypes.c_int),
     "moe_debug_store_h": ([_vp, _sz], ctypes.c_int),
     "moe_debug_stream_read": ([_vp, _sz, _vp, _i32, _vp], ctypes.c_int),
     "moe_debug_routing": ([_W, _i32, _i32, _vp, _sz, ctypes.POINTER(_vp), ctypes.POINTER(_vp)],
@@ -240,6 +242,11 @@ def moe_device_status(ws, stream=None, clear: bool = False) -> int:
     _check(_lib.moe_device_status(_ptr(ws), _stream(stream), ctypes.byref(st), int(clear)),
            "moe_device_status")
     return st.value
+
+
+def moe_debug_set_decode_fused(fused) -> int:
+    """1: the one-token FP4 path runs the fused expert kernel where it fits; 0: separate kernels."""
+    return _check(_lib.moe_debug_set_decode_fused(int(fused)), "moe_debug_set_decode_fused")
 
 
 def moe_debug_time_kernel(which, start_event, stop_event) -> int:

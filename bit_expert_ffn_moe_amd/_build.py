@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SO = os.path.join(PKG, "libbefmoe.so")
 SOURCES = ["moe_api.hip", "actq.hip", "route.hip", "permute.hip", "gemv.hip", "gemm.hip",
-           "combine.hip"]
+           "combine.hip", "decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

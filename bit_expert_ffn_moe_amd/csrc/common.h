@@ -290,6 +290,16 @@ struct WsCtl {
   uint64_t h_slots[32 * 4096];
   // small-T router: group sums [H/256 <= 32][T <= 4][E <= 256]
   uint64_t route_slots[32 * 4 * 256];
+  // one-token fused expert kernel (decode.hip): the launch epoch, the count
+  // of its finished blocks, per-128-block counts of published gate+up units,
+  // then words tagged with the epoch
+  // (never cleared): h values [row 8][2048] and requantised h [row 8][16
+  // blocks of 128][32 code words + 1 scale word, padded to 36]
+  uint32_t dec_epoch, dec_done;
+  uint32_t pad2[62];
+  uint32_t dec_cnt[8 * 16];  // per 128-block of h: gate+up units published (zero between launches)
+  uint64_t dec_h[8 * 2048];
+  uint64_t dec_c[8 * 16 * 36];
 };
 
 __device__ __forceinline__ void set_status(uint32_t* st, uint32_t bit) { atomicOr(st, bit); }

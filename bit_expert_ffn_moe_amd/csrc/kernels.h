@@ -22,7 +22,7 @@ constexpr uint32_t MOE_STATUS_BAD_EXPERT_ID_DEV = 1u;
 struct KernelTimer {
   hipEvent_t start, stop;
 };
-extern KernelTimer g_kernel_timer[5];
+extern KernelTimer g_kernel_timer[6];
 
 struct GemvArgs {
   const uint8_t *gq, *gs, *uq, *us, *dq, *ds;
@@ -60,6 +60,34 @@ struct GemmArgs {
   float* h_dbg;   // debug: fp32 h [T*k+T][I] of the gate+up kernels when set
   const uint8_t* group_mask;  // [E+1] or null: groups with 0 are skipped
 };
+
+// The one-token fused expert kernel (decode.hip): 16 output rows per block
+// (one block per CU), 16 waves, at most 8 h rows (k + 1).
+constexpr int kDecRowsPerBlock = 16;
+constexpr int kDecWaves = 16;
+constexpr int kDecMaxRows = 8;
+struct DecodeArgs {
+  const uint8_t *gq, *gs, *uq, *us, *dq, *ds;  // FP4 weights [E+1][...]
+  const uint8_t* xq;          // the token's E4M3 codes [H] and scales [H/128]
+  const float* xs;
+  const int4* active;         // routed slots {group, row, row + 1} (rows 0 .. k-1)
+  const int32_t* row_of;      // [k+1]: h row of rank j, then the shared row
+  const float* topk_w;        // [k]
+  int E, H, I, k;
+  float* h;                   // [k+1][I] fp32 h (inspection)
+  uint8_t* hq;                // [k+1][I] requantised h (row k: the shared expert's, read)
+  float* hs;                  // [k+1][I/128]
+  uint64_t* dec_h;            // WsCtl::dec_h, dec_c, dec_epoch, dec_done
+  uint64_t* dec_c;
+  uint32_t* epoch;
+  uint32_t* done;
+  uint32_t* cnt;              // [8][16] published gate+up units per 128-block
+  uint32_t* status;
+  void* out;                  // [H] f32 or bf16
+  int out_bf16;
+};
+bool decode_ffn_fits(int fmt, int T, int k, int H, int I);
+hipError_t launch_decode_ffn(const DecodeArgs& a, hipStream_t st);
 
 // Debug sink of the grouped GEMM's fp32 h (moe_debug_store_h).
 struct HSink {

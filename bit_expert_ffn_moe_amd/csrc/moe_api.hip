@@ -13,7 +13,10 @@
 
 namespace bef {
 
-KernelTimer g_kernel_timer[5];
+KernelTimer g_kernel_timer[6];
+// the one-token FP4 path: the fused expert kernel where it fits when set
+// (measured slower than the separate kernels: off by default)
+std::atomic<int> g_decode_fused{0};
 HSink g_h_sink;
 
 __global__ void zero_words_kernel(uint32_t* p, int n) {
@@ -494,6 +497,10 @@ int enqueue_forward(const moe_weights* w, const uint16_t* w_router, const uint16
     fa.ids = at<int32_t>(ws, L.ids), fa.w = at<float>(ws, L.w);
     fa.offsets = offsets, fa.row_token = row_token, fa.row_of = row_of;
     if (gemv_path(w->format, T, k, H, w->inter)) {
+      // decided before anything is enqueued: the fused expert kernel's shape
+      // conditions (it refuses nothing that passes them)
+      const bool fused =
+          g_decode_fused.load() && decode_ffn_fits(w->format, T, k, H, w->inter);
       // one token on the VALU path: the front kernel also quantises x, runs
       // the shared expert's gate+up (its waves quantise x themselves, same
       // rule) and lists the routed groups for the gate+up kernel
@@ -516,6 +523,20 @@ int enqueue_forward(const moe_weights* w, const uint16_t* w_router, const uint16
       a.xq = xq, a.xs = xs, a.offsets = offsets, a.row_token = row_token;
       a.active = at<int4>(ws, L.active);
       a.n_slots = fa.n_active_slots;
+      if (fused) {
+        // routed gate+up, down of all k + 1 rows and the combine, one launch
+        DecodeArgs d;
+        memset(&d, 0, sizeof d);
+        d.gq = a.gq, d.gs = a.gs, d.uq = a.uq, d.us = a.us, d.dq = a.dq, d.ds = a.ds;
+        d.xq = xq, d.xs = xs, d.active = a.active, d.row_of = row_of, d.topk_w = fa.w;
+        d.E = E, d.H = H, d.I = w->inter, d.k = k;
+        d.h = a.h, d.hq = a.hq_ws, d.hs = a.hs_ws;
+        d.dec_h = ctl->dec_h, d.dec_c = ctl->dec_c;
+        d.epoch = &ctl->dec_epoch, d.done = &ctl->dec_done, d.status = &ctl->status;
+        d.cnt = ctl->dec_cnt;
+        d.out = out, d.out_bf16 = out_dtype == MOE_DT_BF16;
+        return launch_status(launch_decode_ffn(d, st));
+      }
       rc = launch_status(launch_gemv_gate_up(a, st));
       if (rc) return rc;
       // down + combine, the rows' groups from the same active list
@@ -887,8 +908,14 @@ int moe_debug_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t
   return launch_status(hipGetLastError());
 }
 
+int moe_debug_set_decode_fused(int32_t fused) {
+  if (fused != 0 && fused != 1) return MOE_EINVAL;
+  g_decode_fused.store(fused);
+  return MOE_OK;
+}
+
 int moe_debug_time_kernel(int32_t which, void* start_event, void* stop_event) {
-  if (which < MOE_KERNEL_GEMV_GATE_UP || which > MOE_KERNEL_GEMM_DOWN) return MOE_EINVAL;
+  if (which < MOE_KERNEL_GEMV_GATE_UP || which > MOE_KERNEL_DECODE_FFN) return MOE_EINVAL;
   if ((start_event == nullptr) != (stop_event == nullptr)) return MOE_EINVAL;
   g_kernel_timer[which].start = (hipEvent_t)start_event;
   g_kernel_timer[which].stop = (hipEvent_t)stop_event;

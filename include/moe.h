@@ -331,13 +331,28 @@ int moe_debug_routing(const moe_weights* w, int32_t T, int32_t k, void* ws, size
                       int32_t** ids, float** topk_w);
 
 /* Kernels that moe_debug_time_kernel can time: the gate+up and the down
- * kernels of the one-token VALU path (GEMV) and of the grouped GEMM. */
+ * kernels of the VALU path (GEMV) and of the grouped GEMM, and the fused
+ * one-token expert kernel (gate+up, down and combine in one launch). */
 enum {
   MOE_KERNEL_GEMV_GATE_UP = 1,
   MOE_KERNEL_GEMM_GATE_UP = 2,
   MOE_KERNEL_GEMV_DOWN = 3,
-  MOE_KERNEL_GEMM_DOWN = 4
+  MOE_KERNEL_GEMM_DOWN = 4,
+  MOE_KERNEL_DECODE_FFN = 5
 };
+
+/* DEBUG/BENCHMARK ONLY -- the one-token path of dsv4_moe_forward with the
+ * router on the device and FP4 weights: `fused` = 1 runs the routed experts'
+ * gate+up, the down projection of all k + 1 experts and the combine as one
+ * persistent kernel wherever it fits (T = 1, k + 1 <= 8, inter <= 2048,
+ * hidden <= 4096 and a multiple of 16 with hidden / 16 <= the device's
+ * compute units), 0 (the default: measured faster) the separate gate+up and
+ * down+combine kernels.  Both give bit-identical outputs.  The fused kernel runs one block per compute unit
+ * and its blocks wait on each other's results (bounded waits): it expects
+ * the device to itself for its duration; when other work holds compute
+ * units, the waits may run out, which sets MOE_STATUS_SYNC_TIMEOUT.
+ * Process-wide and not thread-safe; MOE_EINVAL for other values. */
+int moe_debug_set_decode_fused(int32_t fused);
 
 /* DEBUG/BENCHMARK ONLY -- kernel timing.  While set, every launch of kernel
  * `which` (MOE_KERNEL_*) records `start_event` and `stop_event` (hipEvent_t
