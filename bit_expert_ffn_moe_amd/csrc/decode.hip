@@ -20,9 +20,12 @@
 // down+combine kernels.  Per-block timestamps put the gate+up stream's last
 // waves at 19-23 us (the separate gate+up kernel ends at ~14.5 us) and the
 // exchange chain after it (requantisation, code words, down, combine) at
-// ~7 us; the order of the copies (before or after the gate+up rows) changes
-// nothing.  So the library keeps the separate kernels by default and runs
-// this one only when asked (moe_debug_set_decode_fused).
+// ~7 us.  Neither the order of the copies (before or after the gate+up
+// rows) nor 12 instead of 16 waves per block changed the time; dealing the
+// gate+up rows out to the blocks in 16-row groups, as the separate kernel's
+// blocks get them, made it slower (35 us).  So the library keeps the
+// separate kernels by default and runs this one only when asked
+// (moe_debug_set_decode_fused).
 //
 // The arithmetic is that of the two one-token kernels (gemv.hip) step by
 // step -- the same device functions for the gate+up rows, the same
@@ -60,6 +63,8 @@ namespace bef {
 constexpr int kDecThreads = kDecWaves * 64;
 constexpr int kDecI = 2048;                  // largest intermediate size
 constexpr int kDecCodeWords = 36;            // per 128-block: 32 code words, 1 scale word, pad
+// code words of all routed rows per thread: (kDecMaxRows - 1) x 16 x 33 at most
+constexpr int kDecWordsPerThread = ((kDecMaxRows - 1) * 16 * 33 + kDecThreads - 1) / kDecThreads;
 
 __device__ __forceinline__ uint32_t dec_lds_addr(void* l) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)l);
@@ -186,7 +191,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_ffn_kernel(DecodeArgs a) {
   // ---- all routed code words into LDS; the shared row from the workspace ----
   {
     const int nw = k * I128 * 33;
-    unsigned long long wd[4] = {0, 0, 0, 0};
+    unsigned long long wd[kDecWordsPerThread];
+#pragma unroll
+    for (int q = 0; q < kDecWordsPerThread; ++q) wd[q] = 0;
     const unsigned long long* cw = reinterpret_cast<const unsigned long long*>(a.dec_c);
     auto word_at = [&](int i) {
       const int rc = i / 33, j = i - rc * 33;  // rc = r * I128 + c
@@ -196,7 +203,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_ffn_kernel(DecodeArgs a) {
     for (uint32_t spins = 0;;) {
       bool all = true;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < kDecWordsPerThread; ++q) {
         const int i = tid + q * kDecThreads;
         if (i < nw && (wd[q] & kSlotTagMask) != tag) {
           wd[q] = __hip_atomic_load(word_at(i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -211,7 +218,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_ffn_kernel(DecodeArgs a) {
       __builtin_amdgcn_s_sleep(1);
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kDecWordsPerThread; ++q) {
       const int i = tid + q * kDecThreads;
       if (i < nw) {
         const int rc = i / 33, j = i - rc * 33;
@@ -231,10 +238,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_ffn_kernel(DecodeArgs a) {
   __builtin_amdgcn_s_waitcnt(0);  // this wave's copies into LDS (and everything else)
   __syncthreads();
 
-  // ---- down: wave w < 2R takes h row r = w / 2 and output rows m0 + 8 (w % 2) + 0..7
+  // ---- down: item i < 2R (waves in turn) is h row r = i / 2 and output rows m0 + 8 (i % 2) + 0..7
   // (the per-chunk products and the butterfly of gemv_down_kernel) ----
-  if (wv < 2 * R) {
-    const int r = wv >> 1, i0 = 8 * (wv & 1);
+  for (int it = wv; it < 2 * R; it += kDecWaves) {
+    const int r = it >> 1, i0 = 8 * (it & 1);
     const int ch = min(lane, nch - 1);
     const uint4 a0q = *reinterpret_cast<const uint4*>(&sH[r][32 * ch]);
     const uint4 a1q = *reinterpret_cast<const uint4*>(&sH[r][32 * ch + 16]);

@@ -62,9 +62,9 @@ struct GemmArgs {
 };
 
 // The one-token fused expert kernel (decode.hip): 16 output rows per block
-// (one block per CU), 16 waves, at most 8 h rows (k + 1).
+// (one block per CU), 12 waves, at most 8 h rows (k + 1).
 constexpr int kDecRowsPerBlock = 16;
-constexpr int kDecWaves = 16;
+constexpr int kDecWaves = 12;
 constexpr int kDecMaxRows = 8;
 struct DecodeArgs {
   const uint8_t *gq, *gs, *uq, *us, *dq, *ds;  // FP4 weights [E+1][...]
