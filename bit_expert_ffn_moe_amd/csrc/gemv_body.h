@@ -87,20 +87,24 @@ __device__ __forceinline__ void quant_act_codes(const uint16_t* __restrict__ x_r
 }
 
 // Streams 4 consecutive rows n0.. of group g's gate and up matrices for one
-// activation row through a 2-deep register pipeline: the loads of row i+1
-// are issued after row i's products, which an empty asm statement enforces
-// by passing a zero that depends on row i's sums into row i+1's addresses
-// (without it the compiler hoists every load to the top, and the higher
-// register count costs more than the deeper pipeline gains).  One butterfly
+// activation row through a DEPTH-deep register pipeline: the loads of row
+// i+DEPTH-1 are issued after row i-1's products, which an empty asm
+// statement enforces by passing a zero that depends on those sums into the
+// next row's addresses (without it the compiler hoists every load to the
+// top, and in the gate+up kernel, where many waves share the stream, the
+// higher register count costs more than the deeper pipeline gains).  The
+// front kernel's shared-expert rows, which run beside the router's latency
+// chain with few waves, take DEPTH = 4: all four rows in flight at once
+// (decode step -1%).  One butterfly
 // reduce-scatter then gives every lane one of the 8 totals (4 gate, 4 up),
 // and 4 lanes finish h[n] = silu(g_n) * u_n in parallel (returned in those
 // lanes).
 constexpr int kGuRun = 4;
-template <int NB>
+template <int NB, int DEPTH = 2>
 __device__ __forceinline__ float gate_up_rows(const GUWeights& w, int g, int n0, int lane,
                                               const uint4 (&aq)[NB][2],
                                               const float (&xs_raw)[NB]) {
-  constexpr int RUN = kGuRun, DEPTH = 2;
+  constexpr int RUN = kGuRun;
   const int H = w.H, I = w.I;
   const int nch = H >> 5;
   const size_t rowq = (size_t)(H >> 1), rows_ = (size_t)nch;
@@ -132,8 +136,11 @@ __device__ __forceinline__ float gate_up_rows(const GUWeights& w, int g, int n0,
     psg[SLOT][c] = gsb[(ROW) * rows_ + cs[c] + dep];                                  \
     psu[SLOT][c] = usb[(ROW) * rows_ + cs[c] + dep];                                  \
   }
-  BEF_GU_LOAD(0, 0)
-  // the activations, once the first row is in flight; chunks past the row
+#pragma unroll
+  for (int d = 0; d + 1 < DEPTH; ++d) {
+    BEF_GU_LOAD(d, d)
+  }
+  // the activations, once the first rows are in flight; chunks past the row
   // end get scale 0
   Act16 a0[NB], a1[NB];
   float xsc[NB];
@@ -146,8 +153,8 @@ __device__ __forceinline__ float gate_up_rows(const GUWeights& w, int g, int n0,
   float part[2 * RUN];  // [0..3] gate rows, [4..7] up rows
 #pragma unroll
   for (int i = 0; i < RUN; ++i) {
-    if (i + 1 < RUN) {
-      BEF_GU_LOAD((i + 1) % DEPTH, i + 1)
+    if (i + DEPTH - 1 < RUN) {
+      BEF_GU_LOAD((i + DEPTH - 1) % DEPTH, i + DEPTH - 1)
     }
     const int sl = i % DEPTH;
     float ag = 0.0f, au = 0.0f;
@@ -193,11 +200,11 @@ __device__ __forceinline__ float dot32_fp8(const uint4 w0, const uint4 w1, const
   return acc0 + acc1;
 }
 
-template <int NB>
+template <int NB, int DEPTH = 2>
 __device__ __forceinline__ float gate_up_rows_fp8(const GUWeights8& w, int g, int n0, int lane,
                                                   const uint4 (&aq)[NB][2],
                                                   const float (&xs_raw)[NB]) {
-  constexpr int RUN = kGuRun, DEPTH = 2;
+  constexpr int RUN = kGuRun;
   const int H = w.H, I = w.I;
   const int nch = H >> 5;
   const size_t rowq = (size_t)H;
@@ -224,7 +231,10 @@ __device__ __forceinline__ float gate_up_rows_fp8(const GUWeights8& w, int g, in
     pu[SLOT][c][0] = *reinterpret_cast<const uint4*>(uqb + (ROW) * rowq + co[c] + dep);   \
     pu[SLOT][c][1] = *reinterpret_cast<const uint4*>(uqb + (ROW) * rowq + co[c] + 16 + dep); \
   }
-  BEF_GU8_LOAD(0, 0)
+#pragma unroll
+  for (int d = 0; d + 1 < DEPTH; ++d) {
+    BEF_GU8_LOAD(d, d)
+  }
   Act16 a0[NB], a1[NB];
   float sg[NB], su[NB];
 #pragma unroll
@@ -238,8 +248,8 @@ __device__ __forceinline__ float gate_up_rows_fp8(const GUWeights8& w, int g, in
   float part[2 * RUN];
 #pragma unroll
   for (int i = 0; i < RUN; ++i) {
-    if (i + 1 < RUN) {
-      BEF_GU8_LOAD((i + 1) % DEPTH, i + 1)
+    if (i + DEPTH - 1 < RUN) {
+      BEF_GU8_LOAD((i + DEPTH - 1) % DEPTH, i + DEPTH - 1)
     }
     const int sl = i % DEPTH;
     float ag = 0.0f, au = 0.0f;

@@ -136,11 +136,11 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
       float hv;
       if (FMT == 1) {
         const GUWeights w = {a.sh_gq, a.sh_gs, a.sh_uq, a.sh_us, E, H, a.I};
-        hv = gate_up_rows<NB>(w, E, n0, lane, aq, xsc);
+        hv = gate_up_rows<NB, kGuRun>(w, E, n0, lane, aq, xsc);
       } else {
         const GUWeights8 w = {a.sh_gq, a.sh_uq, reinterpret_cast<const float*>(a.sh_gs),
                               reinterpret_cast<const float*>(a.sh_us), E, H, a.I};
-        hv = gate_up_rows_fp8<NB>(w, E, n0, lane, aq, xsc);
+        hv = gate_up_rows_fp8<NB, kGuRun>(w, E, n0, lane, aq, xsc);
       }
       publish_h(hx, hv, T * k + t, a.I, n0, n0b, tid, lane);
       return;

@@ -21,11 +21,22 @@ from gpu_util import DevLayer, to_host  # noqa: E402
 
 @pytest.mark.parametrize("over", [
     dict(T=1),               # one token: front kernel + VALU GEMV with the h exchange
+    dict(T=1, fused=True),   # one token: front kernel + the fused expert kernel (epoch-tagged words)
     dict(T=3, fmt="fp8"),    # front kernel + VALU GEMV (FP8), 3 tokens
     dict(T=6),               # mid-size router with act_quant, permute, grouped GEMM, combine
     dict(T=40),              # mid-size router with act_quant, permute, grouped GEMM, combine
 ])
 def test_graph_replays_equal_the_eager_forward(over):
+    over = dict(over)
+    fused = over.pop("fused", False)
+    moe.moe_debug_set_decode_fused(1 if fused else 0)
+    try:
+        _replays(over)
+    finally:
+        moe.moe_debug_set_decode_fused(0)
+
+
+def _replays(over):
     L = synth.make_layer("tiny_t8", **over)
     D = DevLayer(L)
     T, H, k = L.wl.T, L.wl.H, L.wl.k
