@@ -210,6 +210,21 @@ def test_debug_h_sink_arguments():
     assert L.moe_debug_store_h(None, 0) == moe.MOE_OK
 
 
+def test_debug_decode_path_switch_and_kernel_ids():
+    L = moe._lib
+    for bad in (-1, 2, 7):
+        assert L.moe_debug_set_decode_fused(bad) == moe.MOE_EINVAL
+    assert L.moe_debug_set_decode_fused(1) == moe.MOE_OK
+    assert L.moe_debug_set_decode_fused(0) == moe.MOE_OK
+    # every kernel id of the timing hook is accepted (clearing), others refused
+    for k in (moe.MOE_KERNEL_GEMV_GATE_UP, moe.MOE_KERNEL_GEMM_GATE_UP, moe.MOE_KERNEL_GEMV_DOWN,
+              moe.MOE_KERNEL_GEMM_DOWN, moe.MOE_KERNEL_DECODE_FFN):
+        assert L.moe_debug_time_kernel(k, None, None) == moe.MOE_OK
+    assert L.moe_debug_time_kernel(0, None, None) == moe.MOE_EINVAL
+    assert L.moe_debug_time_kernel(moe.MOE_KERNEL_DECODE_FFN + 1, None, None) == moe.MOE_EINVAL
+    assert L.moe_debug_time_kernel(moe.MOE_KERNEL_DECODE_FFN, 0x10, None) == moe.MOE_EINVAL
+
+
 def test_noalloc_forward_checks_arguments_and_size_on_host():
     """The allocation-free forward validates like dsv4_moe_forward and
     refuses a call whose workspace need exceeds its static array, before
