@@ -102,7 +102,8 @@ def test_act_quant_encoder_exhaustive_sweep():
                                      (300, 4096, 256, 6), (40, 1024, 100, 16),
                                      (4, 8192, 256, 16), (2, 8192, 200, 11),
                                      (33, 8192, 200, 11), (257, 4096, 256, 6),
-                                     (3, 384, 256, 6), (1024, 4096, 256, 6)])
+                                     (3, 384, 256, 6), (1024, 4096, 256, 6),
+                                     (300, 384, 200, 11), (256, 8192, 100, 16)])
 def test_route_ids_valid_topk(T, H, E, k):
     """The GPU's ids are a top-k of the oracle's logits: equal to the
     oracle's, except between logits within the near-tie band (the kernels
