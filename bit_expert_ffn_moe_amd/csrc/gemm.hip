@@ -34,7 +34,8 @@
 // (global_load_lds_dwordx4), as many stages as fit (at most 6), each waited
 // for explicitly so that the younger stages' loads fly while one is
 // multiplied; the 16-byte chunk positions are XOR-swizzled by row so the
-// MFMA operand reads are conflict-free.
+// MFMA operand reads are conflict-free.  The per-row scales go to rings of
+// their own where they fit (GemmPlan below).
 //
 // The grid is persistent (one block per CU, two for the small FP4 tiles) and
 // XCD-aware: the work items (expert M-tile, N-block), N-blocks of one M-tile
@@ -146,38 +147,71 @@ __device__ __forceinline__ int sw64(int r, int c) { return r * 64 + ((c ^ ((r >>
 constexpr int kTN2 = 256;   // weight rows per tile
 
 // TM = tokens per tile (256, or 128 / 64 when groups are small): wave tile
-// 128 weight rows x TM/4 tokens.  FP4 tiles of at most 128 tokens run two
-// blocks per CU (their registers fit four waves per SIMD and their stages
-// half of the LDS): two independent pipelines, whose barriers do not hold
-// each other up (measured: 32-token verify step -6%, 4096-token FP4 prefill
-// -4%).  The FP8 stages are too large for that.
-constexpr bool gemm_two_per_cu(int fmt, int tm) { return fmt == 1 && tm <= 128; }
+// 128 weight rows x TM/4 tokens.  FP4 tiles of 64 tokens, and the FP4 down
+// tiles of 128, run two blocks per CU (their registers fit four waves per
+// SIMD and their stages half of the LDS): two independent pipelines, whose
+// barriers do not hold each other up (measured: 32-token verify step -6%,
+// 4096-token FP4 prefill -4% when both of its GEMMs ran so).  The FP4
+// gate+up tiles of 128 tokens run one block per CU since the scale rings
+// below, which need the registers of two waves per SIMD (4096-token FP4
+// prefill gate+up -6% against two blocks per CU without them).  The FP8
+// stages are too large for two blocks.
+constexpr bool gemm_two_per_cu(int fmt, int tm, bool gu) {
+  return fmt == 1 && (tm <= 64 || (tm == 128 && !gu));
+}
 
+// Per-tile LDS plan.  Stages: as many as fit in ~156 KB of LDS (~76 KB with
+// two blocks per CU), at most 6.  Scale rings: the scales are tiny next to
+// the codes (4 bytes per weight row or token per K step) but each comes
+// from its own 128-byte line (a row's scales are K/32 bytes, a token's K/32
+// as well), and those lines fell out of L2 between K steps: per-step 4-byte
+// scale loads cost the 4096-token FP4 gate+up's loads about 30% of their
+// time.  With the rings the FP4 weight scales (RW) and the activation scales
+// (RX) leave the stages for two buffers of their own, filled a few K steps
+// ahead with the scales of four K steps per row in one 16-byte load when K
+// is a multiple of 512 (else of one step), so each line is fetched about a
+// quarter as often.  Used where the registers allow (one block per CU) and
+// the rings fit beside the same number of stages.
 template <int FMT, bool GU, int TM>
-__global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void gemm_kernel(
+struct GemmPlan {
+  static constexpr bool kTwo = gemm_two_per_cu(FMT, TM, GU);
+  static constexpr int KB_A = TM * 128;                           // E4M3 activations per K step
+  static constexpr int KB_B = FMT == 1 ? kTN2 * 64 : kTN2 * 128;  // weight codes per K step
+  static constexpr int kStage = KB_A + KB_B + (FMT == 1 ? kTN2 * 4 : 0) + TM * 4;
+  static constexpr int kLdsBudget = kTwo ? 77568 : 159744;
+  static constexpr int NST = (kLdsBudget / kStage) > 6 ? 6 : (kLdsBudget / kStage);
+  static constexpr int kTotalLds = kTwo ? 81920 : 163840;
+  static constexpr int kMisc = 12 * TM + 1576 + 512;  // the kernel's small arrays, and slack
+  static constexpr int kCodes = KB_A + KB_B;
+  static constexpr int kRingW = FMT == 1 ? 2 * kTN2 * 16 : 0, kRingX = 2 * TM * 16;
+  static constexpr bool RX = !kTwo && NST * kCodes + kRingW + kRingX + kMisc <= kTotalLds;
+  static constexpr bool RW =
+      !kTwo && FMT == 1 && (RX || NST * (kCodes + TM * 4) + kRingW + kMisc <= kTotalLds);
+};
+
+template <int FMT, bool GU, int TM, bool SS4>
+__global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM, GU) ? 4 : 2) void gemm_kernel(
     GemmArgs a) {
-  constexpr int NT = TM / 64;                              // token fragments per wave
-  constexpr int KB_A = TM * 128;                           // E4M3 activations per K step
-  constexpr int KB_B = FMT == 1 ? kTN2 * 64 : kTN2 * 128;  // weight codes per K step
-  // stages: as many as fit in ~156 KB of LDS (~76 KB with two blocks per
-  // CU), at most 6
-  constexpr int kStage = KB_A + KB_B + (FMT == 1 ? kTN2 * 4 : 0) + TM * 4;
-  constexpr int kLdsBudget = gemm_two_per_cu(FMT, TM) ? 77568 : 159744;
-  constexpr int NST = (kLdsBudget / kStage) > 6 ? 6 : (kLdsBudget / kStage);
+  using P = GemmPlan<FMT, GU, TM>;
+  constexpr int NT = TM / 64;  // token fragments per wave
+  constexpr int KB_A = P::KB_A, KB_B = P::KB_B, NST = P::NST;
+  constexpr bool RX = P::RX, RW = P::RW;
   static_assert(NST >= 2, "LDS stages");
   constexpr int XL = TM / 8;                               // act-scale DMA lanes per wave
   constexpr int NAI = KB_A / 8192;                         // A DMA instructions per wave
   constexpr int NBI = KB_B / 8192;                         // B DMA instructions per wave
-  constexpr int kLoads = NAI + NBI + (FMT == 1 ? 1 : 0) + 1;  // + FP4 scales + act scales
+  constexpr int kLoads = NAI + NBI + (FMT == 1 && !RW ? 1 : 0) + (RX ? 0 : 1);  // + scales in the stage
   // stage buffers: activation codes, weight codes, FP4 weight scales (4
   // UE8M0 bytes per weight row), activation scales of the K step
 #define BEF_STAGE(i)                                                        \
   __shared__ __align__(16) uint8_t sA##i[NST > i ? KB_A : 16];              \
   __shared__ __align__(16) uint8_t sB##i[NST > i ? KB_B : 16];              \
-  __shared__ __align__(16) uint32_t sS##i[FMT == 1 && NST > i ? kTN2 : 4];  \
-  __shared__ __align__(16) float sX##i[NST > i ? TM : 4];
+  __shared__ __align__(16) uint32_t sS##i[FMT == 1 && !RW && NST > i ? kTN2 : 4]; \
+  __shared__ __align__(16) float sX##i[!RX && NST > i ? TM : 4];
   BEF_STAGE(0) BEF_STAGE(1) BEF_STAGE(2) BEF_STAGE(3) BEF_STAGE(4) BEF_STAGE(5)
 #undef BEF_STAGE
+  __shared__ __align__(16) uint32_t sRW[RW ? 2 * kTN2 * 4 : 4];  // [buffer][row][4 K steps]
+  __shared__ __align__(16) float sRX[RX ? 2 * TM * 4 : 4];       // [buffer][token][4 K steps]
   __shared__ float s_amax[2][TM];
   __shared__ float s_wsc[2][64];  // FP8 weight block scales of the tile, per K step
   __shared__ int s_mtp[258];      // m-tile prefix per group
@@ -319,7 +353,11 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
     // that two N-blocks read a token tile's K steps together (verify_t32 and
     // both prefills: -0.3 to -0.6%).
     const int rot = (s_mtp[g + 1] - s_mtp[g] > 1 ? g * NB + nb : wi) >> 1;
-    const int ks0 = (int)(((uint32_t)rot * 7u) % (uint32_t)KS);
+    // (with four K steps per scale load, the start is rounded down to a
+    // multiple of 4, so that each group of four steps is contiguous in K)
+    constexpr bool ss4 = (RW || RX) && SS4;
+    static_assert(!SS4 || RW || RX, "four-step scale loads only with a ring");
+    const int ks0 = (int)(((uint32_t)rot * 7u) % (uint32_t)KS) & (ss4 ? ~3 : ~0);
     auto kr = [&](int ks) {
       const int k = ks + ks0;
       return k >= KS ? k - KS : k;
@@ -334,8 +372,28 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
         const uint8_t* bb = (GU && (w * NBI + i) * 64 >= 128 * (FMT == 1 ? 4 : 8)) ? baseU : baseG;
         dma16(bb, offB[i] + ks * (FMT == 1 ? 64u : 128u), sB + (w * NBI + i) * 1024);
       }
-      if (FMT == 1 && lane < 32) dma4(baseS, offS + ks * 4u, sS + w * 32);
-      if (lane < XL) dma4((const uint8_t*)baseX, (offX + ks) * 4u, sX + w * XL);
+      if (FMT == 1 && !RW && lane < 32) dma4(baseS, offS + ks * 4u, sS + w * 32);
+      if (!RX && lane < XL) dma4((const uint8_t*)baseX, (offX + ks) * 4u, sX + w * XL);
+    };
+    // the scale rings: the scales of loop steps s .. s+3 (s a multiple of 4)
+    // or of step s alone, into buffer (s/4) mod 2 or s mod 2
+    auto issue_scales = [&](int s_) {
+      const uint32_t k = (uint32_t)kr(s_);
+      const int buf = ss4 ? ((s_ >> 2) & 1) : (s_ & 1);
+      if (RW && lane < 32) {
+        uint32_t* d = sRW + buf * (kTN2 * 4) + (ss4 ? w * 128 : w * 32);
+        if (ss4) dma16(baseS, offS + k * 4u, d);
+        else dma4(baseS, offS + k * 4u, d);
+      }
+      if (RX && lane < XL) {
+        float* d = sRX + buf * (TM * 4) + (ss4 ? w * XL * 4 : w * XL);
+        if (ss4) dma16((const uint8_t*)baseX, (offX + k) * 4u, d);
+        else dma4((const uint8_t*)baseX, (offX + k) * 4u, d);
+      }
+    };
+    // the ring slot of row / token i at loop step ks
+    auto ring_at = [&](int ks, int i, int n) {
+      return ss4 ? ((ks >> 2) & 1) * (n * 4) + i * 4 + (ks & 3) : (ks & 1) * (n * 4) + i;
     };
 
     v4f_t acc[8][NT];
@@ -368,7 +426,7 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
         if (FMT == 1) {
           const uint4 b0 = *reinterpret_cast<const uint4*>(sB + sw64(n, q));
           wv = (v8i_t){(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
-          sw = (int)((sS[n] >> (8 * q)) & 0xffu);
+          sw = (int)(((RW ? sRW[ring_at(ks, n, kTN2)] : sS[n]) >> (8 * q)) & 0xffu);
         } else {
           const uint4 b0 = *reinterpret_cast<const uint4*>(sB + sw128(n, q));
           const uint4 b1 = *reinterpret_cast<const uint4*>(sB + sw128(n, q + 4));
@@ -384,7 +442,8 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
       float cx[NTL], cy[NTL];
 #pragma unroll
       for (int ti = 0; ti < NTL; ++ti) {
-        const float x = sX[wt * 16 * NTL + 16 * ti + (lane & 15)];
+        const int t = wt * 16 * NTL + 16 * ti + (lane & 15);
+        const float x = RX ? sRX[ring_at(ks, t, TM)] : sX[t];
         cx[ti] = x;
         cy[ti] = x;
       }
@@ -465,6 +524,7 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
         default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * kLoads)); break;
       }
     };
+    if (RW || RX) issue_scales(0);
 #pragma unroll
     for (int i = 0; i < NST - 1; ++i) {
       if (i < KS) {
@@ -484,6 +544,13 @@ __global__ __launch_bounds__(kGThreads, gemm_two_per_cu(FMT, TM) ? 4 : 2) void g
         wait_stages(min(NST - 2, KS - 1 - ks));                             \
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);                             \
         block_barrier();                                                    \
+        if (RW || RX) {                                                     \
+          if (ss4) {                                                        \
+            if ((ks & 3) == 1 && ks + 3 < KS) issue_scales(ks + 3);         \
+          } else if (ks + 1 < KS) {                                         \
+            issue_scales(ks + 1);                                           \
+          }                                                                 \
+        }                                                                   \
         if (ks + NST - 1 < KS) {                                            \
           const Stage nx = stage((j + NST - 1) % NST);                      \
           issue(ks + NST - 1, nx.a, nx.b, nx.s, nx.x);                      \
@@ -599,17 +666,28 @@ static int grid_blocks() {
   return g_cu_count[dev];
 }
 
+template <int FMT, bool GU, int TM, bool SS4>
+static hipError_t launch_g4(const GemmArgs& a, hipStream_t st) {
+  const KernelTimer& tm = g_kernel_timer[GU ? MOE_KERNEL_GEMM_GATE_UP : MOE_KERNEL_GEMM_DOWN];
+  const dim3 grid((gemm_two_per_cu(FMT, TM, GU) ? 2 : 1) * grid_blocks());
+  if (tm.start)
+    hipExtLaunchKernelGGL(gemm_kernel<FMT, GU, TM, SS4>, grid, dim3(kGThreads), 0, st, tm.start,
+                          tm.stop, 0, a);
+  else
+    gemm_kernel<FMT, GU, TM, SS4><<<grid, dim3(kGThreads), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+// with scale rings, the contraction length decides their form: four K
+// steps per scale load when it is a multiple of 512
 template <int FMT, bool GU, int TM>
 static hipError_t launch_g(const GemmArgs& a, hipStream_t st) {
   if (a.E + 1 > 257 || (GU ? a.I : a.H) % 128 != 0) return hipErrorInvalidValue;
-  const KernelTimer& tm = g_kernel_timer[GU ? MOE_KERNEL_GEMM_GATE_UP : MOE_KERNEL_GEMM_DOWN];
-  const dim3 grid((gemm_two_per_cu(FMT, TM) ? 2 : 1) * grid_blocks());
-  if (tm.start)
-    hipExtLaunchKernelGGL(gemm_kernel<FMT, GU, TM>, grid, dim3(kGThreads), 0, st, tm.start,
-                          tm.stop, 0, a);
-  else
-    gemm_kernel<FMT, GU, TM><<<grid, dim3(kGThreads), 0, st>>>(a);
-  return hipGetLastError();
+  using P = GemmPlan<FMT, GU, TM>;
+  if constexpr (P::RW || P::RX) {
+    if ((GU ? a.H : a.I) % 512 == 0) return launch_g4<FMT, GU, TM, true>(a, st);
+  }
+  return launch_g4<FMT, GU, TM, false>(a, st);
 }
 
 // Token tile by the routed groups' average size: 256 from 128 rows (each

@@ -86,7 +86,15 @@ def _run(name, sample=None, threads=0, **over):
                                   dict(E=1, k=1, T=9), dict(E=3, k=3, T=17),
                                   dict(T=3, H=384), dict(T=3, H=384, fmt="fp8"),
                                   dict(T=5, H=384), dict(T=5, H=384, fmt="fp8"),
-                                  dict(T=1, H=384), dict(T=40, H=640, fmt="fp8")])
+                                  dict(T=1, H=384), dict(T=40, H=640, fmt="fp8"),
+                                  # scale rings: one K step per scale load (K not a multiple
+                                  # of 512) in 128- and 256-token tiles, and a single group of
+                                  # four steps (K = 512)
+                                  dict(T=130, routing="zipf", zipf_s=1.0, fmt="fp8", H=384),
+                                  dict(T=520, fmt="fp8", H=640),
+                                  dict(T=130, routing="zipf", zipf_s=1.0, H=512),
+                                  dict(T=130, routing="zipf", zipf_s=1.0, fmt="fp8", H=512,
+                                       I=512)])
 def test_tiny_layer(over):
     _run("tiny_t8", **over)
 
