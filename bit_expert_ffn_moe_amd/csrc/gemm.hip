@@ -170,8 +170,11 @@ constexpr bool gemm_two_per_cu(int fmt, int tm, bool gu) {
 // (RX) leave the stages for two buffers of their own, filled a few K steps
 // ahead with the scales of four K steps per row in one 16-byte load when K
 // is a multiple of 512 (else of one step), so each line is fetched about a
-// quarter as often.  Used where the registers allow (one block per CU) and
-// the rings fit beside the same number of stages.
+// quarter as often.  Used where the registers allow: at one block per CU
+// where the rings fit beside the same number of stages, and for the 64-token
+// FP4 tiles at two blocks per CU with two stages instead of three
+// (32-token verify: gate+up -14%, down -11%); the 128-token FP4 down tiles at
+// two blocks per CU have no registers left for the ring reads.
 template <int FMT, bool GU, int TM>
 struct GemmPlan {
   static constexpr bool kTwo = gemm_two_per_cu(FMT, TM, GU);
@@ -179,14 +182,16 @@ struct GemmPlan {
   static constexpr int KB_B = FMT == 1 ? kTN2 * 64 : kTN2 * 128;  // weight codes per K step
   static constexpr int kStage = KB_A + KB_B + (FMT == 1 ? kTN2 * 4 : 0) + TM * 4;
   static constexpr int kLdsBudget = kTwo ? 77568 : 159744;
-  static constexpr int NST = (kLdsBudget / kStage) > 6 ? 6 : (kLdsBudget / kStage);
+  static constexpr int NST0 = (kLdsBudget / kStage) > 6 ? 6 : (kLdsBudget / kStage);
   static constexpr int kTotalLds = kTwo ? 81920 : 163840;
   static constexpr int kMisc = 12 * TM + 1576 + 512;  // the kernel's small arrays, and slack
   static constexpr int kCodes = KB_A + KB_B;
   static constexpr int kRingW = FMT == 1 ? 2 * kTN2 * 16 : 0, kRingX = 2 * TM * 16;
-  static constexpr bool RX = !kTwo && NST * kCodes + kRingW + kRingX + kMisc <= kTotalLds;
-  static constexpr bool RW =
-      !kTwo && FMT == 1 && (RX || NST * (kCodes + TM * 4) + kRingW + kMisc <= kTotalLds);
+  static constexpr int NSTR0 = (kTotalLds - kRingW - kRingX - kMisc) / kCodes;
+  static constexpr int NSTR = NSTR0 < NST0 ? NSTR0 : NST0;  // stages beside the rings
+  static constexpr bool kRings = (!kTwo || TM == 64) && NSTR >= 2 && (NSTR == NST0 || kTwo);
+  static constexpr bool RX = kRings, RW = kRings && FMT == 1;
+  static constexpr int NST = kRings ? NSTR : NST0;
 };
 
 template <int FMT, bool GU, int TM, bool SS4>
