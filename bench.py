@@ -256,6 +256,11 @@ def time_kernel(B, which, n_ev):
     import numpy as np
     import torch
     evs = [(B.hip.event(), B.hip.event()) for _ in range(n_ev)]
+    # a bounded spin on the stream first (~20 ms), so that the steps are all
+    # queued before the GPU reaches them and run back to back as in the graph
+    # replays, instead of trailing the host's launches
+    with torch.cuda.stream(B.stream):
+        torch.cuda._sleep(50_000_000)
     for i in range(n_ev):
         B.moe.moe_debug_time_kernel(which, evs[i][0], evs[i][1])
         B.product_step(i)
