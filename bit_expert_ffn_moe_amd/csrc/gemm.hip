@@ -171,10 +171,12 @@ constexpr bool gemm_two_per_cu(int fmt, int tm, bool gu) {
 // ahead with the scales of four K steps per row in one 16-byte load when K
 // is a multiple of 512 (else of one step), so each line is fetched about a
 // quarter as often.  Used where the registers allow: at one block per CU
-// where the rings fit beside the same number of stages, and for the 64-token
-// FP4 tiles at two blocks per CU with two stages instead of three
-// (32-token verify: gate+up -14%, down -11%); the 128-token FP4 down tiles at
-// two blocks per CU have no registers left for the ring reads.
+// where the rings fit beside the same number of stages, and at two blocks
+// per CU for the 64-token FP4 tiles (two stages instead of three; 32-token
+// verify: gate+up -14%, down -11%) and the 128-token FP4 down tiles
+// (4096-token FP4 prefill down -7%).  The 128-token FP4 gate+up tiles at two
+// blocks per CU spilled address registers inside the K loop with them (hence
+// one block per CU for those).
 template <int FMT, bool GU, int TM>
 struct GemmPlan {
   static constexpr bool kTwo = gemm_two_per_cu(FMT, TM, GU);
@@ -189,7 +191,7 @@ struct GemmPlan {
   static constexpr int kRingW = FMT == 1 ? 2 * kTN2 * 16 : 0, kRingX = 2 * TM * 16;
   static constexpr int NSTR0 = (kTotalLds - kRingW - kRingX - kMisc) / kCodes;
   static constexpr int NSTR = NSTR0 < NST0 ? NSTR0 : NST0;  // stages beside the rings
-  static constexpr bool kRings = (!kTwo || TM == 64) && NSTR >= 2 && (NSTR == NST0 || kTwo);
+  static constexpr bool kRings = (!kTwo || TM == 64 || !GU) && NSTR >= 2 && (NSTR == NST0 || kTwo);
   static constexpr bool RX = kRings, RW = kRings && FMT == 1;
   static constexpr int NST = kRings ? NSTR : NST0;
 };
