@@ -243,12 +243,6 @@ __device__ __forceinline__ float butterfly32(const float (&v)[32]) {
   return e;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
-}
-
 // Max over aligned groups of G lanes (G = 2, 4, 8, 16, 32 or 64), in every
 // lane of the group: DPP inside rows of 16 (quad_perm [1,0,3,2], quad_perm
 // [2,3,0,1], row_half_mirror, row_mirror -- each pairs the halves of the

@@ -86,7 +86,7 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ z, int E, in
   }
   const float my_z = (lane < k) ? z[my_id] : 0.0f;
   const float sg = (lane < k) ? 1.0f / (1.0f + expf(-my_z)) : 0.0f;
-  const float sum = wave_sum(sg);
+  const float sum = wave_sum_dpp(sg);
   if (lane < k) {
     ids_out[lane] = my_id;
     w_out[lane] = sg / sum;
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(256) void route_front_kernel(FrontArgs a) {
     const int id = (lane < P) ? s_ids[lane] : 0x7fffffff;
     int rank = 0;
     for (int qq = 0; qq < P; ++qq) {
-      const int iq = s_ids[qq];
+      const int iq = __builtin_amdgcn_readlane(id, qq);  // P <= 64: the pairs are lanes
       rank += (iq < id) | ((iq == id) & (qq < lane));
     }
     if (lane < P) {
