@@ -59,17 +59,18 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
   const int n0b = (blockIdx.x - slot * bpg) * 4 * RUN;
   const int n0 = n0b + wv * RUN;
   for (int r = r0; r < r1; ++r) {
-    const int t = row_token[r];
-    uint4 aq[NB][2];
-    float xsc[NB];
-    load_act_codes<NB>(xq + (size_t)t * w.H, xs + (size_t)t * (w.H >> 7), w.H, lane, aq, xsc);
+    // the row's token is looked up once its first weight rows are in flight
+    auto acts = [&](uint4 (&aq)[NB][2], float (&xsc)[NB]) {
+      const int t = row_token[r];
+      load_act_codes<NB>(xq + (size_t)t * w.H, xs + (size_t)t * (w.H >> 7), w.H, lane, aq, xsc);
+    };
     float hv;
     if (FMT == 1) {
-      hv = gate_up_rows<NB>(w, g, n0, lane, aq, xsc);
+      hv = gate_up_rows<NB>(w, g, n0, lane, acts);
     } else {
       const GUWeights8 w8 = {w.gq, w.uq, reinterpret_cast<const float*>(w.gs),
                              reinterpret_cast<const float*>(w.us), w.E, w.H, w.I};
-      hv = gate_up_rows_fp8<NB>(w8, g, n0, lane, aq, xsc);
+      hv = gate_up_rows_fp8<NB>(w8, g, n0, lane, acts);
     }
     publish_h(hx, hv, r, w.I, n0, n0b, tid, lane);
   }

@@ -87,7 +87,9 @@ __device__ __forceinline__ void quant_act_codes(const uint16_t* __restrict__ x_r
 }
 
 // Streams 4 consecutive rows n0.. of group g's gate and up matrices for one
-// activation row through a DEPTH-deep register pipeline: the loads of row
+// activation row, whose codes and scales acts(aq, xs) loads once the first
+// weight rows are in flight (so a lookup of the row's token does not delay
+// the weight stream), through a DEPTH-deep register pipeline: the loads of row
 // i+DEPTH-1 are issued after row i-1's products, which an empty asm
 // statement enforces by passing a zero that depends on those sums into the
 // next row's addresses (without it the compiler hoists every load to the
@@ -100,10 +102,9 @@ __device__ __forceinline__ void quant_act_codes(const uint16_t* __restrict__ x_r
 // and 4 lanes finish h[n] = silu(g_n) * u_n in parallel (returned in those
 // lanes).
 constexpr int kGuRun = 4;
-template <int NB, int DEPTH = 2>
+template <int NB, int DEPTH = 2, class Acts>
 __device__ __forceinline__ float gate_up_rows(const GUWeights& w, int g, int n0, int lane,
-                                              const uint4 (&aq)[NB][2],
-                                              const float (&xs_raw)[NB]) {
+                                              Acts&& acts) {
   constexpr int RUN = kGuRun;
   const int H = w.H, I = w.I;
   const int nch = H >> 5;
@@ -140,21 +141,30 @@ __device__ __forceinline__ float gate_up_rows(const GUWeights& w, int g, int n0,
   for (int d = 0; d + 1 < DEPTH; ++d) {
     BEF_GU_LOAD(d, d)
   }
-  // the activations, once the first rows are in flight; chunks past the row
-  // end get scale 0
+  // the activation loads, once the first rows are in flight (the compiler
+  // barrier keeps acts' loads, and any lookup they wait for, behind them)
+  uint4 aq[NB][2];
+  float xs_raw[NB];
+  asm volatile("" ::: "memory");
+  acts(aq, xs_raw);
   Act16 a0[NB], a1[NB];
   float xsc[NB];
-#pragma unroll
-  for (int c = 0; c < NB; ++c) {
-    e4m3x16_to_h2(aq[c][0], a0[c]);
-    e4m3x16_to_h2(aq[c][1], a1[c]);
-    xsc[c] = (lane + 64 * c < nch) ? xs_raw[c] : 0.0f;
-  }
   float part[2 * RUN];  // [0..3] gate rows, [4..7] up rows
 #pragma unroll
   for (int i = 0; i < RUN; ++i) {
     if (i + DEPTH - 1 < RUN) {
       BEF_GU_LOAD((i + DEPTH - 1) % DEPTH, i + DEPTH - 1)
+    }
+    if (i == 0) {
+      // converted after the next row's loads are issued (the wait for the
+      // activations then leaves them in flight); chunks past the row end get
+      // scale 0
+#pragma unroll
+      for (int c = 0; c < NB; ++c) {
+        e4m3x16_to_h2(aq[c][0], a0[c]);
+        e4m3x16_to_h2(aq[c][1], a1[c]);
+        xsc[c] = (lane + 64 * c < nch) ? xs_raw[c] : 0.0f;
+      }
     }
     const int sl = i % DEPTH;
     float ag = 0.0f, au = 0.0f;
@@ -200,10 +210,9 @@ __device__ __forceinline__ float dot32_fp8(const uint4 w0, const uint4 w1, const
   return acc0 + acc1;
 }
 
-template <int NB, int DEPTH = 2>
+template <int NB, int DEPTH = 2, class Acts>
 __device__ __forceinline__ float gate_up_rows_fp8(const GUWeights8& w, int g, int n0, int lane,
-                                                  const uint4 (&aq)[NB][2],
-                                                  const float (&xs_raw)[NB]) {
+                                                  Acts&& acts) {
   constexpr int RUN = kGuRun;
   const int H = w.H, I = w.I;
   const int nch = H >> 5;
@@ -235,21 +244,27 @@ __device__ __forceinline__ float gate_up_rows_fp8(const GUWeights8& w, int g, in
   for (int d = 0; d + 1 < DEPTH; ++d) {
     BEF_GU8_LOAD(d, d)
   }
+  uint4 aq[NB][2];
+  float xs_raw[NB];
+  asm volatile("" ::: "memory");
+  acts(aq, xs_raw);
   Act16 a0[NB], a1[NB];
   float sg[NB], su[NB];
-#pragma unroll
-  for (int c = 0; c < NB; ++c) {
-    e4m3x16_to_h2(aq[c][0], a0[c]);
-    e4m3x16_to_h2(aq[c][1], a1[c]);
-    const float xsc = (lane + 64 * c < nch) ? xs_raw[c] : 0.0f;
-    sg[c] = xsc * wsg[c];
-    su[c] = xsc * wsu[c];
-  }
   float part[2 * RUN];
 #pragma unroll
   for (int i = 0; i < RUN; ++i) {
     if (i + DEPTH - 1 < RUN) {
       BEF_GU8_LOAD((i + DEPTH - 1) % DEPTH, i + DEPTH - 1)
+    }
+    if (i == 0) {
+#pragma unroll
+      for (int c = 0; c < NB; ++c) {
+        e4m3x16_to_h2(aq[c][0], a0[c]);
+        e4m3x16_to_h2(aq[c][1], a1[c]);
+        const float xsc = (lane + 64 * c < nch) ? xs_raw[c] : 0.0f;
+        sg[c] = xsc * wsg[c];
+        su[c] = xsc * wsu[c];
+      }
     }
     const int sl = i % DEPTH;
     float ag = 0.0f, au = 0.0f;
@@ -266,6 +281,29 @@ __device__ __forceinline__ float gate_up_rows_fp8(const GUWeights8& w, int g, in
   const float tot = butterfly8(part);
   const float up = xchg32(tot);
   return silu_mul_accurate(tot, up);
+}
+
+// The same with the activation codes and scales already in registers.
+template <int NB>
+struct ActRegs {
+  const uint4 (&aq)[NB][2];
+  const float (&xs)[NB];
+  __device__ __forceinline__ void operator()(uint4 (&q)[NB][2], float (&s)[NB]) const {
+#pragma unroll
+    for (int c = 0; c < NB; ++c) q[c][0] = aq[c][0], q[c][1] = aq[c][1], s[c] = xs[c];
+  }
+};
+template <int NB, int DEPTH = 2>
+__device__ __forceinline__ float gate_up_rows(const GUWeights& w, int g, int n0, int lane,
+                                              const uint4 (&aq)[NB][2],
+                                              const float (&xs_raw)[NB]) {
+  return gate_up_rows<NB, DEPTH>(w, g, n0, lane, ActRegs<NB>{aq, xs_raw});
+}
+template <int NB, int DEPTH = 2>
+__device__ __forceinline__ float gate_up_rows_fp8(const GUWeights8& w, int g, int n0, int lane,
+                                                  const uint4 (&aq)[NB][2],
+                                                  const float (&xs_raw)[NB]) {
+  return gate_up_rows_fp8<NB, DEPTH>(w, g, n0, lane, ActRegs<NB>{aq, xs_raw});
 }
 
 // The lanes that hold a finished h value after gate_up_rows (bit 5 = 0 and
