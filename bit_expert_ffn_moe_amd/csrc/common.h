@@ -19,12 +19,41 @@ typedef __attribute__((address_space(1))) void* glb_ptr_t;
 
 // s_waitcnt immediates (gfx9: vmcnt [3:0] + [15:14], expcnt [6:4], lgkmcnt [11:8])
 constexpr int waitcnt_vm(int n) { return 0xF70 | (n & 0xF) | ((n >> 4) << 14); }
+// s_waitcnt immediate of lgkmcnt(0) (vmcnt and expcnt left at their maxima)
+constexpr int kWaitLgkm0 = 0xC07F;
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v4f_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+
+// Workgroup barrier that is also a compiler barrier for memory accesses: the
+// s_barrier builtin is modelled as touching no memory, so LDS reads could be
+// moved across it; an asm statement with a memory clobber cannot be.  (It
+// waits for nothing: the callers wait for their own loads explicitly.)
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Direct global->LDS loads of 16 or 4 bytes per lane: global address base +
+// voff (base wave-uniform), LDS address M0 + size x lane, with M0 the
+// wave-uniform LDS base l.  Written as asm statements (no register output,
+// LDS written, hence the memory clobber): the compiler's tracking of the
+// builtin form marks the LDS counter out of order, so every later LDS read
+// then waits for all outstanding ones (lgkmcnt(0)) and the first MFMA of a
+// K step waits for all of the step's operand reads.  Unseen by the compiler,
+// these loads are waited for explicitly (vmcnt before the barrier that precedes
+// the first LDS read of the copied data).
+__device__ __forceinline__ uint32_t lds_addr(void* l) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)l);
+}
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, void* l) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr(l))
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const uint8_t* base, uint32_t voff, void* l) {
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr(l))
+               : "memory");
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 

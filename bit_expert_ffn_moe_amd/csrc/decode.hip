@@ -66,18 +66,6 @@ constexpr int kDecCodeWords = 36;            // per 128-block: 32 code words, 1 
 // code words of all routed rows per thread: (kDecMaxRows - 1) x 16 x 33 at most
 constexpr int kDecWordsPerThread = ((kDecMaxRows - 1) * 16 * 33 + kDecThreads - 1) / kDecThreads;
 
-__device__ __forceinline__ uint32_t dec_lds_addr(void* l) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)l);
-}
-// Direct global->LDS load of 16 bytes per lane: global base (wave-uniform)
-// + voff, LDS M0 + 16 x lane.  An asm statement: the compiler does not track
-// it, so the loads are waited for explicitly (vmcnt(0) before the barrier
-// that precedes the first LDS read of the copied rows).
-__device__ __forceinline__ void dec_dma16(const uint8_t* base, uint32_t voff, void* l) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(dec_lds_addr(l))
-               : "memory");
-}
-
 template <int NB>
 __global__ __launch_bounds__(kDecThreads) void decode_ffn_kernel(DecodeArgs a) {
   // LDS: W_down rows of the block (codes, then UE8M0 scales) per h row, the
@@ -177,10 +165,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_ffn_kernel(DecodeArgs a) {
       const int g = __builtin_amdgcn_readfirstlane(sG[r]);
       if (j + 1 < per_row) {
         const uint8_t* src = a.dq + ((size_t)g * H + m0) * (size_t)(I >> 1);
-        dec_dma16(src, (uint32_t)(1024 * j + 16 * lane), &sW[r][1024 * j]);
+        dma16(src, (uint32_t)(1024 * j + 16 * lane), &sW[r][1024 * j]);
       } else {
         const uint8_t* src = a.ds + ((size_t)g * H + m0) * (size_t)(I >> 5);
-        dec_dma16(src, (uint32_t)min(16 * lane, sb - 16), &sS[r][0]);
+        dma16(src, (uint32_t)min(16 * lane, sb - 16), &sS[r][0]);
       }
     }
   }

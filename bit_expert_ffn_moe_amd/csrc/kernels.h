@@ -10,6 +10,7 @@ namespace bef {
 constexpr int kRouteSmallT = 4;           // router: per-chunk blocks + last-block top-k
 constexpr int kRouteMaxGroups = 32;       // router: 256-row groups, H <= 8192
 constexpr int kRouteSplitT = 256;         // router: experts also split in quarters below this T
+constexpr int kRouteMfmaRows = 512;       // router from kRouteSplitT tokens: rows per group sum
 constexpr int kPermuteSmallPairs = 2048;  // permute: single block up to this many pairs
 constexpr int kPermuteTokBlock = 256;     // permute: tokens per block above that
 constexpr int kGemvMaxRows = 8;           // VALU GEMV path: rows (k + 1) per token
@@ -127,14 +128,16 @@ hipError_t launch_route_front(const FrontArgs& a, hipStream_t st);
 
 hipError_t launch_act_quant(const void* x, bool bf16, int64_t rows, int32_t cols, uint8_t* q,
                             float* s, hipStream_t st);
-// T > kRouteSmallT needs gsum: (H/256) * T * E floats of workspace (group sums).
+// T > kRouteSmallT needs gsum: (H/256) * T * E floats of workspace (group sums;
+// from kRouteSplitT tokens on, H/kRouteMfmaRows of them are used), and from
+// kRouteSplitT tokens on wrT: E * H bf16 (the router matrix transposed).
 // xq/xs set: the act_quant of x runs in the same launch (T > kRouteSmallT) or
 // in the front kernel (T <= kRouteSmallT).
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int H, int E, int k,
-                        int32_t* ids, float* w, WsCtl* ctl, float* gsum, hipStream_t st,
-                        uint8_t* xq = nullptr, float* xs = nullptr);
+                        int32_t* ids, float* w, WsCtl* ctl, float* gsum, uint16_t* wrT,
+                        hipStream_t st, uint8_t* xq = nullptr, float* xs = nullptr);
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
-                          int32_t* row_token, int32_t* row_of, int32_t* cnt, int32_t* base,
+                          int32_t* row_token, int32_t* row_of, int32_t* cnt,
                           uint32_t* status, hipStream_t st);
 hipError_t launch_combine(const float* y, const int32_t* row_of, const float* topk_w, int T, int k,
                           int H, void* out, bool bf16, hipStream_t st);

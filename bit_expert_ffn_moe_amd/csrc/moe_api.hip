@@ -65,8 +65,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // layer call: control | permute scratch (T, E) | router partials (T, H, E) |
 // everything else (needs the weights' shapes).
 struct Layout {
-  size_t ctl, cnt, base, gsum, ids, w, xq, xs, offsets, row_token, row_of, active, h, hq, hs, y,
-      total;
+  size_t ctl, cnt, gsum, wrT, ids, w, xq, xs, offsets, row_token, row_of, active, h, hq, hs,
+      y, total;
   size_t end_permute, end_route, end_ffn;
 };
 
@@ -90,12 +90,13 @@ Layout layout_for(int E, int H, int I, int T, int k, bool with_h) {
   o += up(kCtlBytes);
   L.cnt = o;
   o += up(nblk * E * 4);
-  L.base = o;
-  o += up(nblk * E * 4);
   L.end_permute = o;
   // router group sums for T > kRouteSmallT: [ceil(H/256)][T][E] f32
   L.gsum = o;
   if (T > kRouteSmallT) o += up((size_t)((H / 64 + 3) / 4) * T * E * 4);
+  // the router matrix transposed, [E][H] bf16, from kRouteSplitT tokens on
+  L.wrT = o;
+  if (T >= kRouteSplitT) o += up((size_t)E * H * 2);
   L.end_route = o;
   L.ids = o;
   o += up((size_t)T * k * 4);
@@ -330,7 +331,7 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, int32_t T, int32_t H,
   WsCtl* ctl = at<WsCtl>(ws, L.ctl);
   return launch_status(
       launch_route(x, w_router, T, H, E, k, topk_ids, topk_w, ctl, at<float>(ws, L.gsum),
-                   (hipStream_t)stream));
+                   at<uint16_t>(ws, L.wrT), (hipStream_t)stream));
 }
 
 int act_quant_fp8(const void* x, int32_t x_dtype, int64_t rows, int32_t cols, uint8_t* q,
@@ -362,8 +363,8 @@ int moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_
   if (rc) return rc;
   WsCtl* ctl = at<WsCtl>(ws, L.ctl);
   return launch_status(launch_permute(topk_ids, T, k, E, offsets, row_token, row_of,
-                                      at<int32_t>(ws, L.cnt), at<int32_t>(ws, L.base),
-                                      &ctl->status, (hipStream_t)stream));
+                                      at<int32_t>(ws, L.cnt), &ctl->status,
+                                      (hipStream_t)stream));
 }
 
 int moe_expert_ffn(const moe_weights* w, const uint8_t* xq, const float* xs, int32_t T, int32_t k,
@@ -558,7 +559,7 @@ int enqueue_forward(const moe_weights* w, const uint16_t* w_router, const uint16
     int32_t* ids_ws = at<int32_t>(ws, L.ids);
     float* w_ws = at<float>(ws, L.w);
     rc = launch_status(launch_route(x, w_router, T, H, E, k, ids_ws, w_ws, ctl,
-                                    at<float>(ws, L.gsum), st, xq, xs));
+                                    at<float>(ws, L.gsum), at<uint16_t>(ws, L.wrT), st, xq, xs));
     if (rc) return rc;
     ids = ids_ws;
     tw = w_ws;
@@ -567,8 +568,7 @@ int enqueue_forward(const moe_weights* w, const uint16_t* w_router, const uint16
     if (rc) return rc;
   }
   rc = launch_status(launch_permute(ids, T, k, E, offsets, row_token, row_of,
-                                    at<int32_t>(ws, L.cnt), at<int32_t>(ws, L.base),
-                                    &ctl->status, st));
+                                    at<int32_t>(ws, L.cnt), &ctl->status, st));
   if (rc) return rc;
   rc = enqueue_gate_up(w, xq, xs, T, k, offsets, row_token, L, ws, st);
   if (rc) return rc;
@@ -758,7 +758,7 @@ int moe_forward_host_experts(const moe_weights* host_w, const moe_weights* slot_
   float* xs = at<float>(ws, L.xs);
   // 1. the router (with the act_quant of x) on the GPU; the ids to the host
   rc = launch_status(launch_route(x, w_router, T, H, E, k, ids_dev, tw_dev, ctl,
-                                  at<float>(ws, L.gsum), st, xq, xs));
+                                  at<float>(ws, L.gsum), at<uint16_t>(ws, L.wrT), st, xq, xs));
   if (rc) return rc;
   int32_t* h_ids = (int32_t*)host_scratch;
   int32_t* h_slot_ids = (int32_t*)((uint8_t*)host_scratch + up((size_t)T * k * 4));
@@ -840,8 +840,7 @@ int moe_forward_host_experts(const moe_weights* host_w, const moe_weights* slot_
   int32_t* row_of = at<int32_t>(ws, L.row_of);
   float* y = at<float>(ws, L.y);
   rc = launch_status(launch_permute(slot_ids, T, k, NS, offsets, row_token, row_of,
-                                    at<int32_t>(ws, L.cnt), at<int32_t>(ws, L.base),
-                                    &ctl->status, st));
+                                    at<int32_t>(ws, L.cnt), &ctl->status, st));
   if (rc) return rc;
   rc = enqueue_gate_up(slot_w, xq, xs, T, k, offsets, row_token, L, ws, st, masks);
   if (rc) return rc;

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void permute_small_kernel(
   }
 }
 
-// Large T: three passes over token blocks of kPermuteTokBlock tokens.
+// Large T: two passes over token blocks of kPermuteTokBlock tokens.
 // Pass 1: per-block counts cnt[b][e] (LDS atomics).
 __global__ __launch_bounds__(256) void permute_count_kernel(const int32_t* __restrict__ ids,
                                                             int T, int k, int E,
@@ -138,45 +138,46 @@ __global__ __launch_bounds__(256) void permute_count_kernel(const int32_t* __res
   if (tid < E) cnt[(size_t)b * E + tid] = s_cnt[tid];
 }
 
-// Pass 2 (one block): running sums over blocks per expert, scan over experts.
-// base[b][e] = offsets[e] + sum_{b' < b} cnt[b'][e].
-__global__ __launch_bounds__(256) void permute_scan_kernel(int nblk, int T, int E,
-                                                           const int32_t* __restrict__ cnt,
-                                                           int32_t* __restrict__ base,
-                                                           int32_t* __restrict__ offsets) {
-  __shared__ int stmp[8];
-  const int e = threadIdx.x;
-  int tot = 0;
-  if (e < E)
-    for (int b = 0; b < nblk; ++b) tot += cnt[(size_t)b * E + e];
-  int total;
-  const int pre = block256_exclusive_scan(e < E ? tot : 0, stmp, &total);
-  if (e < E) {
-    offsets[e] = pre;
-    int run = pre;
-    for (int b = 0; b < nblk; ++b) {
-      base[(size_t)b * E + e] = run;
-      run += cnt[(size_t)b * E + e];
-    }
-  }
-  if (e == 0) {
-    offsets[E] = total;
-    offsets[E + 1] = total + T;
-  }
-}
-
-// Pass 3: the block's pairs get their rows chunk by chunk.
+// Pass 2: block b forms its experts' bases from the counts of every block
+// -- tot[e] = sum over all blocks, base[e] = offsets[e] + sum over blocks
+// before b, with offsets the exclusive scan of tot over experts (block 0
+// writes it) -- then its pairs get their rows chunk by chunk.
 __global__ __launch_bounds__(256) void permute_scatter_kernel(
-    const int32_t* __restrict__ ids, int T, int k, int E, const int32_t* __restrict__ base,
-    const int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
-    int32_t* __restrict__ row_of) {
+    const int32_t* __restrict__ ids, int T, int k, int E, int nblk,
+    const int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ row_of) {
   __shared__ int s_base[256], s_run[256], s_hist[4][256];
+  __shared__ int stmp[8];
   const int b = blockIdx.x;
   const int t0 = b * kPermuteTokBlock;
   const int nt = min(kPermuteTokBlock, T - t0);
   const int P = nt * k;
   const int tid = threadIdx.x;
-  s_base[tid] = tid < E ? base[(size_t)b * E + tid] : 0;
+  int before = 0, tot = 0;
+  if (tid < E) {
+    // 8 counts in flight at a time
+    for (int b0 = 0; b0 < nblk; b0 += 8) {
+      int c[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        c[j] = (b0 + j < nblk) ? cnt[(size_t)(b0 + j) * E + tid] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        tot += c[j];
+        before += (b0 + j < b) ? c[j] : 0;
+      }
+    }
+  }
+  int total;
+  const int pre = block256_exclusive_scan(tid < E ? tot : 0, stmp, &total);
+  s_base[tid] = tid < E ? pre + before : 0;
+  if (b == 0) {
+    if (tid < E) offsets[tid] = pre;
+    if (tid == 0) {
+      offsets[E] = total;
+      offsets[E + 1] = total + T;
+    }
+  }
   clear_rank_state(s_run, s_hist);
   __syncthreads();
   for (int c0 = 0; c0 < P; c0 += 256) {
@@ -190,16 +191,15 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
       row_of[(size_t)t * (k + 1) + (p % k)] = row;
     }
   }
-  const int shared0 = offsets[E];
   for (int i = tid; i < nt; i += 256) {
     const int t = t0 + i;
-    row_token[shared0 + t] = t;
-    row_of[(size_t)t * (k + 1) + k] = shared0 + t;
+    row_token[total + t] = t;
+    row_of[(size_t)t * (k + 1) + k] = total + t;
   }
 }
 
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
-                          int32_t* row_token, int32_t* row_of, int32_t* cnt, int32_t* base,
+                          int32_t* row_token, int32_t* row_of, int32_t* cnt,
                           uint32_t* status, hipStream_t st) {
   if (E < 1 || E > 256 || k < 1) return hipErrorInvalidValue;  // one thread per expert
   if ((int64_t)T * k <= kPermuteSmallPairs) {
@@ -208,8 +208,8 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offs
   }
   const int nblk = (T + kPermuteTokBlock - 1) / kPermuteTokBlock;
   permute_count_kernel<<<nblk, 256, 0, st>>>(ids, T, k, E, cnt, row_of, status);
-  permute_scan_kernel<<<1, 256, 0, st>>>(nblk, T, E, cnt, base, offsets);
-  permute_scatter_kernel<<<nblk, 256, 0, st>>>(ids, T, k, E, base, offsets, row_token, row_of);
+  permute_scatter_kernel<<<nblk, 256, 0, st>>>(ids, T, k, E, nblk, cnt, offsets, row_token,
+                                              row_of);
   return hipGetLastError();
 }
 

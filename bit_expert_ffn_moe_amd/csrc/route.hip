@@ -328,89 +328,136 @@ struct ActQuantArgs {
 
 // ---------------------------------------------------------------------------
 // T > 4, in two kernels: the group sums G[g][t][e] over rows 256 g .. 256 g +
-// 255 (route_group_mfma_kernel from kRouteSplitT tokens on, else
-// route_group_quarter_kernel), then route_reduce_kernel: a block per 4
-// tokens adds the group sums in ascending group order (thread e owns expert
-// e) and one wave per token runs the top-k.  Splitting over H keeps the GPU
-// busy at moderate T.
+// 255 (route_group_quarter_kernel) or, from kRouteSplitT tokens on, over
+// rows 512 g .. 512 g + 511 (route_group_mfma_kernel, after the router
+// matrix is transposed), then
+// route_reduce_kernel: a block per 4 tokens adds the group sums in
+// ascending group order (thread e owns expert e) and one wave per token runs
+// the top-k.  Splitting over H keeps the GPU busy at moderate T.
 // ---------------------------------------------------------------------------
-// The group sums on the matrix cores (T >= kRouteSplitT): block (g,
-// tile) takes rows 256 g .. +255 (fewer in the last group) for 256 tokens
-// and all E <= 256 experts with v_mfma_f32_16x16x32_bf16 (bf16 products are
-// exact; the matrix cores add them in fp32 in an order of their own, so the
-// ids are a top-k of these logits like the VALU kernels').  The block's
-// router rows go to LDS once, transposed to [expert][h] (rows h, h+1 of an
-// expert packed into one dword; rows padded to 132 dwords so the 16 lanes of
-// a fragment read spread over the banks).  8 waves, each 32 tokens x all
-// experts (2 x 16 tiles of 16 x 16); a lane's token fragment (8 consecutive
-// h of one token, 16 contiguous bytes) comes straight from x, all K steps'
-// fragments loaded before the multiplies.  Writes G[g][t][e] for the reduce.
-constexpr int kRmStride = 132;  // dwords per transposed router row in LDS
+// The router matrix transposed, wr [H][E] -> wrT [E][H] (bf16), in 64 x 64
+// tiles through LDS with 16-byte global accesses (8 consecutive experts of
+// one row in -- element by element when E is not a multiple of 8 -- and 8
+// consecutive rows of one expert out): the matrix-core router below then
+// copies 16-byte runs of h per expert straight into LDS.
+__global__ __launch_bounds__(256) void route_transpose_kernel(const uint16_t* __restrict__ wr,
+                                                              int H, int E,
+                                                              uint16_t* __restrict__ wrT) {
+  __shared__ uint16_t tile[64][66];  // [h][e], rows padded against bank conflicts
+  const int h0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = 256 * j + tid, h = i >> 3, e8 = (i & 7) * 8;
+    const uint16_t* src = wr + (size_t)(h0 + h) * E + e0 + e8;
+    if (E % 8 == 0) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (h0 + h < H && e0 + e8 < E) v = *reinterpret_cast<const uint4*>(src);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        tile[h][e8 + 2 * m] = (uint16_t)(u[m] & 0xffffu);
+        tile[h][e8 + 2 * m + 1] = (uint16_t)(u[m] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        tile[h][e8 + m] = (h0 + h < H && e0 + e8 + m < E) ? src[m] : (uint16_t)0;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = 256 * j + tid, e = i >> 3, h8 = (i & 7) * 8;
+    if (e0 + e < E && h0 + h8 < H) {
+      uint32_t u[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        u[m] = (uint32_t)tile[h8 + 2 * m][e] | ((uint32_t)tile[h8 + 2 * m + 1][e] << 16);
+      *reinterpret_cast<uint4*>(wrT + (size_t)(e0 + e) * H + h0 + h8) =
+          make_uint4(u[0], u[1], u[2], u[3]);
+    }
+  }
+}
 
+// The group sums on the matrix cores (T >= kRouteSplitT): block (g, tile)
+// takes rows kRouteMfmaRows g .. +kRouteMfmaRows-1 (fewer in the last
+// group) for 256 tokens and all E <= 256 experts with
+// v_mfma_f32_16x16x32_bf16 (bf16 products are exact; the matrix cores add
+// them in fp32 in an order of their own, so the ids are a top-k of these
+// logits like the VALU kernels').  The rows pass through LDS 256 at a time:
+// per pass, direct global->LDS loads copy each expert's 256 h values (512
+// bytes, 32 runs of 16) from wrT, run c of expert e stored at run position
+// c xor (e mod 16), so that the 16 lanes of a fragment read (16 experts,
+// one run) hit distinct banks.  The products of every pass accumulate in
+// the same MFMA results.  8 waves, each 32 tokens x all experts (2 x 16
+// tiles of 16 x 16); a lane's token fragment (8 consecutive h of one token,
+// 16 contiguous bytes) comes straight from x, a pass's fragments loaded
+// before its router rows.  Writes G[g][t][e] for the reduce: with 512 rows
+// a group, the group sums of an 8192-token batch take half the bytes they
+// take with 256 (67 instead of 134 MB, written and read again).
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 __global__ __launch_bounds__(512) void route_group_mfma_kernel(const uint16_t* __restrict__ x,
-                                                               const uint16_t* __restrict__ wr,
+                                                               const uint16_t* __restrict__ wrT,
                                                                int T, int H, int E,
                                                                float* __restrict__ gsum) {
-  __shared__ __align__(16) uint32_t swt[256 * kRmStride];
+  __shared__ __align__(16) uint8_t swt[256 * 512];  // [expert][32 runs of 16 bytes]
   const int g = blockIdx.x, t0 = blockIdx.y * 256;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int h0 = 256 * g, nh = min(256, H - h0);  // 128 or 256 rows
   const int q = lane >> 4, r = lane & 15;
-  // this lane's token fragments for every K step, loads issued first
-  constexpr int KS = 8;
-  uint4 av[KS][2];
-#pragma unroll
-  for (int mf = 0; mf < 2; ++mf) {
-    const int t = min(t0 + 32 * w + 16 * mf + r, T - 1);
-    const uint16_t* xr = x + (size_t)t * H + h0 + 8 * q;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      av[ks][mf] = (32 * ks < nh) ? *reinterpret_cast<const uint4*>(xr + 32 * ks)
-                                  : make_uint4(0, 0, 0, 0);
-  }
-  // the router rows, transposed into LDS as (h, h+1) pairs per expert
-  auto lo2 = [](uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); };
-  auto hi2 = [](uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); };
-  auto row8 = [&](int h, int e8) -> uint4 {
-    const uint16_t* src = wr + (size_t)h * E + e8;
-    if (E == 256) return *reinterpret_cast<const uint4*>(src);
-    uint16_t v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = (e8 + u < E) ? src[u] : (uint16_t)0;
-    return make_uint4(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
-                      v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16));
-  };
-  // consecutive lanes take consecutive row pairs of one 8-expert column
-  // block, so their LDS writes (one dword per expert) fall in consecutive banks
-  const int np = nh / 2;
-  for (int it = tid; it < np * 32; it += 512) {
-    const int p = it % np, e8 = (it / np) * 8;
-    const uint4 a = row8(h0 + 2 * p, e8), b = row8(h0 + 2 * p + 1, e8);
-    const uint32_t pr[8] = {lo2(a.x, b.x), hi2(a.x, b.x), lo2(a.y, b.y), hi2(a.y, b.y),
-                            lo2(a.z, b.z), hi2(a.z, b.z), lo2(a.w, b.w), hi2(a.w, b.w)};
-#pragma unroll
-    for (int u = 0; u < 8; ++u) swt[(e8 + u) * kRmStride + p] = pr[u];
-  }
-  __syncthreads();
+  constexpr int KS = 8;  // 32-row MFMA steps per pass of 256 rows
+  const uint8_t* wbase = reinterpret_cast<const uint8_t*>(wrT);
   v4f_t acc[2][16];
 #pragma unroll
   for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
     for (int f = 0; f < 16; ++f) acc[mf][f] = (v4f_t){0.0f, 0.0f, 0.0f, 0.0f};
+  for (int pass = 0; pass < kRouteMfmaRows / 256; ++pass) {
+    const int h0 = kRouteMfmaRows * g + 256 * pass;
+    if (h0 >= H) break;  // block-uniform
+    const int nh = min(256, H - h0);  // rows of this pass (a multiple of 64)
+    // this lane's token fragments for every K step of the pass, loads issued first
+    uint4 av[KS][2];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    if (32 * ks >= nh) break;
-    const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, av[ks][0]);
-    const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, av[ks][1]);
+    for (int mf = 0; mf < 2; ++mf) {
+      const int t = min(t0 + 32 * w + 16 * mf + r, T - 1);
+      const uint16_t* xr = x + (size_t)t * H + h0 + 8 * q;
 #pragma unroll
-    for (int f = 0; f < 16; ++f) {
-      const uint4 bv =
-          *reinterpret_cast<const uint4*>(&swt[(16 * f + r) * kRmStride + 16 * ks + 4 * q]);
-      const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bv);
-      acc[0][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc[0][f], 0, 0, 0);
-      acc[1][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc[1][f], 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks)
+        av[ks][mf] = (32 * ks < nh) ? *reinterpret_cast<const uint4*>(xr + 32 * ks)
+                                    : make_uint4(0, 0, 0, 0);
+    }
+    // every wave is done with the previous pass's rows before they are replaced
+    if (pass > 0) {
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      block_barrier();
+    }
+    // the router rows: LDS run position s = 512 i + tid holds run
+    // (s mod 32) xor (e mod 16) of expert e = s / 32 (experts past E repeat
+    // the last one, runs past the pass's rows repeat its last run: neither
+    // is read)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int sp = 512 * i + tid, e = sp >> 5, c = (sp & 31) ^ (e & 15);
+      const uint32_t off = ((uint32_t)min(e, E - 1) * (uint32_t)H + (uint32_t)(h0 + min(8 * c, nh - 8))) * 2u;
+      dma16(wbase, off, swt + (size_t)(512 * i + 64 * w) * 16);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    block_barrier();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (32 * ks >= nh) break;
+      const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, av[ks][0]);
+      const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, av[ks][1]);
+#pragma unroll
+      for (int f = 0; f < 16; ++f) {
+        const uint4 bv =
+            *reinterpret_cast<const uint4*>(swt + (size_t)((16 * f + r) * 32 + ((4 * ks + q) ^ r)) * 16);
+        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bv);
+        acc[0][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc[0][f], 0, 0, 0);
+        acc[1][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc[1][f], 0, 0, 0);
+      }
     }
   }
   // tile (mf, f): lane holds experts 16 f + r, tokens 16 mf + 4 q + v of the wave's 32
@@ -522,27 +569,28 @@ __global__ __launch_bounds__(256) void route_group_quarter_kernel(
     if (e0 + j < E) dst[e0 + j] = grp[j];
 }
 
-// The logits of 4 tokens per block: group sums added in ascending group order
-// (thread e owns expert e; all group loads issued before the adds), then
-// one wave per token runs the top-k.
+// The logits of 4 tokens per block: the ng group sums added in ascending
+// group order (thread e owns expert e; all group loads issued before the
+// adds, GMAX >= ng of them, the index clamped to the last group), then one
+// wave per token runs the top-k.
+template <int GMAX>
 __global__ __launch_bounds__(256) void route_reduce_kernel(const float* __restrict__ gsum, int T,
-                                                           int H, int E, int k,
+                                                           int ng, int E, int k,
                                                            int32_t* __restrict__ ids,
                                                            float* __restrict__ w) {
   __shared__ float sz[4][256];
   const int t0 = blockIdx.x * 4, tid = threadIdx.x;
-  const int ng = (H / 64 + 3) / 4;
   const int e = min(tid, E - 1);
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
     const int t = min(t0 + tt, T - 1);
-    float v[kRouteMaxGroups];
+    float v[GMAX];
 #pragma unroll
-    for (int g = 0; g < kRouteMaxGroups; ++g)
+    for (int g = 0; g < GMAX; ++g)
       v[g] = gsum[((size_t)min(g, ng - 1) * T + t) * E + e];
     float acc = v[0];
 #pragma unroll
-    for (int g = 1; g < kRouteMaxGroups; ++g)
+    for (int g = 1; g < GMAX; ++g)
       if (g < ng) acc = acc + v[g];
     sz[tt][tid] = (t0 + tt < T && tid < E) ? acc : 0.0f;
   }
@@ -552,8 +600,8 @@ __global__ __launch_bounds__(256) void route_reduce_kernel(const float* __restri
 }
 
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int H, int E, int k,
-                        int32_t* ids, float* w, WsCtl* ctl, float* gsum, hipStream_t st,
-                        uint8_t* xq, float* xs) {
+                        int32_t* ids, float* w, WsCtl* ctl, float* gsum, uint16_t* wrT,
+                        hipStream_t st, uint8_t* xq, float* xs) {
   if (T <= kRouteSmallT) {
     FrontArgs a = {};
     a.x = x, a.wr = wr, a.T = T, a.H = H, a.E = E, a.k = k;
@@ -576,11 +624,18 @@ hipError_t launch_route(const uint16_t* x, const uint16_t* wr, int T, int H, int
     const int nqx = (int)((aq.nb + ny * nz - 1) / (ny * nz));
     route_group_quarter_kernel<<<dim3(ng + nqx, ny, nz), dim3(256), 0, st>>>(x, wr, T, H, E,
                                                                             gsum, aq);
+    route_reduce_kernel<kRouteMaxGroups>
+        <<<dim3((T + 3) / 4), dim3(256), 0, st>>>(gsum, T, ng, E, k, ids, w);
   } else {
-    route_group_mfma_kernel<<<dim3(ng, (T + 255) / 256), dim3(512), 0, st>>>(x, wr, T, H, E,
-                                                                            gsum);
+    if (!wrT || (size_t)E * H * 2 > 0xffffffffu) return hipErrorInvalidValue;
+    const int ngm = (H + kRouteMfmaRows - 1) / kRouteMfmaRows;
+    route_transpose_kernel<<<dim3((H + 63) / 64, (E + 63) / 64), dim3(256), 0, st>>>(wr, H, E,
+                                                                                   wrT);
+    route_group_mfma_kernel<<<dim3(ngm, (T + 255) / 256), dim3(512), 0, st>>>(x, wrT, T, H, E,
+                                                                             gsum);
+    route_reduce_kernel<kRouteMaxGroups * 256 / kRouteMfmaRows>
+        <<<dim3((T + 3) / 4), dim3(256), 0, st>>>(gsum, T, ngm, E, k, ids, w);
   }
-  route_reduce_kernel<<<dim3((T + 3) / 4), dim3(256), 0, st>>>(gsum, T, H, E, k, ids, w);
   if (xq && T >= kRouteSplitT) return launch_act_quant(x, true, T, H, xq, xs, st);
   return hipGetLastError();
 }

@@ -125,8 +125,9 @@ int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
  * for a given T: below 256 tokens, 64-wide chunk partials (chains of fused
  * multiply-adds in ascending h from +0), sums of 4 consecutive chunks in
  * ascending order, those group sums in ascending order; from 256 tokens on,
- * the same 256-row group sums formed on the matrix cores (bf16 MFMA, fp32
- * accumulation in the hardware's order).  The ids are deterministic.  They are the
+ * sums over 512-row groups formed on the matrix cores (bf16 MFMA, fp32
+ * accumulation in the hardware's order), added in ascending group order.
+ * The ids are deterministic.  They are the
  * exact top-k of these logits; logits summed in any other order differ by
  * rounding only, so another order can rank two experts differently only
  * where their logits lie within rounding distance of each other.

@@ -115,7 +115,8 @@ def test_route_ids_valid_topk(T, H, E, k):
     wr = synth.normal_bf16(900 + T, 2, (H, E), 0.02)
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    ws_b = (1 << 22) + ((H // 64 + 3) // 4) * T * E * 4   # control block + group sums
+    # control block + group sums (+ the transposed router from 256 tokens on)
+    ws_b = (1 << 22) + ((H // 64 + 3) // 4) * T * E * 4 + (E * H * 2 if T >= 256 else 0)
     ws = torch.zeros(ws_b, dtype=torch.uint8, device="cuda")
     moe.moe_workspace_init(ws, ws_b)
     moe.moe_route(to_dev(x), to_dev(wr), T, H, E, k, ids, w, ws, ws_b)
