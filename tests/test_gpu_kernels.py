@@ -222,7 +222,7 @@ def _permute_gpu(ids, E):
 @pytest.mark.parametrize("T,k,E,kind", [(1, 6, 256, "uniform"), (32, 6, 256, "zipf"),
                                         (300, 6, 256, "uniform"), (341, 8, 64, "zipf"),
                                         (4096, 6, 256, "zipf"), (8192, 6, 256, "uniform"),
-                                        (1000, 6, 256, "one_group")])
+                                        (1000, 6, 256, "one_group"), (2600, 6, 200, "zipf")])
 def test_permute_bitexact(T, k, E, kind):
     _print("permute", T, k, E, kind)
     if kind == "zipf":
