@@ -264,3 +264,34 @@ def test_host_experts_call_checks_arguments_on_host():
         moe.moe_workspace_bytes(host_w, 4, 6)
     assert moe.moe_host_experts_scratch_bytes(32, 4, 6) >= 2 * 4 * 6 * 4 + 2 * 33
     assert np.all(cache.slot_of == -1)
+
+
+def _route_ws_need(T, H, E, k=6):
+    """Smallest workspace moe_route accepts (the check precedes any HIP call:
+    below it the call returns MOE_EWORKSPACE, from it on another status)."""
+    p, ws = 0x100000, 0x200000
+
+    def rc(b):
+        return moe.raw_call("moe_route", p, p, T, H, E, k, p, p, ws, b, None)
+    lo, hi = 0, 1 << 34
+    assert rc(hi) != moe.MOE_EWORKSPACE
+    while lo + 1 < hi:
+        mid = (lo + hi) // 2
+        if rc(mid) == moe.MOE_EWORKSPACE:
+            lo = mid
+        else:
+            hi = mid
+    return hi
+
+
+@pytest.mark.parametrize("H,E", [(4096, 256), (384, 200), (8192, 100)])
+def test_route_workspace_holds_the_transposed_router_from_256_tokens(H, E):
+    """From 256 tokens on the router copies its matrix transposed into the
+    workspace ([E][H] bf16) besides the group sums, so the router section
+    grows by at least E*H*2 bytes from 255 to 256 tokens; below that it grows
+    by the group sums of one token only."""
+    n254, n255, n256 = (_route_ws_need(T, H, E) for T in (254, 255, 256))
+    groups = (H // 64 + 3) // 4
+    assert n255 - n254 <= groups * E * 4 + 256
+    assert n256 - n255 >= E * H * 2
+    assert moe.moe_workspace_bytes(_w(E=E, H=H), 256, 6) >= n256
