@@ -135,10 +135,16 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(
     int g = E;  // rows past the T*k routed ones: the shared expert
     if (active) {
       if (r < n_rows - T) {
+        // the slot holding row r (the slots' row ranges are disjoint): lane j
+        // loads entry q0 + j, a ballot finds the match -- one load round trip
+        // for up to 64 slots, where a loop of scalar loads waited for each
+        // entry in turn
         g = 0;
-        for (int q = 0; q < n_slots; ++q) {
-          const int4 v = active[q];
-          if (v.x >= 0 && r >= v.y && r < v.z) g = v.x;
+        for (int q0 = 0; q0 < n_slots; q0 += 64) {
+          const int4 v = active[min(q0 + lane, n_slots - 1)];
+          const uint64_t m =
+              __ballot((q0 + lane < n_slots) & (v.x >= 0) & (r >= v.y) & (r < v.z));
+          if (m) g = __builtin_amdgcn_readlane(v.x, __ffsll((long long)m) - 1);
         }
       }
     } else {
